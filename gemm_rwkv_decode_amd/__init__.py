@@ -1,1 +1,130 @@
-"""Placeholder; replaced by the binding below once the C-ABI exists."""
+"""Python binding of librq (include/rq.h): group-wise low-bit weight
+dequantization and dequantize-and-multiply on MI355X (gfx950).
+
+Argument marshalling only.  Every computation runs in the HIP kernels of
+``librq.so``; there is no CPU fallback.  If the library is missing, every call
+raises ``RqLibraryMissing`` (build it with ``python gemm_rwkv_decode_amd/build.py``
+or ``__graft_entry__.build()``).
+
+Tensors are torch tensors on the GPU, contiguous:
+
+* ``qweight``: uint8 ``[N][K/2]`` (4-bit) or int8 ``[N][K]`` (8-bit);
+* ``scales``: float16 ``[N][K/group]`` (symmetric) or uint8 ``[N][K/256][8]``
+  superblock records (asymmetric); ``zeros``: ``None`` (symmetric) or uint8
+  records (asymmetric);
+* ``x``: float16 ``[M][K]``; ``y``: float32 ``[M][N]``.
+
+Work is enqueued on torch's current stream (or the ``stream`` given).
+"""
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "RQ_OK", "RQ_LAYOUT_SYM", "RQ_LAYOUT_ASYM_SB", "RQ_OUT_F32", "RQ_OUT_CODES_I8",
+    "RQ_MAX_M", "RqError", "RqLibraryMissing", "rq_dequant", "rq_gemv",
+    "rq_gemm_smallm", "rq_status_string", "rq_version", "lib", "LIB_PATH",
+]
+
+RQ_OK = 0
+RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED, RQ_ERR_ALIGN = 1, 2, 3, 4
+RQ_ERR_LAUNCH, RQ_ERR_ALIAS, RQ_ERR_DEVICE = 5, 6, 7
+RQ_LAYOUT_SYM, RQ_LAYOUT_ASYM_SB = 0, 1
+RQ_OUT_F32, RQ_OUT_CODES_I8 = 0, 1
+RQ_MAX_M = 64
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librq.so")
+_lib = None
+_lock = threading.Lock()
+
+
+class RqLibraryMissing(RuntimeError):
+    pass
+
+
+class RqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({rq_status_string(status)})")
+
+
+def lib():
+    """The loaded librq (ctypes), signatures declared."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RqLibraryMissing(
+                    f"{LIB_PATH} not found: build it with gemm_rwkv_decode_amd/build.py")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i = ctypes.c_void_p, ctypes.c_int
+            L.rq_dequant.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+            L.rq_dequant.restype = i
+            for name in ("rq_gemv", "rq_gemm_smallm"):
+                f = getattr(L, name)
+                f.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+                f.restype = i
+            L.rq_status_string.argtypes = [i]
+            L.rq_status_string.restype = ctypes.c_char_p
+            L.rq_version.argtypes = []
+            L.rq_version.restype = i
+            _lib = L
+    return _lib
+
+
+def rq_status_string(status: int) -> str:
+    return lib().rq_status_string(int(status)).decode()
+
+
+def rq_version() -> int:
+    return lib().rq_version()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("librq takes GPU tensors only")
+    if not t.is_contiguous():
+        raise ValueError("librq takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream, like):
+    if stream is not None:
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return int(torch.cuda.current_stream(like.device).cuda_stream)
+
+
+def rq_dequant(qweight, scales, zeros, out, N, K, bits, group, layout,
+               out_kind=RQ_OUT_F32, stream=None):
+    """Unpack (out_kind RQ_OUT_CODES_I8, out int8 [N][K]) or dequantize
+    (RQ_OUT_F32, out float32 [N][K]) the packed weights."""
+    st = lib().rq_dequant(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out), int(N),
+                          int(K), int(bits), int(group), int(layout), int(out_kind),
+                          _stream(stream, qweight))
+    if st != RQ_OK:
+        raise RqError("rq_dequant", st)
+    return out
+
+
+def rq_gemv(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, stream=None):
+    """y[m][n] = sum_k x[m][k] w[n][k] on the vector units (tuned for M <= 8)."""
+    st = lib().rq_gemv(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y), int(M),
+                       int(N), int(K), int(bits), int(group), int(layout),
+                       _stream(stream, qweight))
+    if st != RQ_OK:
+        raise RqError("rq_gemv", st)
+    return y
+
+
+def rq_gemm_smallm(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
+                   stream=None):
+    """Same product on the matrix cores (tuned for 16 <= M <= 64)."""
+    st = lib().rq_gemm_smallm(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                              int(M), int(N), int(K), int(bits), int(group), int(layout),
+                              _stream(stream, qweight))
+    if st != RQ_OK:
+        raise RqError("rq_gemm_smallm", st)
+    return y

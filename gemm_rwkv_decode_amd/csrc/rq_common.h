@@ -1,0 +1,124 @@
+// rq_common.h -- device helpers shared by the librq kernels (gfx950 only).
+//
+// Internal to librq.  Formats and readings are stated in include/rq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+typedef uint32_t u32;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+
+// Format ids of the kernels (a function of layout and bits).
+enum Fmt { FMT_S4 = 0, FMT_S8 = 1, FMT_A4 = 2 };
+
+constexpr int SUPERBLOCK = 256;  // k per asymmetric superblock
+constexpr int SB_GROUP = 32;     // k per asymmetric group
+
+// Codes in one 16-byte chunk of a row.
+template <int FMT>
+struct Chunk {
+  static constexpr int codes = (FMT == FMT_S8) ? 16 : 32;
+};
+
+__device__ __forceinline__ h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ u32 as_u32(h2 v) { return __builtin_bit_cast(u32, v); }
+
+// Streaming (read-once) 16-byte load of packed codes.
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 load_stream8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ u32 load_stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Exact code -> binary16 conversion.
+//
+// A 4-bit value u placed in the low mantissa bits of 0x6400 (= 1024.0) gives
+// the binary16 number 1024 + u; in bits 4-7 it gives 1024 + 16u.  Both are
+// exact, and so are (1024 + u) - c and (1024 + 16u)/16 - c for the small
+// integer c used below, so every code reaches fp16 without rounding.
+// ---------------------------------------------------------------------------
+
+// One dword of 4-bit codes, k = 0..7 in nibbles 0..7 (even k low).  Returns
+// the pairs (q0,q4) (q1,q5) (q2,q6) (q3,q7) as binary16.  SIGNED selects 4-bit
+// two's complement codes (-8..7); otherwise codes are unsigned (0..15).
+template <bool SIGNED>
+__device__ __forceinline__ void unpack4(u32 d, h2 q[4]) {
+  if (SIGNED) d ^= 0x88888888u;  // two's complement nibble -> q + 8
+  const u32 lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+  const u32 d2 = d >> 8;
+  const u32 t0 = (d & lo) | magic;   // 1024 + u0, 1024 + u4
+  const u32 t1 = (d & hi) | magic;   // 1024 + 16 u1, 1024 + 16 u5
+  const u32 t2 = (d2 & lo) | magic;  // 1024 + u2, 1024 + u6
+  const u32 t3 = (d2 & hi) | magic;  // 1024 + 16 u3, 1024 + 16 u7
+  const _Float16 b0 = SIGNED ? (_Float16)-1032.0f : (_Float16)-1024.0f;
+  const _Float16 b1 = SIGNED ? (_Float16)-72.0f : (_Float16)-64.0f;
+  const h2 bias0 = {b0, b0};
+  const h2 bias1 = {b1, b1};
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  q[0] = as_h2(t0) + bias0;
+  q[1] = __builtin_elementwise_fma(as_h2(t1), sixteenth, bias1);
+  q[2] = as_h2(t2) + bias0;
+  q[3] = __builtin_elementwise_fma(as_h2(t3), sixteenth, bias1);
+}
+
+// One dword of int8 codes, k = 0..3 in bytes 0..3.  Returns (q0,q1) (q2,q3).
+// A byte u = q + 128 placed in the low 8 mantissa bits of 0x6400 is 1024 + u.
+__device__ __forceinline__ void unpack8(u32 d, h2 q[2]) {
+  d ^= 0x80808080u;  // two's complement byte -> q + 128
+  const u32 t0 = __builtin_amdgcn_perm(0x64646464u, d, 0x04010400u);  // u0 | u1
+  const u32 t1 = __builtin_amdgcn_perm(0x64646464u, d, 0x04030402u);  // u2 | u3
+  const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  q[0] = as_h2(t0) + bias;
+  q[1] = as_h2(t1) + bias;
+}
+
+// Activation pairs matching unpack4: from the 8 halves x0..x7 held in four
+// dwords w0=(x0,x1) w1=(x2,x3) w2=(x4,x5) w3=(x6,x7) build
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+__device__ __forceinline__ void pair_x4(u32 w0, u32 w1, u32 w2, u32 w3, h2 p[4]) {
+  p[0] = as_h2(__builtin_amdgcn_perm(w2, w0, 0x05040100u));
+  p[1] = as_h2(__builtin_amdgcn_perm(w2, w0, 0x07060302u));
+  p[2] = as_h2(__builtin_amdgcn_perm(w3, w1, 0x05040100u));
+  p[3] = as_h2(__builtin_amdgcn_perm(w3, w1, 0x07060302u));
+}
+
+// Exact binary16 -> binary32 of the low / high half of a dword.
+__device__ __forceinline__ float half_lo(u32 v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(u32 v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// Asymmetric superblock record {binary16 base; 48-bit field of eight 6-bit
+// sub-codes} held in two dwords r.x (bytes 0-3) and r.y (bytes 4-7).
+// Returns base * sub_j, exact in binary32 (11 + 6 significant bits).
+__device__ __forceinline__ float record_value(u32x2 r, int j) {
+  const uint64_t all = ((uint64_t)r.y << 32) | r.x;
+  const u32 sub = (u32)(all >> (16 + 6 * j)) & 0x3Fu;
+  return half_lo(r.x) * (float)sub;
+}
+
+// Sum over the LPR consecutive lanes of a row group; every lane of the group
+// receives the total.  LPR is a power of two <= 64.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, LPR);
+  return v;
+}
+
+}  // namespace rq

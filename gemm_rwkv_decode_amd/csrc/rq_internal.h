@@ -1,0 +1,51 @@
+// rq_internal.h -- host-side launchers shared between the translation units
+// of librq.  Arguments have been validated by rq_api.hip before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace rq {
+
+struct Problem {
+  const void* qweight;
+  const void* scales;
+  const void* zeros;
+  const void* x;  // binary16 [M][K]
+  float* y;       // [M][N]
+  int M, N, K, group;
+  int fmt;        // Fmt
+};
+
+// Tuning knobs of one GEMV launch (chosen by choose_gemv unless overridden).
+struct GemvCfg {
+  int lpr;    // lanes per row (power of two, 8..64); 0 = generic kernel
+  int cpl;    // 16-byte chunks per lane per row (1 or 2)
+  int npass;  // row passes per workgroup (rows per workgroup = npass*64/lpr)
+  int mt;     // activation rows per launch (1, 2, 4, 8)
+};
+
+GemvCfg choose_gemv(int fmt, int M, int N, int K);
+hipError_t launch_gemv(const Problem& p, const GemvCfg& c, hipStream_t s);
+
+struct GemmCfg {
+  int nt;      // 16-row N-tiles per wave (4 waves per workgroup)
+  int mt;      // 16-row M-tiles (1..4)
+  int splits;  // K split across workgroups
+};
+
+// The matrix-core kernel needs K to be a whole number of its LDS chunks.
+bool gemm_supports(int fmt, int M, int K);
+GemmCfg choose_gemm(int fmt, int M, int N, int K, int group);
+// ws: float workspace of at least splits*M*N entries; counters: zeroed
+// unsigned array with at least ceil(N / (64*nt)) entries.  Both unused when
+// splits == 1.
+hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws,
+                       unsigned* counters, hipStream_t s);
+size_t gemm_workspace_floats(const GemmCfg& c, int M, int N);
+int gemm_counters(const GemmCfg& c, int N);
+
+hipError_t launch_dequant(const void* qweight, const void* scales, const void* zeros,
+                          void* out, int N, int K, int group, int fmt, int out_kind,
+                          hipStream_t s);
+
+}  // namespace rq

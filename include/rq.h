@@ -1,0 +1,135 @@
+/*
+ * rq.h -- C interface of librq: group-wise low-bit weight dequantization and
+ * dequantize-and-multiply (GEMV / small-M GEMM) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A weight matrix W with N rows (outputs) and K columns
+ * (inputs) is stored as packed integer codes q[n][k] plus per-group scale
+ * material; rows are [out][in], as the FFN key (16384x4096) and FFN value
+ * (4096x16384) of a width-4096 RWKV-7 model are listed on the package page
+ * "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization Details").
+ * Three storage formats are supported:
+ *
+ *   RQ_LAYOUT_SYM, bits = 4, group in {32, 64, 128}
+ *       The 4-bit symmetric format with one scale per group of consecutive
+ *       weights of a row; group 64 is the format of the model card
+ *       "RWKV-7 G1 1.5B -- int4 GPTQ for rwkv-sglang" (opening paragraph,
+ *       section "Format & loading").  qweight: uint8 [N][K/2], two codes per
+ *       byte, the even k in bits 0-3, each code a 4-bit two's complement
+ *       integer (-8..7).  scales: IEEE binary16 [N][K/group].  w = s * q.
+ *   RQ_LAYOUT_SYM, bits = 8, group in {16, 32, 64}
+ *       The 8-bit symmetric projection format of the REDUCTION preset (group
+ *       16) in the news article "rwkv-quant: keeping one matrix in bf16 ..."
+ *       (section "Two presets and six sizes").  qweight: int8 [N][K] two's
+ *       complement.  scales: binary16 [N][K/group].  w = s * q.
+ *   RQ_LAYOUT_ASYM_SB, bits = 4, group = 32
+ *       The 4-bit asymmetric superblock projection format of the COMPRESSION
+ *       preset (same article and section): each 32-wide group has its own
+ *       scale and shift.  qweight: uint8 [N][K/2], unsigned codes 0..15, even
+ *       k in bits 0-3.  A superblock is 256 consecutive k of one row (eight
+ *       groups).  scales: [N][K/256] records of 8 bytes: binary16 d in bytes
+ *       0-1 (little endian), then eight 6-bit unsigned sub-scales sc_j packed
+ *       LSB-first in the 48-bit little-endian field of bytes 2-7 (sc_j at bits
+ *       6j..6j+5).  zeros: records of the same shape holding m and the
+ *       sub-mins mn_j.  With j = (k mod 256)/32:
+ *       w = (d * sc_j) * q - (m * mn_j).
+ *
+ * Every dequantized weight is the binary32 value nearest (ties to even) the
+ * exact value of its formula; for these formats that value is the same however
+ * the products are grouped, so there is exactly one right answer.
+ *
+ * Pointers.  Every pointer is device memory owned by the caller and must be
+ * 16-byte aligned.  The library does not free or retain caller memory, never
+ * copies to the host and never synchronizes: work is enqueued on `stream`
+ * (a hipStream_t; NULL means the null stream) and the call returns after the
+ * enqueue.  Outputs must not overlap any input.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call, so a call
+ * that returns an error other than RQ_ERR_LAUNCH or RQ_ERR_DEVICE has
+ * enqueued nothing.  A kernel fault is reported by the caller's next
+ * synchronization, as for any asynchronous HIP work.  No exception crosses
+ * this interface and nothing is printed.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RQ_OK = 0,
+    RQ_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    RQ_ERR_SHAPE = 2,       /* M, N, K or group violate the shape rules         */
+    RQ_ERR_UNSUPPORTED = 3, /* (layout, bits, group, out_kind) not supported    */
+    RQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
+    RQ_ERR_LAUNCH = 5,      /* the kernel launch was rejected by the runtime    */
+    RQ_ERR_ALIAS = 6,       /* an output range overlaps an input range          */
+    RQ_ERR_DEVICE = 7       /* no usable gfx950 device, or device memory for the
+                               split-K workspace could not be obtained           */
+} rq_status;
+
+typedef enum { RQ_LAYOUT_SYM = 0, RQ_LAYOUT_ASYM_SB = 1 } rq_layout;
+
+typedef enum {
+    RQ_OUT_F32 = 0,     /* binary32 weights [N][K]                               */
+    RQ_OUT_CODES_I8 = 1 /* the integer codes as int8 [N][K]: -8..7 (4-bit sym),
+                           -128..127 (8-bit), 0..15 (asymmetric)                 */
+} rq_out_kind;
+
+/* Largest M accepted by rq_gemv and rq_gemm_smallm. */
+#define RQ_MAX_M 64
+
+/*
+ * rq_dequant -- unpack the codes of W, or dequantize W to binary32.
+ * Defines the dequantization of the formats above (the model card's accuracy
+ * paragraph reports that the serving kernel reproduces the offline dequant bit
+ * for bit; this call is that offline dequant).
+ *   out: RQ_OUT_F32 -> float [N][K]; RQ_OUT_CODES_I8 -> int8 [N][K].
+ *   zeros: NULL for RQ_LAYOUT_SYM, required for RQ_LAYOUT_ASYM_SB.
+ * Shape rules: N >= 1, K >= group, K % group == 0, K*bits/8 % 16 == 0, and for
+ * the asymmetric layout K % 256 == 0.
+ */
+rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
+                     void* out, int N, int K, int bits, int group, int layout,
+                     int out_kind, void* stream);
+
+/*
+ * rq_gemv -- y[m][n] = sum_k x[m][k] * w[n][k] for 1 <= M <= RQ_MAX_M, where w
+ * is the dequantized weight above (the weight-only decode product whose speed
+ * the model card reports against fp16, section "Speed").
+ *   x: binary16 [M][K] row-major.  y: float [M][N] row-major, overwritten.
+ * Each output is within 1e-3 * sum_k |x[m][k] * w[n][k]| of the exact value
+ * (fp32 accumulation).  Tuned for M <= 8 (the per-token decode shape); larger M
+ * is processed in passes of up to 8 rows.
+ * Shape rules as for rq_dequant, plus 1 <= M <= RQ_MAX_M.
+ */
+rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
+                  const void* x, float* y, int M, int N, int K, int bits,
+                  int group, int layout, void* stream);
+
+/*
+ * rq_gemm_smallm -- the same product and contract as rq_gemv, computed on the
+ * matrix cores (fp16 MFMA on exact integer codes, fp32 per-group scaling).
+ * Tuned for 16 <= M <= 64 (batched decode); smaller M is padded to 16.
+ * For some shapes the K dimension is split across workgroups; the partial sums
+ * then pass through a workspace the library allocates once per (device,
+ * stream) and keeps until the process ends (a call that needs a larger one
+ * than the stream already has allocates it before enqueuing, which
+ * synchronizes that device).  Partial sums are added in a fixed order, so
+ * results are deterministic.
+ */
+rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* zeros,
+                         const void* x, float* y, int M, int N, int K, int bits,
+                         int group, int layout, void* stream);
+
+/* A static, NUL-terminated English description of a status value. */
+const char* rq_status_string(int status);
+
+/* Interface version: (major << 16) | minor. */
+int rq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H */

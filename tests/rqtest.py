@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+oracle on the same bytes, compare."""
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+import gemm_rwkv_decode_amd as rq
+from gemm_rwkv_decode_amd import synth as S
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def fmt(tag, bits, group, layout):
+    return S.Fmt(tag, bits, group, layout)
+
+
+ALL_FORMATS = [
+    S.INT4_G64, S.INT8_G16, S.ASYM4_G32,
+    fmt("int4g32", 4, 32, S.LAYOUT_SYM), fmt("int4g128", 4, 128, S.LAYOUT_SYM),
+    fmt("int8g32", 8, 32, S.LAYOUT_SYM), fmt("int8g64", 8, 64, S.LAYOUT_SYM),
+]
+
+
+def to_dev(p: S.Packed) -> S.Packed:
+    d = "cuda"
+    return S.Packed(p.qweight.to(d), p.scales.to(d),
+                    None if p.zeros is None else p.zeros.to(d), p.N, p.K, p.fmt)
+
+
+def to_np(p: S.Packed):
+    """numpy views of a packed matrix for the oracle (copied to the host)."""
+    q = p.qweight.cpu().contiguous().numpy()
+    s = p.scales.cpu().contiguous().numpy()
+    z = None if p.zeros is None else p.zeros.cpu().contiguous().numpy()
+    return q, s, z
+
+
+def oracle_y(p: S.Packed, x: torch.Tensor):
+    q, s, z = to_np(p)
+    xx = x.cpu().numpy()
+    return O.gemv_ref(q, s, z, xx, p.N, p.K, p.fmt.bits, p.fmt.group, p.fmt.layout,
+                      threads=THREADS)
+
+
+def oracle_dequant(p: S.Packed):
+    q, s, z = to_np(p)
+    return O.dequant(q, s, z, p.N, p.K, p.fmt.bits, p.fmt.group, p.fmt.layout)
+
+
+def oracle_codes(p: S.Packed):
+    q, _, _ = to_np(p)
+    return O.unpack_codes(q, p.N, p.K, p.fmt.bits, p.fmt.layout)
+
+
+def run(entry, p: S.Packed, x: torch.Tensor, y=None):
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, p.N), dtype=torch.float32, device="cuda")
+    f = rq.rq_gemv if entry == "gemv" else rq.rq_gemm_smallm
+    f(p.qweight, p.scales, p.zeros, x, y, M, p.N, p.K, p.fmt.bits, p.fmt.group,
+      p.fmt.layout)
+    return y
+
+
+def dequant(p: S.Packed, kind=rq.RQ_OUT_F32):
+    dt = torch.float32 if kind == rq.RQ_OUT_F32 else torch.int8
+    out = torch.empty((p.N, p.K), dtype=dt, device="cuda")
+    rq.rq_dequant(p.qweight, p.scales, p.zeros, out, p.N, p.K, p.fmt.bits, p.fmt.group,
+                  p.fmt.layout, kind)
+    return out
+
+
+def assert_close(y, y_ref, bound, what=""):
+    yy = y.detach().cpu().numpy() if torch.is_tensor(y) else y
+    nbad, first, worst = O.check(yy, y_ref, bound)
+    if nbad:
+        flat = yy.ravel()
+        i = first
+        raise AssertionError(
+            f"{what}: {nbad} of {flat.size} outputs outside 1e-3*sum|wx|; first at "
+            f"{np.unravel_index(i, yy.shape)}: got {flat[i]!r}, ref {y_ref.ravel()[i]!r}, "
+            f"bound {bound.ravel()[i]!r}; worst ratio {worst:.3g}")
+    return worst

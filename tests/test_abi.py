@@ -1,0 +1,151 @@
+"""librq's C interface on the CPU: the library loads, exports every function
+include/rq.h declares, and rejects bad arguments on the host before any HIP
+call (so these run without a GPU: fake, never-dereferenced addresses are
+used).  The status values are the ones the header defines."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_rwkv_decode_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq.h")
+
+A = 0x7F0000000000  # a 16-byte-aligned address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z_0-9]+)\s*\(", src)))
+
+
+def header_enum(name):
+    src = open(HEADER).read()
+    m = re.search(r"\b" + name + r"\s*=\s*(\d+)", src)
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rq.LIB_PATH):
+        pytest.fail("librq.so is not built (run __graft_entry__.build())")
+    return rq.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) >= {"rq_dequant", "rq_gemv", "rq_gemm_smallm", "rq_status_string",
+                          "rq_version"}
+    for n in names:
+        assert hasattr(L, n), f"librq.so does not export {n}"
+
+
+def test_status_values_match_header():
+    for n in ["RQ_OK", "RQ_ERR_NULL", "RQ_ERR_SHAPE", "RQ_ERR_UNSUPPORTED", "RQ_ERR_ALIGN",
+              "RQ_ERR_LAUNCH", "RQ_ERR_ALIAS", "RQ_ERR_DEVICE", "RQ_LAYOUT_SYM",
+              "RQ_LAYOUT_ASYM_SB", "RQ_OUT_F32", "RQ_OUT_CODES_I8"]:
+        assert getattr(rq, n) == header_enum(n), n
+    assert rq.RQ_MAX_M == int(re.search(r"#define RQ_MAX_M (\d+)", open(HEADER).read()).group(1))
+
+
+def test_version_and_strings(L):
+    assert rq.rq_version() == (1 << 16)
+    seen = set()
+    for s in range(8):
+        t = rq.rq_status_string(s)
+        assert t and t not in seen
+        seen.add(t)
+    assert rq.rq_status_string(99) == "unknown status"
+
+
+def gemv_args(**kw):
+    a = dict(qw=A, sc=A + (1 << 30), z=None, x=A + (2 << 30), y=A + (3 << 30), M=1, N=64,
+             K=256, bits=4, group=64, layout=0)
+    a.update(kw)
+    return [a["qw"], a["sc"], a["z"], a["x"], a["y"], a["M"], a["N"], a["K"], a["bits"],
+            a["group"], a["layout"], None]
+
+
+def dq_args(**kw):
+    a = dict(qw=A, sc=A + (1 << 30), z=None, out=A + (3 << 30), N=64, K=256, bits=4,
+             group=64, layout=0, kind=0)
+    a.update(kw)
+    return [a["qw"], a["sc"], a["z"], a["out"], a["N"], a["K"], a["bits"], a["group"],
+            a["layout"], a["kind"], None]
+
+
+CASES = [
+    ("null qweight", dict(qw=None), rq.RQ_ERR_NULL),
+    ("null scales", dict(sc=None), rq.RQ_ERR_NULL),
+    ("asym without zeros", dict(layout=1, group=32, K=512), rq.RQ_ERR_NULL),
+    ("sym with zeros", dict(z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
+    ("3-bit codes", dict(bits=3), rq.RQ_ERR_UNSUPPORTED),
+    ("int4 group 48", dict(group=48), rq.RQ_ERR_UNSUPPORTED),
+    ("int4 group 16", dict(group=16), rq.RQ_ERR_UNSUPPORTED),
+    ("int8 group 128", dict(bits=8, group=128), rq.RQ_ERR_UNSUPPORTED),
+    ("unknown layout", dict(layout=2), rq.RQ_ERR_UNSUPPORTED),
+    ("asym group 64", dict(layout=1, group=64, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
+    ("asym 8-bit", dict(layout=1, group=32, bits=8, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
+    ("K not a multiple of group", dict(K=96), rq.RQ_ERR_SHAPE),
+    ("K below group", dict(K=32), rq.RQ_ERR_SHAPE),
+    ("N zero", dict(N=0), rq.RQ_ERR_SHAPE),
+    ("N negative", dict(N=-5), rq.RQ_ERR_SHAPE),
+    ("asym K not whole superblocks", dict(layout=1, group=32, K=288, z=A + (4 << 30)),
+     rq.RQ_ERR_SHAPE),
+    ("misaligned qweight", dict(qw=A + 8), rq.RQ_ERR_ALIGN),
+    ("misaligned scales", dict(sc=A + (1 << 30) + 2), rq.RQ_ERR_ALIGN),
+    ("misaligned zeros", dict(layout=1, group=32, K=512, z=A + (4 << 30) + 4),
+     rq.RQ_ERR_ALIGN),
+]
+
+GEMV_ONLY = [
+    ("null x", dict(x=None), rq.RQ_ERR_NULL),
+    ("null y", dict(y=None), rq.RQ_ERR_NULL),
+    ("M zero", dict(M=0), rq.RQ_ERR_SHAPE),
+    ("M above 64", dict(M=65), rq.RQ_ERR_SHAPE),
+    ("misaligned x", dict(x=A + (2 << 30) + 2), rq.RQ_ERR_ALIGN),
+    ("misaligned y", dict(y=A + (3 << 30) + 4), rq.RQ_ERR_ALIGN),
+    ("y overlaps x", dict(y=A + (2 << 30) + 16), rq.RQ_ERR_ALIAS),
+    ("y overlaps codes", dict(y=A + 64), rq.RQ_ERR_ALIAS),
+    ("y overlaps scales", dict(y=A + (1 << 30)), rq.RQ_ERR_ALIAS),
+]
+
+
+@pytest.mark.parametrize("fn", ["rq_gemv", "rq_gemm_smallm"])
+@pytest.mark.parametrize("what,kw,status", CASES + GEMV_ONLY, ids=[c[0] for c in CASES + GEMV_ONLY])
+def test_product_rejects(L, fn, what, kw, status):
+    assert getattr(L, fn)(*gemv_args(**kw)) == status, what
+
+
+DQ_ONLY = [
+    ("null out", dict(out=None), rq.RQ_ERR_NULL),
+    ("unknown output kind", dict(kind=2), rq.RQ_ERR_UNSUPPORTED),
+    ("misaligned out", dict(out=A + (3 << 30) + 8), rq.RQ_ERR_ALIGN),
+    ("out overlaps codes", dict(out=A + 16), rq.RQ_ERR_ALIAS),
+]
+
+
+@pytest.mark.parametrize("what,kw,status", CASES + DQ_ONLY, ids=[c[0] for c in CASES + DQ_ONLY])
+def test_dequant_rejects(L, what, kw, status):
+    assert L.rq_dequant(*dq_args(**kw)) == status, what
+
+
+def test_valid_call_without_gpu_reports_device(L):
+    """A valid call on a machine without a gfx950 device returns RQ_ERR_DEVICE
+    (nothing is launched; the fake addresses are never touched)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.rq_gemv(*gemv_args()) == rq.RQ_ERR_DEVICE
+    assert L.rq_gemm_smallm(*gemv_args(M=32)) == rq.RQ_ERR_DEVICE
+    assert L.rq_dequant(*dq_args()) == rq.RQ_ERR_DEVICE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    t = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        rq.rq_dequant(t, t, None, t, 1, 32, 4, 32, 0)

@@ -1,0 +1,270 @@
+"""GPU parity: librq against the CPU oracle on the same seeded bytes.
+
+Bar: rq_dequant and the unpacked codes bit-exact; rq_gemv and rq_gemm_smallm
+within |y - y_ref| <= 1e-3 * sum_k |w x| per output; one-hot and integer-exact
+inputs (where every partial sum is exact) bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import gemm_rwkv_decode_amd as rq
+from gemm_rwkv_decode_amd import synth as S
+from tests import rqtest as T
+
+pytestmark = pytest.mark.gpu
+
+ENTRIES = ["gemv", "gemm"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def small(fmt, N, K, tag=0):
+    p = S.gen_matrix(90 + tag, 0, 0, N, K, fmt)
+    return T.to_dev(p)
+
+
+def x_for(M, K, seed, massive=True):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((M, K), generator=g)
+    if massive:
+        x[:, K // 3] *= 200.0
+    return x.half().cuda()
+
+
+# --------------------------------------------------------------- dequant ---
+DQ_SHAPES = [(37, 512), (1, 256), (129, 768)]
+
+
+@pytest.mark.parametrize("f", T.ALL_FORMATS, ids=lambda f: f.tag)
+@pytest.mark.parametrize("N,K", DQ_SHAPES)
+def test_dequant_bit_exact(f, N, K):
+    if K % 256 and f.layout == S.LAYOUT_ASYM_SB:
+        pytest.skip("asymmetric K must be whole superblocks")
+    T.say(f"dequant {f.tag} N={N} K={K}")
+    p = small(f, N, K)
+    w = T.dequant(p).cpu().numpy()
+    ref = T.oracle_dequant(p)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32))
+    c = T.dequant(p, rq.RQ_OUT_CODES_I8).cpu().numpy()
+    assert np.array_equal(c, T.oracle_codes(p))
+
+
+@pytest.mark.parametrize("N,K,f", [(768, 768, S.INT4_G64), (2048, 2048, S.INT8_G16),
+                                   (2560, 2560, S.ASYM4_G32), (4096, 4096, S.INT4_G64),
+                                   (16384, 4096, S.INT4_G64), (2560, 10240, S.ASYM4_G32)])
+def test_dequant_bit_exact_config_shapes(N, K, f):
+    T.say(f"dequant {f.tag} N={N} K={K}")
+    p = small(f, N, K, tag=1)
+    w = T.dequant(p).cpu().numpy()
+    assert np.array_equal(w.view(np.uint32), T.oracle_dequant(p).view(np.uint32))
+    c = T.dequant(p, rq.RQ_OUT_CODES_I8).cpu().numpy()
+    assert np.array_equal(c, T.oracle_codes(p))
+
+
+@pytest.mark.parametrize("f", [S.INT4_G64, S.INT8_G16, S.ASYM4_G32], ids=lambda f: f.tag)
+def test_dequant_subnormal_and_extreme_values(f):
+    """binary16 subnormal / negative / largest scales, the code -8 (4-bit) and
+    -128 (8-bit): still bit-exact."""
+    N, K = 16, 512
+    T.say(f"dequant extremes {f.tag}")
+    p, codes = S.gen_matrix(77, 0, 0, N, K, f, keep_codes=True)
+    if f.layout == S.LAYOUT_SYM:
+        lo = -8 if f.bits == 4 else -128
+        codes[:, ::5] = lo
+        sc = p.scales.clone().view(torch.int16)
+        special = torch.tensor([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF - 0x10000, 0x0400,
+                                0x0000, -0x8000], dtype=torch.int16)
+        sc.view(-1)[: special.numel() * 3] = special.repeat(3)
+        p = S.encode(codes, f, scales=sc.view(torch.float16))
+    else:
+        B = K // 256
+        d = torch.full((N, B), 2.0 ** -24, dtype=torch.float16)
+        d[::2] = 65504.0
+        m = torch.full((N, B), 2.0 ** -20, dtype=torch.float16)
+        sc = torch.randint(0, 64, (N, B, 8), dtype=torch.int16).to(torch.uint8)
+        mn = torch.randint(0, 64, (N, B, 8), dtype=torch.int16).to(torch.uint8)
+        p = S.encode(codes, f, d=d, sc=sc, m=m, mn=mn)
+    p = T.to_dev(p)
+    w = T.dequant(p).cpu().numpy()
+    assert np.array_equal(w.view(np.uint32), T.oracle_dequant(p).view(np.uint32))
+    assert np.array_equal(T.dequant(p, rq.RQ_OUT_CODES_I8).cpu().numpy(), T.oracle_codes(p))
+
+
+# ------------------------------------------------------- products, small ---
+SHAPES = [(37, 512), (100, 768), (256, 2048), (8, 256)]
+GEMV_MS = [1, 2, 3, 4, 5, 8, 9, 16, 33, 64]
+GEMM_MS = [1, 7, 16, 17, 32, 48, 64]
+
+
+@pytest.mark.parametrize("f", T.ALL_FORMATS, ids=lambda f: f.tag)
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_product_parity_small(f, N, K, entry):
+    if K % 256 and f.layout == S.LAYOUT_ASYM_SB:
+        pytest.skip("asymmetric K must be whole superblocks")
+    p = small(f, N, K, tag=2)
+    for M in (GEMV_MS if entry == "gemv" else GEMM_MS):
+        T.say(f"{entry} {f.tag} M={M} N={N} K={K}")
+        x = x_for(M, K, seed=M * 1000 + N)
+        y = T.run(entry, p, x)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"{entry} {f.tag} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("N,K,f", [(50, 544, T.fmt("int4g32", 4, 32, S.LAYOUT_SYM)),
+                                   (70, 64, S.INT4_G64), (20, 16, S.INT8_G16),
+                                   (3, 48 * 16, S.INT8_G16)])
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_product_parity_odd_k(N, K, f, entry):
+    """Row lengths whose chunk count has no power-of-two split (generic kernel;
+    the matrix-core entry falls back to it too) and the smallest legal K."""
+    p = small(f, N, K, tag=3)
+    for M in (1, 3, 16, 40):
+        T.say(f"{entry} odd-K {f.tag} M={M} N={N} K={K}")
+        x = x_for(M, K, seed=M + K)
+        y = T.run(entry, p, x)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"{entry} {f.tag} M={M} N={N} K={K}")
+
+
+def test_generic_kernel_forced(monkeypatch):
+    """The generic kernel also serves shapes the tuned one handles."""
+    monkeypatch.setenv("RQ_GEMV_LPR", "-1")
+    for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
+        p = small(f, 45, 1024, tag=4)
+        for M in (1, 5):
+            T.say(f"generic {f.tag} M={M}")
+            x = x_for(M, 1024, seed=M)
+            y = T.run("gemv", p, x)
+            yr, b = T.oracle_y(p, x)
+            T.assert_close(y, yr, b, f"generic {f.tag} M={M}")
+
+
+@pytest.mark.parametrize("npass", ["1", "3", "8"])
+def test_gemv_pass_counts(monkeypatch, npass):
+    """Row passes per workgroup (odd and even counts, ragged last block)."""
+    monkeypatch.setenv("RQ_GEMV_NPASS", npass)
+    for f in (S.INT4_G64, S.ASYM4_G32):
+        p = small(f, 1000, 512, tag=5)
+        x = x_for(2, 512, seed=7)
+        T.say(f"npass={npass} {f.tag}")
+        y = T.run("gemv", p, x)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"npass={npass} {f.tag}")
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "4", "16"])
+@pytest.mark.parametrize("nt", ["1", "2"])
+def test_gemm_split_and_tiles(monkeypatch, splits, nt):
+    monkeypatch.setenv("RQ_GEMM_SPLITS", splits)
+    monkeypatch.setenv("RQ_GEMM_NT", nt)
+    for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
+        p = small(f, 300, 4096, tag=6)
+        for M in (16, 33, 64):
+            T.say(f"gemm splits={splits} nt={nt} {f.tag} M={M}")
+            x = x_for(M, 4096, seed=M)
+            y = T.run("gemm", p, x)
+            yr, b = T.oracle_y(p, x)
+            T.assert_close(y, yr, b, f"splits={splits} nt={nt} {f.tag} M={M}")
+
+
+# ------------------------------------------------------ exact cases ---
+@pytest.mark.parametrize("f", [S.INT4_G64, S.INT8_G16, S.ASYM4_G32], ids=lambda f: f.tag)
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_one_hot_is_bit_exact(f, entry):
+    """x rows = e_j: every output is one weight, reached without rounding."""
+    N, K = 200, 1024
+    p = small(f, N, K, tag=7)
+    w = T.dequant(p).cpu()
+    for M in (1, 16, 64):
+        js = torch.arange(M) * 37 % K
+        x = torch.zeros((M, K), dtype=torch.float16)
+        x[torch.arange(M), js] = 1.0
+        T.say(f"one-hot {entry} {f.tag} M={M}")
+        y = T.run(entry, p, x.cuda()).cpu()
+        assert torch.equal(y, w[:, js].T.contiguous()), f"{entry} {f.tag} M={M}"
+
+
+@pytest.mark.parametrize("f", [S.INT4_G64, S.INT8_G16, S.ASYM4_G32], ids=lambda f: f.tag)
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_integer_inputs_are_exact(f, entry):
+    """Unit scales and small integer x: every partial sum is an exact integer
+    in binary32, so y must equal the integer matmul of the unpacked codes."""
+    N, K = 96, 2048
+    p, codes = S.gen_matrix(91, 0, 0, N, K, f, keep_codes=True)
+    if f.layout == S.LAYOUT_SYM:
+        p = S.encode(codes, f, scales=torch.ones((N, K // f.group), dtype=torch.float16))
+        W = codes.to(torch.int64)
+    else:
+        B = K // 256
+        g = torch.Generator().manual_seed(5)
+        sc = torch.randint(0, 64, (N, B, 8), generator=g, dtype=torch.int16).to(torch.uint8)
+        mn = torch.randint(0, 64, (N, B, 8), generator=g, dtype=torch.int16).to(torch.uint8)
+        one = torch.ones((N, B), dtype=torch.float16)
+        p = S.encode(codes, f, d=one, sc=sc, m=one, mn=mn)
+        sck = sc.reshape(N, B * 8).repeat_interleave(32, dim=1).to(torch.int64)
+        mnk = mn.reshape(N, B * 8).repeat_interleave(32, dim=1).to(torch.int64)
+        W = sck * codes.to(torch.int64) - mnk
+    p = T.to_dev(p)
+    for M in (1, 4, 16, 64):
+        g = torch.Generator().manual_seed(M)
+        xi = torch.randint(-4, 5, (M, K), generator=g)
+        T.say(f"integer {entry} {f.tag} M={M}")
+        y = T.run(entry, p, xi.half().cuda()).cpu()
+        expect = (xi.to(torch.int64) @ W.T).to(torch.float64)
+        assert torch.equal(y.to(torch.float64), expect), f"{entry} {f.tag} M={M}"
+
+
+# ------------------------------------------------------ contract details ---
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_guard_bands_untouched_and_deterministic(entry):
+    f = S.INT4_G64
+    N, K, M, PAD = 333, 4096, 24, 64
+    p = small(f, N, K, tag=8)
+    x = x_for(M, K, seed=3)
+    big = torch.full((M * N + 2 * PAD,), float("nan"), dtype=torch.float32, device="cuda")
+    big.view(torch.int32)[:PAD] = 0x7FC0DEAD
+    big.view(torch.int32)[-PAD:] = 0x7FC0BEEF
+    y = big[PAD:PAD + M * N].view(M, N)
+    T.say(f"guard {entry}")
+    T.run(entry, p, x, y)
+    torch.cuda.synchronize()
+    gi = big.view(torch.int32).cpu()
+    assert torch.all(gi[:PAD] == 0x7FC0DEAD) and torch.all(gi[-PAD:] == 0x7FC0BEEF)
+    y1 = y.clone()
+    T.run(entry, p, x, y)
+    assert torch.equal(y1.view(torch.int32), y.view(torch.int32)), "not deterministic"
+    yr, b = T.oracle_y(p, x)
+    T.assert_close(y, yr, b, f"guard {entry}")
+
+
+def test_misaligned_output_is_rejected_and_untouched():
+    p = small(S.INT4_G64, 64, 256, tag=9)
+    x = x_for(1, 256, seed=1)
+    buf = torch.zeros(65, dtype=torch.float32, device="cuda")
+    with pytest.raises(rq.RqError) as e:
+        rq.rq_gemv(p.qweight, p.scales, None, x, buf[1:], 1, 64, 256, 4, 64, 0)
+    assert e.value.status == rq.RQ_ERR_ALIGN
+    assert torch.count_nonzero(buf).item() == 0
+
+
+def test_side_stream():
+    p = small(S.INT8_G16, 512, 2048, tag=10)
+    x = x_for(16, 2048, seed=2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y1 = T.run("gemv", p, x)
+        y2 = T.run("gemm", p, x)
+    s.synchronize()
+    yr, b = T.oracle_y(p, x)
+    T.assert_close(y1, yr, b, "side stream gemv")
+    T.assert_close(y2, yr, b, "side stream gemm")
