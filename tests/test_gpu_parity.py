@@ -81,8 +81,9 @@ def test_dequant_subnormal_and_extreme_values(f):
         lo = -8 if f.bits == 4 else -128
         codes[:, ::5] = lo
         sc = p.scales.clone().view(torch.int16)
-        special = torch.tensor([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF - 0x10000, 0x0400,
-                                0x0000, -0x8000], dtype=torch.int16)
+        bits16 = [0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x0400, 0x0000, 0x8000]
+        special = torch.tensor([b - 0x10000 if b >= 0x8000 else b for b in bits16],
+                               dtype=torch.int16)
         sc.view(-1)[: special.numel() * 3] = special.repeat(3)
         p = S.encode(codes, f, scales=sc.view(torch.float16))
     else:
