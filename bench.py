@@ -26,6 +26,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "int4-g64 GEMV HBM GB/s (% of peak) at D=4096 M=1; TFLOP/s at M=32"
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 memory
+# counters; valid only while the kernel sources hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rq_gemv_int4g64_4096x16384_m1_traffic.json")
+KERNEL_SOURCES = ["gemm_rwkv_decode_amd/csrc/rq_gemv.hip",
+                  "gemm_rwkv_decode_amd/csrc/rq_common.h",
+                  "gemm_rwkv_decode_amd/csrc/rq_internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(shape):
+    """Counter-measured bytes per launch for `shape`, or None if absent or the
+    kernel has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash() or t.get("shape") != shape:
+        return None
+    return t.get("bytes_per_launch")
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
@@ -41,11 +69,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--m32-steps", type=int, default=20)
     ap.add_argument("--graph", action="store_true",
-                    help="replay the step as a captured graph instead of direct launches")
+                    help="replay each step as a captured graph instead of direct launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2,
                     help="layers of the step the CPU oracle times")
     ap.add_argument("--layers", type=int, default=None, help="(testing) fewer layers")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first copy 64 MiB with rq_probe_copy (the reference kernel "
+                         "for scaling the memory-traffic counters)")
     return ap.parse_args()
 
 
@@ -62,6 +93,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        a = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            rq.lib().rq_probe_copy(a.data_ptr(), b.data_ptr(), 64 << 20,
+                                   torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        del a, b
     cfg = S.CONFIGS[4]
     fmt = S.INT4_G64
     mats = cfg.matrices()
@@ -71,9 +110,7 @@ def main():
 
     # ---- inputs, resident in HBM --------------------------------------------
     t0 = time.time()
-    W = []
-    for (l, mi, N, K) in mats:
-        W.append(S.gen_matrix(cfg.cid, l, mi, N, K, fmt, device=dev))
+    W = [S.gen_matrix(cfg.cid, l, mi, N, K, fmt, device=dev) for (l, mi, N, K) in mats]
     X1 = [S.gen_x(cfg, l, mi, 1, K, device=dev) for (l, mi, N, K) in mats]
     X32 = [S.gen_x(cfg, l, mi, 32, K, device=dev) for (l, mi, N, K) in mats]
     Y1 = [torch.empty((1, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
@@ -87,71 +124,128 @@ def main():
         return weight_bytes + sum(2 * M * K + 4 * M * N for (_, _, N, K) in mats)
 
     flops_per_m = sum(2 * N * K for (_, _, N, K) in mats)
+    B, G, LAY = 4, 64, 0
 
-    def step(M):
-        X, Y = (X1, Y1) if M == 1 else (X32, Y32)
-        f = rq.rq_gemv if M < 16 else rq.rq_gemm_smallm
-        for p, x, y, (_, _, N, K) in zip(W, X, Y, mats):
-            f(p.qweight, p.scales, None, x, y, M, N, K, 4, 64, 0)
+    def prob(i, M):  # noqa: E306
+        p = W[i]
+        (_, _, N, K) = mats[i]
+        x, y = (X1[i], Y1[i]) if M == 1 else (X32[i], Y32[i])
+        return (p.qweight, p.scales, None, x, y, N, K)
 
-    def timed(M, steps, warmup, graph):
-        for _ in range(warmup):
-            step(M)
-        torch.cuda.synchronize()
-        run = lambda: step(M)  # noqa: E731
+    def schedule(kind, M, stream=None):
+        """Prepared calls of one step, in execution order, on `stream`."""
+        calls = []
+        prep = lambda *a: rq.prepare(*a, stream=stream)  # noqa: E731
+        entry = "rq_gemv" if M < 16 else "rq_gemm_smallm"
+        if kind == "layer" and M < 16:
+            # per layer: receptance/key/value in one launch, then output,
+            # FFN key, FFN value -- the dependency order of a decode step
+            by_layer = {}
+            for i, (l, mi, N, K) in enumerate(mats):
+                by_layer.setdefault(l, {})[mi] = i
+            for l in sorted(by_layer):
+                ix = by_layer[l]
+                calls.append(prep("rq_gemv_batched", [prob(ix[m], M) for m in (0, 1, 2)],
+                                  M, B, G, LAY))
+                for m in (3, 4, 5):
+                    q = prob(ix[m], M)
+                    calls.append(prep(entry, *q[:5], M, q[5], q[6], B, G, LAY))
+        elif kind == "batched":
+            # every product of the step through the grouped entry point
+            ps = [prob(i, M) for i in range(len(mats))]
+            for k in range(0, len(ps), rq.RQ_MAX_BATCH):
+                calls.append(prep("rq_gemv_batched", ps[k:k + rq.RQ_MAX_BATCH], M, B, G, LAY))
+        else:  # one launch per matrix
+            for i in range(len(mats)):
+                q = prob(i, M)
+                calls.append(prep(entry, *q[:5], M, q[5], q[6], B, G, LAY))
+        return calls
+
+    def timed(kind, M, steps, warmup, graph):
+        """Seconds per step.  Graph mode prepares the calls on a side stream,
+        captures one step there and replays it."""
         if graph:
-            g = torch.cuda.CUDAGraph()
             s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
+            calls = schedule(kind, M, stream=s)
             with torch.cuda.stream(s):
-                step(M)  # the split-K workspace is allocated outside capture
+                for _ in range(warmup):
+                    for c in calls:
+                        c()
                 torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s):
-                    step(M)
+                    for c in calls:
+                        c()
             torch.cuda.synchronize()
             run = g.replay
-            for _ in range(warmup):
-                run()
-            torch.cuda.synchronize()
+        else:
+            calls = schedule(kind, M)
+
+            def run():
+                for c in calls:
+                    c()
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
         t = time.perf_counter()
         for _ in range(steps):
             run()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t) / steps
+        return (time.perf_counter() - t) / steps, len(calls)
 
-    # ---- M = 1: the headline ------------------------------------------------
-    log("timing M=1")
-    sec1 = timed(1, args.steps, args.warmup, args.graph)
+    # ---- M = 1: the headline (dependency-ordered decode step) ---------------
+    scheds = {}
+    for kind in ("layer", "matrix", "batched"):
+        log(f"timing M=1 schedule {kind}")
+        sec, ncalls = timed(kind, 1, args.steps, args.warmup, args.graph)
+        scheds[kind] = {"launch_calls": ncalls, "ms_per_step": round(sec * 1e3, 4),
+                        "GBps": round(step_bytes(1) / sec / 1e9, 2)}
+    sec1 = scheds["layer"]["ms_per_step"] * 1e-3
     gbs = step_bytes(1) / sec1 / 1e9
 
-    # ---- per-kernel durations with events (same launches, same stream) -----
-    log("per-kernel events")
-    shapes = {}
-    for _ in range(3):
-        evs = []
-        stream = torch.cuda.current_stream()
-        for p, x, y, (_, _, N, K) in zip(W, X1, Y1, mats):
+    # ---- per-shape launch time: events around back-to-back launches of one
+    # shape over all layers (distinct, cold matrices), same stream -----------
+    log("per-shape events")
+    per_kernel = {}
+    groups = {"rkv batched 3x(4096x4096)": [], "4096x4096": [], "16384x4096": [],
+              "4096x16384": []}
+    by_layer = {}
+    for i, (l, mi, N, K) in enumerate(mats):
+        by_layer.setdefault(l, {})[mi] = i
+    for l in sorted(by_layer):
+        ix = by_layer[l]
+        groups["rkv batched 3x(4096x4096)"].append(
+            rq.prepare("rq_gemv_batched", [prob(ix[m], 1) for m in (0, 1, 2)], 1, B, G, LAY))
+        for m, key in ((3, "4096x4096"), (4, "16384x4096"), (5, "4096x16384")):
+            q = prob(ix[m], 1)
+            groups[key].append(rq.prepare("rq_gemv", *q[:5], 1, q[5], q[6], B, G, LAY))
+    nbytes = {"rkv batched 3x(4096x4096)": 3 * (fmt.weight_bytes(4096, 4096) + 2 * 4096 + 4 * 4096),
+              "4096x4096": fmt.weight_bytes(4096, 4096) + 2 * 4096 + 4 * 4096,
+              "16384x4096": fmt.weight_bytes(16384, 4096) + 2 * 4096 + 4 * 16384,
+              "4096x16384": fmt.weight_bytes(4096, 16384) + 2 * 16384 + 4 * 4096}
+    stream = torch.cuda.current_stream()
+    for key, calls in groups.items():
+        for c in calls[:4]:
+            c()
+        ts = []
+        for _ in range(3):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            rq.rq_gemv(p.qweight, p.scales, None, x, y, 1, N, K, 4, 64, 0)
+            for c in calls:
+                c()
             b.record(stream)
-            evs.append(((N, K), a, b))
-        torch.cuda.synchronize()
-        for key, a, b in evs:
-            shapes.setdefault(key, []).append(a.elapsed_time(b) * 1e-3)
-    per_kernel = {}
-    for (N, K), ts in shapes.items():
-        avg = sum(ts) / len(ts)
-        nbytes = fmt.weight_bytes(N, K) + 2 * K + 4 * N
-        per_kernel[f"{N}x{K}"] = {"avg_us": avg * 1e6, "launches_per_step": len(ts) // 3,
-                                  "bytes": nbytes, "GBps": nbytes / avg / 1e9}
-    dom = max(per_kernel.items(), key=lambda kv: kv[1]["avg_us"] * kv[1]["launches_per_step"])
-    dom_name, dom_v = dom
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3 / len(calls))
+        avg = min(ts)
+        per_kernel[key] = {"us_per_launch": round(avg * 1e6, 3), "launches_per_step": len(calls),
+                           "bytes": nbytes[key], "GBps": round(nbytes[key] / avg / 1e9, 1)}
+    dom_name, dom_v = max(per_kernel.items(),
+                          key=lambda kv: kv[1]["us_per_launch"] * kv[1]["launches_per_step"])
 
     # ---- M = 32 (matrix cores) ---------------------------------------------
     log("timing M=32")
-    sec32 = timed(32, args.m32_steps, 2, args.graph)
+    sec32, _ = timed("matrix", 32, args.m32_steps, 2, args.graph)
     tflops32 = 32 * flops_per_m / sec32 / 1e12
 
     # ---- CPU oracle on a bounded sample of the same step --------------------
@@ -188,6 +282,9 @@ def main():
         "data": "synthetic (seeded, generated on the GPU)",
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "launch_mode": "graph" if args.graph else "stream",
+        "schedule": "per layer: one grouped launch for receptance/key/value, then output, "
+                    "FFN key, FFN value (244 launches per step)",
+        "schedules_m1": scheds,
         "config": {"workload": "RWKV-7 13.3B-shaped decode weight stream, int4 sym g64",
                    "layers": nlayers, "matrices": len(mats), "M": 1,
                    "shapes": "per layer 4x(4096x4096), 16384x4096, 4096x16384",
@@ -196,12 +293,13 @@ def main():
                 "tflops": round(tflops32, 2),
                 "pct_of_fp16_mfma_peak": round(100 * tflops32 / FP16_MFMA_PEAK_TFLOPS, 2),
                 "GBps": round(step_bytes(32) / sec32 / 1e9, 2)},
-        "per_kernel_m1": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv
-                              for kk, vv in v.items()} for k, v in per_kernel.items()},
-        "roofline": {"bound": "hbm", "kernel": f"rq_gemv int4 g64 {dom_name} M=1",
-                     "achieved": round(dom_v["GBps"], 1), "peak": HBM_PEAK_GBS,
+        "per_shape_m1": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": f"int4 g64 GEMV {dom_name}, M=1",
+                     "achieved": dom_v["GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_v["GBps"] / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(dom_name),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, "
+                                     "scaled by a 64 MiB copy)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

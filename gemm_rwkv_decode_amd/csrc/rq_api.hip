@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <map>
@@ -12,6 +13,30 @@
 #include "rq.h"
 #include "rq_common.h"
 #include "rq_internal.h"
+#include "rq_probe.h"
+
+namespace rq {
+
+static Tuning g_tuning;
+static std::once_flag g_tuning_once;
+
+static int env_or_zero(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
+static void read_tuning() {
+  g_tuning = Tuning{env_or_zero("RQ_GEMV_LPR"), env_or_zero("RQ_GEMV_CPL"),
+                    env_or_zero("RQ_GEMV_NPASS"), env_or_zero("RQ_GEMM_NT"),
+                    env_or_zero("RQ_GEMM_SPLITS")};
+}
+
+const Tuning& tuning() {
+  std::call_once(g_tuning_once, read_tuning);
+  return g_tuning;
+}
+
+}  // namespace rq
 
 namespace {
 
@@ -59,6 +84,8 @@ rq_status check_weights(const void* qweight, const void* scales, const void* zer
   if (layout == RQ_LAYOUT_SYM && zeros) return RQ_ERR_UNSUPPORTED;
   if (N < 1 || K < group || K % group != 0) return RQ_ERR_SHAPE;
   if (((size_t)K * bits / 8) % 16 != 0) return RQ_ERR_SHAPE;
+  // kernels index within an operand with 32-bit offsets
+  if (code_bytes(N, K, bits) >= ((size_t)1 << 31)) return RQ_ERR_SHAPE;
   if (layout == RQ_LAYOUT_ASYM_SB && K % 256 != 0) return RQ_ERR_SHAPE;
   if (!aligned16(qweight) || !aligned16(scales) || (zeros && !aligned16(zeros)))
     return RQ_ERR_ALIGN;
@@ -78,7 +105,8 @@ rq_status check_output(const void* out, size_t out_bytes, const void* qweight,
   return RQ_OK;
 }
 
-// The current device must be a gfx950; checked once per device.
+// The current device must be a gfx950; checked once per device (the verdict
+// is shared; each thread also remembers its last device and verdict).
 rq_status check_device(int* dev_out) {
   static std::mutex mu;
   static int verdict[64];  // 0 unknown, 1 ok, 2 unusable
@@ -86,6 +114,11 @@ rq_status check_device(int* dev_out) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return RQ_ERR_DEVICE;
+  }
+  thread_local int last_ok_dev = -1;
+  if (dev == last_ok_dev) {
+    *dev_out = dev;
+    return RQ_OK;
   }
   std::lock_guard<std::mutex> lk(mu);
   if (verdict[dev] == 0) {
@@ -97,25 +130,25 @@ rq_status check_device(int* dev_out) {
     verdict[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
   }
   if (verdict[dev] != 1) return RQ_ERR_DEVICE;
+  last_ok_dev = dev;
   *dev_out = dev;
   return RQ_OK;
 }
 
 // Split-K workspace: one per (device, stream), grown on demand, never freed.
+// Calls on one stream are ordered, so they may share it; calls on different
+// streams get different buffers.
 struct Workspace {
   float* partial = nullptr;
   size_t floats = 0;
-  unsigned* counters = nullptr;
-  size_t ncounters = 0;
 };
 
-rq_status get_workspace(int dev, hipStream_t stream, size_t floats, size_t ncounters,
-                        Workspace* out) {
+rq_status get_workspace(int dev, hipStream_t stream, size_t floats, Workspace* out) {
   static std::mutex mu;
   static std::map<std::pair<int, hipStream_t>, Workspace> cache;
   std::lock_guard<std::mutex> lk(mu);
   Workspace& w = cache[std::make_pair(dev, stream)];
-  if (w.floats >= floats && w.ncounters >= ncounters) {
+  if (w.floats >= floats) {
     *out = w;
     return RQ_OK;
   }
@@ -123,30 +156,20 @@ rq_status get_workspace(int dev, hipStream_t stream, size_t floats, size_t ncoun
   if (stream && hipStreamIsCapturing(stream, &cs) == hipSuccess &&
       cs != hipStreamCaptureStatusNone)
     return RQ_ERR_DEVICE;  // cannot allocate while a graph is being captured
-  const size_t want_f = floats > ((size_t)4 << 20) ? floats : ((size_t)4 << 20);
-  const size_t want_c = ncounters > 65536 ? ncounters : 65536;
-  if (hipDeviceSynchronize() != hipSuccess) return RQ_ERR_DEVICE;
-  if (w.partial) (void)hipFree(w.partial);
-  if (w.counters) (void)hipFree(w.counters);
+  const size_t want = floats > ((size_t)4 << 20) ? floats : ((size_t)4 << 20);
+  // the old buffer may still be in use by work queued on this stream
+  if (w.partial) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return RQ_ERR_DEVICE;
+    (void)hipFree(w.partial);
+  }
   w = Workspace{};
   float* p = nullptr;
-  unsigned* c = nullptr;
-  if (hipMalloc(&p, want_f * sizeof(float)) != hipSuccess) {
+  if (hipMalloc(&p, want * sizeof(float)) != hipSuccess) {
     (void)hipGetLastError();
-    return RQ_ERR_DEVICE;
-  }
-  if (hipMalloc(&c, want_c * sizeof(unsigned)) != hipSuccess ||
-      hipMemset(c, 0, want_c * sizeof(unsigned)) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
-    (void)hipGetLastError();
-    (void)hipFree(p);
-    if (c) (void)hipFree(c);
     return RQ_ERR_DEVICE;
   }
   w.partial = p;
-  w.floats = want_f;
-  w.counters = c;
-  w.ncounters = want_c;
+  w.floats = want;
   *out = w;
   return RQ_OK;
 }
@@ -158,6 +181,8 @@ rq_status check_product(const void* qweight, const void* scales, const void* zer
   rq_status st = check_weights(qweight, scales, zeros, N, K, bits, group, layout, fmt);
   if (st != RQ_OK) return st;
   if (M < 1 || M > RQ_MAX_M) return RQ_ERR_SHAPE;
+  if ((size_t)M * K * 2 >= ((size_t)1 << 31) || (size_t)M * N * 4 >= ((size_t)1 << 31))
+    return RQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(y)) return RQ_ERR_ALIGN;
   return check_output(y, (size_t)M * N * 4, qweight, scales, zeros, x, N, K, bits, group,
                       layout, M);
@@ -203,6 +228,58 @@ rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 
+rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits,
+                          int group, int layout, void* stream) {
+  if (!problems) return RQ_ERR_NULL;
+  if (count < 1 || count > RQ_MAX_BATCH) return RQ_ERR_SHAPE;
+  int fmt = -1;
+  for (int i = 0; i < count; i++) {
+    const rq_problem& q = problems[i];
+    rq_status st = check_product(q.qweight, q.scales, q.zeros, q.x, q.y, M, q.N, q.K, bits,
+                                 group, layout, &fmt);
+    if (st != RQ_OK) return st;
+  }
+  // outputs against the other problems' inputs and outputs
+  for (int i = 0; i < count; i++) {
+    const rq_problem& a = problems[i];
+    for (int j = 0; j < count; j++) {
+      if (j == i) continue;
+      const rq_problem& b = problems[j];
+      rq_status st = check_output(a.y, (size_t)M * a.N * 4, b.qweight, b.scales, b.zeros,
+                                  b.x, b.N, b.K, bits, group, layout, M);
+      if (st != RQ_OK) return st;
+      if (overlaps(range_of(a.y, (size_t)M * a.N * 4), range_of(b.y, (size_t)M * b.N * 4)))
+        return RQ_ERR_ALIAS;
+    }
+  }
+  int dev;
+  rq_status st = check_device(&dev);
+  if (st != RQ_OK) return st;
+  // group by K (launch shapes depend on K), keeping the caller's order within
+  rq::Problem pb[RQ_MAX_BATCH];
+  const rq::Problem* order[RQ_MAX_BATCH];
+  bool done[RQ_MAX_BATCH] = {false};
+  for (int i = 0; i < count; i++) {
+    const rq_problem& q = problems[i];
+    pb[i] = rq::Problem{q.qweight, q.scales, q.zeros, q.x, q.y, M, q.N, q.K, group, fmt};
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < count; i++) {
+    if (done[i]) continue;
+    int n = 0, rows = 0;
+    for (int j = i; j < count; j++) {
+      if (!done[j] && pb[j].K == pb[i].K) {
+        order[n++] = &pb[j];
+        rows += pb[j].N;
+        done[j] = true;
+      }
+    }
+    const rq::GemvCfg c = rq::choose_gemv(fmt, M, rows, pb[i].K);
+    if (rq::launch_gemv_many(order, n, c, s) != hipSuccess) return RQ_ERR_LAUNCH;
+  }
+  return RQ_OK;
+}
+
 rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* zeros,
                          const void* x, float* y, int M, int N, int K, int bits,
                          int group, int layout, void* stream) {
@@ -215,7 +292,7 @@ rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* ze
   if (st != RQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   rq::Problem p{qweight, scales, zeros, x, y, M, N, K, group, fmt};
-  if (!rq::gemm_supports(fmt, M, K)) {
+  if (!rq::gemm_supports(fmt, M, K, group)) {
     // K is not a whole number of the matrix-core kernel's chunks
     const rq::GemvCfg c = rq::choose_gemv(fmt, M, N, K);
     return rq::launch_gemv(p, c, s) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
@@ -223,11 +300,10 @@ rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* ze
   const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
   Workspace w;
   if (c.splits > 1) {
-    st = get_workspace(dev, s, rq::gemm_workspace_floats(c, M, N),
-                       (size_t)rq::gemm_counters(c, N), &w);
+    st = get_workspace(dev, s, rq::gemm_workspace_floats(c, M, N), &w);
     if (st != RQ_OK) return st;
   }
-  const hipError_t e = rq::launch_gemm(p, c, w.partial, w.counters, s);
+  const hipError_t e = rq::launch_gemm(p, c, w.partial, s);
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 
@@ -246,5 +322,11 @@ const char* rq_status_string(int status) {
 }
 
 int rq_version(void) { return (1 << 16) | 0; }
+
+int rq_tuning_reload(void) {
+  rq::tuning();  // make sure the one-time read has happened
+  rq::read_tuning();
+  return RQ_OK;
+}
 
 }  // extern "C"

@@ -56,13 +56,17 @@ __device__ __forceinline__ u32 load_stream4(const void* p) {
 // two's complement codes (-8..7); otherwise codes are unsigned (0..15).
 template <bool SIGNED>
 __device__ __forceinline__ void unpack4(u32 d, h2 q[4]) {
-  if (SIGNED) d ^= 0x88888888u;  // two's complement nibble -> q + 8
-  const u32 lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+  // (d & mask) ^ key: the AND keeps one nibble per half-word, the XOR both
+  // flips the two's-complement sign bit (q -> q + 8) and sets the exponent
+  // bits of 1024.0 (they lie outside the mask) -- one three-input bit op.
+  const u32 lo = 0x000F000Fu, hi = 0x00F000F0u;
+  const u32 key_lo = SIGNED ? 0x64086408u : 0x64006400u;
+  const u32 key_hi = SIGNED ? 0x64806480u : 0x64006400u;
   const u32 d2 = d >> 8;
-  const u32 t0 = (d & lo) | magic;   // 1024 + u0, 1024 + u4
-  const u32 t1 = (d & hi) | magic;   // 1024 + 16 u1, 1024 + 16 u5
-  const u32 t2 = (d2 & lo) | magic;  // 1024 + u2, 1024 + u6
-  const u32 t3 = (d2 & hi) | magic;  // 1024 + 16 u3, 1024 + 16 u7
+  const u32 t0 = (d & lo) ^ key_lo;   // 1024 + u0, 1024 + u4
+  const u32 t1 = (d & hi) ^ key_hi;   // 1024 + 16 u1, 1024 + 16 u5
+  const u32 t2 = (d2 & lo) ^ key_lo;  // 1024 + u2, 1024 + u6
+  const u32 t3 = (d2 & hi) ^ key_hi;  // 1024 + 16 u3, 1024 + 16 u7
   const _Float16 b0 = SIGNED ? (_Float16)-1032.0f : (_Float16)-1024.0f;
   const _Float16 b1 = SIGNED ? (_Float16)-72.0f : (_Float16)-64.0f;
   const h2 bias0 = {b0, b0};
@@ -112,12 +116,24 @@ __device__ __forceinline__ float record_value(u32x2 r, int j) {
   return half_lo(r.x) * (float)sub;
 }
 
-// Sum over the LPR consecutive lanes of a row group; every lane of the group
-// receives the total.  LPR is a power of two <= 64.
+// Sum over the LPR consecutive lanes of a row group (LPR a power of two <=
+// 64); every lane of the group receives the total.  Within a row of 16 lanes
+// the exchanges are DPP moves (quad swaps, half-row and row mirrors); wider
+// groups finish with cross-row shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, LPR);
+  if constexpr (LPR >= 2) v += dpp_mov<0xB1>(v);   // quad_perm(1,0,3,2): lane ^ 1
+  if constexpr (LPR >= 4) v += dpp_mov<0x4E>(v);   // quad_perm(2,3,0,1): lane ^ 2
+  if constexpr (LPR >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror: i <-> 7 - i
+  if constexpr (LPR >= 16) v += dpp_mov<0x140>(v); // row_mirror: i <-> 15 - i
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 

@@ -25,22 +25,27 @@
 // per chunk), shared by the four waves; codes and scales of chunk c+1 are
 // loaded into registers while chunk c is multiplied.
 //
-// Split-K reduction.  Every K-range writes its partial tile to a workspace;
-// the workgroup that finishes last for a row block (atomic counter) adds the
-// partials in K-range order and stores y, then resets the counter.  Results
-// are therefore deterministic.  No workgroup waits for another.
+// Split-K reduction.  When the K dimension is split, every K-range writes its
+// partial tile to a workspace with plain stores and a second, small kernel
+// adds the partials in K-range order into y.  Results are deterministic; no
+// workgroup waits for another and no device-wide fence is needed (a fence per
+// workgroup would write the whole L2 back each time).
 #include "rq_common.h"
 #include "rq_internal.h"
 
-#include <stdlib.h>
 
 namespace rq {
 
 constexpr int GEMM_WAVES = 4;
 
-// k per LDS chunk of x: 128 for 8-bit codes and for M > 32 (keeps the double
-// buffered x tile and the register image of the next chunk small), else 256.
-constexpr int gemm_kc(int fmt, int mt) { return (fmt == FMT_S8 || mt >= 3) ? 128 : 256; }
+// k per LDS chunk of x.  Larger chunks put more code bytes in flight per
+// wave (the next chunk is loaded while this one is multiplied); the double
+// buffered x tile is 2 * 16*MT * (KC+8) halves.
+// At most 8 groups per chunk: every group of a chunk is unrolled.
+constexpr int gemm_kc(int fmt, int mt, int g) {
+  const int base = fmt == FMT_S8 ? (mt >= 3 ? 128 : 256) : (mt >= 3 ? 256 : 512);
+  return base < 8 * g ? base : 8 * g;
+}
 
 template <int FMT>
 struct MfmaT {
@@ -197,21 +202,24 @@ __device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
 #pragma unroll
   for (int g = 0; g < GPC; g++) {
     f4 P[NT][MT];
+    // A fragments of every K-step of the group and every M-tile, read from
+    // LDS before the first MFMA so the reads overlap each other
+    u32 a[DPG][MT][4];
 #pragma unroll
-    for (int s = 0; s < DPG; s++) {
-      // A fragments of this K-step for every M-tile
-      u32 a[MT][4];
+    for (int s = 0; s < DPG; s++)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
         const _Float16* src = xb + (mt * 16 + col) * XSTR + g * G + h * QPL + s * (KS / 4);
         if constexpr (FMT == FMT_S8) {
           const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-          a[mt][0] = v.x; a[mt][1] = v.y;
+          a[s][mt][0] = v.x; a[s][mt][1] = v.y;
         } else {
           const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-          a[mt][0] = v.x; a[mt][1] = v.y; a[mt][2] = v.z; a[mt][3] = v.w;
+          a[s][mt][0] = v.x; a[s][mt][1] = v.y; a[s][mt][2] = v.z; a[s][mt][3] = v.w;
         }
       }
+#pragma unroll
+    for (int s = 0; s < DPG; s++) {
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         u32 b[4];
@@ -228,7 +236,7 @@ __device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
         }
 #pragma unroll
         for (int mt = 0; mt < MT; mt++)
-          P[nt][mt] = mfma_step<FMT>(a[mt], b, s == 0 ? f4{0, 0, 0, 0} : P[nt][mt]);
+          P[nt][mt] = mfma_step<FMT>(a[s][mt], b, s == 0 ? f4{0, 0, 0, 0} : P[nt][mt]);
       }
     }
     // group epilogue in binary32
@@ -259,6 +267,9 @@ __device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
         }
       }
     }
+    // keep the scheduler from hoisting later groups' LDS reads into this one
+    // (it would hold every group's fragments in registers at once)
+    if constexpr (MT * NT >= 4) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -266,8 +277,7 @@ template <int FMT, int MT, int NT, int KC, int G>
 __global__ void __launch_bounds__(64 * GEMM_WAVES)
 k_gemm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
        const void* __restrict__ zeros, const _Float16* __restrict__ x,
-       float* __restrict__ y, float* __restrict__ ws, unsigned* __restrict__ counters,
-       int M, int N, int K, int kr) {
+       float* __restrict__ out, int M, int N, int K, int kr) {
   constexpr int MP = 16 * MT;
   constexpr int XSTR = KC + 8;
   constexpr int XSN = (FMT == FMT_A4) ? (KC / 32) * MP : 4;
@@ -275,15 +285,15 @@ k_gemm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
 
   __shared__ __attribute__((aligned(16))) _Float16 xl[2][MP * XSTR];
   __shared__ __attribute__((aligned(16))) float xsum[2][XSN];
-  __shared__ unsigned last_flag;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 4;
   const int col = lane & 15;
   const int split = blockIdx.y;
-  const int splits = gridDim.y;
   const int k_begin = split * kr;
+  // y itself, or this K-range's slice of the partial-sum workspace
+  float* __restrict__ y = out + (size_t)split * M * N;
   const int nchunks = kr / KC;
   const int row_base = blockIdx.x * (64 * NT) + wave * (16 * NT);
 
@@ -328,20 +338,6 @@ k_gemm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
   }
 
   // ---- write out -----------------------------------------------------------
-  if (splits == 1) {
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++) {
-      const int n = row_base + nt * 16 + col;
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int m = mt * 16 + 4 * h + i;
-          if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i];
-        }
-    }
-    return;
-  }
 #pragma unroll
   for (int nt = 0; nt < NT; nt++) {
     const int n = row_base + nt * 16 + col;
@@ -350,34 +346,21 @@ k_gemm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int m = mt * 16 + 4 * h + i;
-        if (m < M && n < N) ws[((size_t)split * M + m) * N + n] = acc[nt][mt][i];
+        if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i];
       }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&counters[blockIdx.x], 1u);
-    last_flag = (prev == (unsigned)(splits - 1)) ? 1u : 0u;
+}
+
+// y[i] = sum over K-ranges s = 0..splits-1 (in order) of ws[s][i], i < count.
+__global__ void __launch_bounds__(256)
+k_split_reduce(const float* __restrict__ ws, float* __restrict__ y, size_t count,
+               int splits) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (size_t)gridDim.x * blockDim.x) {
+    float v = 0.0f;
+    for (int sp = 0; sp < splits; sp++) v += ws[(size_t)sp * count + i];
+    y[i] = v;
   }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-#pragma unroll
-  for (int nt = 0; nt < NT; nt++) {
-    const int n = row_base + nt * 16 + col;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = mt * 16 + 4 * h + i;
-        if (m < M && n < N) {
-          float v = 0.0f;
-          for (int sp = 0; sp < splits; sp++) v += ws[((size_t)sp * M + m) * N + n];
-          y[(size_t)m * N + n] = v;
-        }
-      }
-  }
-  if (threadIdx.x == 0) counters[blockIdx.x] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -387,30 +370,28 @@ size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
   return c.splits > 1 ? (size_t)c.splits * M * N : 0;
 }
 
-int gemm_counters(const GemmCfg& c, int N) {
-  const int rb = 64 * c.nt;
-  return (N + rb - 1) / rb;
-}
 
-bool gemm_supports(int fmt, int M, int K) {
+bool gemm_supports(int fmt, int M, int K, int group) {
   const int mt = (M + 15) / 16;
-  return K % gemm_kc(fmt, mt) == 0;
+  return K % gemm_kc(fmt, mt, group) == 0;
 }
 
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
-  (void)group;
   GemmCfg c{};
   c.mt = (M + 15) / 16;
-  c.nt = 1;
-  const char* e = getenv("RQ_GEMM_NT");
-  if (e) c.nt = atoi(e) == 1 ? 1 : 2;
+  c.nt = 1;  // two N-tiles per wave measured slower (registers, occupancy)
+  const Tuning& tu = tuning();
+  if (tu.gemm_nt) c.nt = tu.gemm_nt == 1 ? 1 : 2;
+  if (c.mt > 2) c.nt = 1;
   const int rowblocks = (N + 64 * c.nt - 1) / (64 * c.nt);
-  const int kc = gemm_kc(fmt, c.mt);
+  const int kc = gemm_kc(fmt, c.mt, group);
   const int maxsplit = K / kc;  // the caller has checked K % kc == 0
-  // enough workgroups for every CU; splits must divide K into whole chunks
-  int want = (256 + rowblocks - 1) / rowblocks;
-  e = getenv("RQ_GEMM_SPLITS");
-  if (e) want = atoi(e);
+  // About 256 workgroups (512 for K >= 8192, whose rows are long enough to
+  // split further), measured best on MI355X for the RWKV-7 shapes; splits must
+  // divide K into whole chunks and the partial sums stay under 64 MiB.
+  const int target = (K >= 8192) ? 512 : 256;
+  int want = (target + rowblocks - 1) / rowblocks;
+  if (tu.gemm_splits) want = tu.gemm_splits;
   if (want > maxsplit) want = maxsplit;
   if (want < 1) want = 1;
   int s = want;
@@ -420,48 +401,53 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
 }
 
 template <int FMT, int MT, int NT, int G>
-static void launch_g(const Problem& p, const GemmCfg& c, float* ws, unsigned* counters,
-                     hipStream_t s) {
-  constexpr int KC = gemm_kc(FMT, MT);
+static void launch_g(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+  constexpr int KC = gemm_kc(FMT, MT, G);
   const int rowblocks = (p.N + 64 * NT - 1) / (64 * NT);
   const int kr = p.K / c.splits;
+  float* out = (c.splits > 1) ? ws : p.y;
   hipLaunchKernelGGL((k_gemm<FMT, MT, NT, KC, G>), dim3(rowblocks, c.splits),
                      dim3(64 * GEMM_WAVES), 0, s, static_cast<const uint8_t*>(p.qweight),
-                     p.scales, p.zeros, static_cast<const _Float16*>(p.x), p.y, ws,
-                     counters, p.M, p.N, p.K, kr);
+                     p.scales, p.zeros, static_cast<const _Float16*>(p.x), out, p.M, p.N,
+                     p.K, kr);
+  if (c.splits > 1) {
+    const size_t count = (size_t)p.M * p.N;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, ws, p.y,
+                       count, c.splits);
+  }
 }
 
 template <int FMT, int MT, int NT>
-static void launch_group(const Problem& p, const GemmCfg& c, float* ws, unsigned* counters,
-                         hipStream_t s) {
+static void launch_group(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
   if constexpr (FMT == FMT_S8) {
-    if (p.group == 16) return launch_g<FMT, MT, NT, 16>(p, c, ws, counters, s);
-    if (p.group == 32) return launch_g<FMT, MT, NT, 32>(p, c, ws, counters, s);
-    return launch_g<FMT, MT, NT, 64>(p, c, ws, counters, s);
+    if (p.group == 16) return launch_g<FMT, MT, NT, 16>(p, c, ws, s);
+    if (p.group == 32) return launch_g<FMT, MT, NT, 32>(p, c, ws, s);
+    return launch_g<FMT, MT, NT, 64>(p, c, ws, s);
   } else if constexpr (FMT == FMT_A4) {
-    return launch_g<FMT, MT, NT, 32>(p, c, ws, counters, s);
+    return launch_g<FMT, MT, NT, 32>(p, c, ws, s);
   } else {
-    if (p.group == 32) return launch_g<FMT, MT, NT, 32>(p, c, ws, counters, s);
-    if (p.group == 64) return launch_g<FMT, MT, NT, 64>(p, c, ws, counters, s);
-    return launch_g<FMT, MT, NT, 128>(p, c, ws, counters, s);
+    if (p.group == 32) return launch_g<FMT, MT, NT, 32>(p, c, ws, s);
+    if (p.group == 64) return launch_g<FMT, MT, NT, 64>(p, c, ws, s);
+    return launch_g<FMT, MT, NT, 128>(p, c, ws, s);
   }
 }
 
 template <int FMT>
-static void launch_fmt(const Problem& p, const GemmCfg& c, float* ws, unsigned* counters,
-                       hipStream_t s) {
+static void launch_fmt(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
 #define RQ_G(MT_, NT_) \
-  if (c.mt == MT_ && c.nt == NT_) return launch_group<FMT, MT_, NT_>(p, c, ws, counters, s)
+  if (c.mt == MT_ && c.nt == NT_) return launch_group<FMT, MT_, NT_>(p, c, ws, s)
+  // two N-tiles per wave only up to M = 32 (above, the registers run out)
+  RQ_G(1, 2); RQ_G(2, 2);
   RQ_G(1, 1); RQ_G(2, 1); RQ_G(3, 1); RQ_G(4, 1);
-  RQ_G(1, 2); RQ_G(2, 2); RQ_G(3, 2); RQ_G(4, 2);
 #undef RQ_G
 }
 
-hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, unsigned* counters,
-                       hipStream_t s) {
-  if (p.fmt == FMT_S4) launch_fmt<FMT_S4>(p, c, ws, counters, s);
-  else if (p.fmt == FMT_S8) launch_fmt<FMT_S8>(p, c, ws, counters, s);
-  else launch_fmt<FMT_A4>(p, c, ws, counters, s);
+hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+  if (p.fmt == FMT_S4) launch_fmt<FMT_S4>(p, c, ws, s);
+  else if (p.fmt == FMT_S8) launch_fmt<FMT_S8>(p, c, ws, s);
+  else launch_fmt<FMT_A4>(p, c, ws, s);
   return hipGetLastError();
 }
 

@@ -10,8 +10,9 @@
 //     so that the LPR lanes of a row read one contiguous run of LPR*16 bytes;
 //   * the activations a lane needs (its chunks of x for every row of M) are
 //     loaded once into registers and reused for every weight row;
-//   * the block's rows are visited in `npass` passes; the code loads of pass
-//     p+1 are issued before pass p is computed (two passes in flight).
+//   * a lane visits NP rows of the block and issues the code loads of all of
+//     them (NP*CPL 16-byte loads) before it waits for the first: the loads of
+//     a small matrix are all in flight at once.
 //
 // Arithmetic per 16-byte chunk: codes become exact binary16 integers
 // (rq_common.h), v_dot2_f32_f16 multiplies them by binary16 x and accumulates
@@ -21,7 +22,6 @@
 #include "rq_common.h"
 #include "rq_internal.h"
 
-#include <stdlib.h>
 
 namespace rq {
 
@@ -118,99 +118,202 @@ __device__ __forceinline__ void load_pass(PassData<FMT, CPL>& pd,
   }
 }
 
-// Largest workgroup: 16 waves for one activation row, 8 waves above (the
-// activation registers grow with M and a smaller workgroup leaves each wave
-// more of the register file).
-template <int MT>
-struct GemvMax {
-  static constexpr int threads = (MT >= 2) ? 512 : 1024;
+// Problems of one launch: they share the format, K and M; blocks
+// [block_begin, next block_begin) belong to entry i.
+struct GemvEntry {
+  const uint8_t* qw;
+  const uint8_t* sc;
+  const uint8_t* zr;
+  const _Float16* x;
+  float* y;
+  int N;
+  int block_begin;
 };
 
-template <int FMT, int LPR, int CPL, int MT>
-__device__ __forceinline__ void gemv_pass(const PassData<FMT, CPL>& pd,
-                                          const h2 (&xr)[MT][CPL][Chunk<FMT>::codes / 2],
-                                          const float (&xs)[MT][CPL], float* __restrict__ y,
-                                          float* part, int p, int row0, int RB, int w,
-                                          int SK, int rs, int li, int Mrows, int N) {
-  constexpr int RPW = 64 / LPR;
-  float acc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; m++) acc[m] = 0.0f;
-#pragma unroll
-  for (int c = 0; c < CPL; c++) {
-#pragma unroll
-    for (int m = 0; m < MT; m++) {
-      const float d = chunk_dot<FMT>(pd.code[c], xr[m][c]);
-      acc[m] = __builtin_fmaf(d, pd.s[c], acc[m]);
-      if (FMT == FMT_A4) acc[m] = __builtin_fmaf(-pd.t[c], xs[m][c], acc[m]);
-    }
-  }
-  const int n = row0 + p * RPW + rs;
-#pragma unroll
-  for (int m = 0; m < MT; m++) {
-    const float v = group_sum<LPR>(acc[m]);
-    if (li == 0) {
-      if (SK == 1) {
-        if (m < Mrows && n < N) y[(size_t)m * N + n] = v;
-      } else {
-        part[((size_t)w * RB + p * RPW + rs) * MT + m] = v;
-      }
-    }
-  }
+template <int B>
+struct GemvBatch {
+  GemvEntry e[B];
+  int count;
+};
+
+// Raw scale material of one chunk, kept undecoded until it is used so that
+// no wait on its load stands between the loads of a wave.
+template <int FMT>
+struct ScaleRaw {
+  u32x2 s;  // sym: binary16 bits in s.x; asym: scale record
+  u32x2 z;  // asym: zero record
+};
+
+// Largest workgroup: the activation registers grow with MT*CPL, and a smaller
+// workgroup leaves each wave more of the register file.
+constexpr int gemv_max_threads(int mt, int cpl) {
+  return (mt * cpl >= 4) ? 256 : (mt * cpl >= 2 ? 512 : 1024);
 }
 
-template <int FMT, int LPR, int CPL, int MT>
-__global__ void __launch_bounds__(GemvMax<MT>::threads)
-k_gemv(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
-       const void* __restrict__ zeros, const _Float16* __restrict__ x,
-       float* __restrict__ y, int Mrows, int N, int K, int group, int npass) {
+// One workgroup: SK waves (one K-slice each) x RB = (64/LPR)*NP rows.  Every
+// lane issues the loads of all NP rows it visits before it waits for any of
+// them: NP*CPL 16-byte code loads in flight per lane.
+//
+// Offsets are 32-bit (the host keeps every operand below 2 GiB), so loads use
+// a scalar base plus a vector offset.  `ssh` turns a row's code offset into
+// its scale offset: a row holds K*bits/8 code bytes and 2K/group scale bytes
+// (sym) or K/32 record bytes (asym), a power-of-two ratio.  `gsh` = log2 of
+// the group size.
+template <int FMT, int LPR, int CPL, int MT, int NP, int B>
+__global__ void __launch_bounds__(gemv_max_threads(MT, CPL))
+k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
   constexpr int RPW = 64 / LPR;
+  constexpr int RB = RPW * NP;
   constexpr int CPC = Chunk<FMT>::codes;
   constexpr int XP = CPC / 2;
   extern __shared__ float part[];  // [SK][RB][MT]
+
+  // the problem this workgroup belongs to (uniform scan of the table)
+  const uint8_t* __restrict__ qw = bt.e[0].qw;
+  const uint8_t* __restrict__ scales = bt.e[0].sc;
+  const uint8_t* __restrict__ zeros = bt.e[0].zr;
+  const _Float16* __restrict__ x = bt.e[0].x;
+  float* __restrict__ y = bt.e[0].y;
+  int N = bt.e[0].N;
+  int block0 = 0;
+#pragma unroll
+  for (int i = 1; i < B; i++) {
+    if (i < bt.count && (int)blockIdx.x >= bt.e[i].block_begin) {
+      qw = bt.e[i].qw;
+      scales = bt.e[i].sc;
+      zeros = bt.e[i].zr;
+      x = bt.e[i].x;
+      y = bt.e[i].y;
+      N = bt.e[i].N;
+      block0 = bt.e[i].block_begin;
+    }
+  }
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int SK = blockDim.x >> 6;
   const int rs = lane / LPR;
   const int li = lane % LPR;
-  const int RB = RPW * npass;
-  const int row0 = blockIdx.x * RB;
+  const int row0 = ((int)blockIdx.x - block0) * RB;
+  const u32 row_bytes = (FMT == FMT_S8) ? (u32)K : (u32)K / 2;
 
   int kc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; c++) kc[c] = w * (LPR * CPL) + c * LPR + li;
 
+  u32 roff[NP];  // code offset of each visited row
+#pragma unroll
+  for (int p = 0; p < NP; p++) roff[p] = (u32)min(row0 + p * RPW + rs, N - 1) * row_bytes;
+
+  // 1. codes of every row this lane visits
+  u32x4 code[NP][CPL];
+#pragma unroll
+  for (int p = 0; p < NP; p++)
+#pragma unroll
+    for (int c = 0; c < CPL; c++) code[p][c] = load_stream16(qw + (roff[p] + kc[c] * 16u));
+  __builtin_amdgcn_sched_barrier(0);  // keep the code loads ahead of everything else
+  // 2. their scale material
+  ScaleRaw<FMT> sr[NP][CPL];
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const u32 srow = roff[p] >> ssh;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      const u32 k0 = (u32)kc[c] * CPC;
+      if constexpr (FMT == FMT_A4) {
+        const u32 o = srow + (k0 / SUPERBLOCK) * 8u;
+        sr[p][c].s = *reinterpret_cast<const u32x2*>(scales + o);
+        sr[p][c].z = *reinterpret_cast<const u32x2*>(zeros + o);
+      } else {
+        sr[p][c].s.x = *reinterpret_cast<const uint16_t*>(scales + srow + ((k0 >> gsh) << 1));
+        sr[p][c].s.y = 0;
+        sr[p][c].z = u32x2{0, 0};
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. the activations of this lane's chunks: all raw loads first, then the
+  //    pairing (a wait inside the load loop would also wait for the codes)
+  constexpr int XV = CPC / 8;  // 16-byte pieces of x per chunk
+  u32x4 xraw[MT][CPL][XV];
+#pragma unroll
+  for (int m = 0; m < MT; m++) {
+    // rows past Mrows re-read the last row (always valid) and are zeroed
+    // after the loads, so no branch or wait sits between the loads
+    const u32 mm = (MT == 1) ? 0u : (u32)min(m, Mrows - 1);
+#pragma unroll
+    for (int c = 0; c < CPL; c++)
+#pragma unroll
+      for (int v = 0; v < XV; v++)
+        xraw[m][c][v] = reinterpret_cast<const u32x4*>(x + (mm * (u32)K + kc[c] * CPC))[v];
+  }
+#pragma unroll
+  for (int m = 1; m < MT; m++)
+    if (m >= Mrows)
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int v = 0; v < XV; v++) xraw[m][c][v] = u32x4{0, 0, 0, 0};
+  __builtin_amdgcn_sched_barrier(0);
   h2 xr[MT][CPL][XP];
   float xs[MT][CPL];
 #pragma unroll
   for (int m = 0; m < MT; m++) {
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
-      if (m < Mrows) {
-        load_x_chunk<FMT>(x + (size_t)m * K, kc[c] * CPC, xr[m][c], &xs[m][c]);
-      } else {
+      float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < XP; i++) xr[m][c][i] = h2{0, 0};
-        xs[m][c] = 0.0f;
+      for (int v = 0; v < XV; v++) {
+        const u32x4 wv = xraw[m][c][v];
+        if constexpr (FMT == FMT_S8) {
+          xr[m][c][4 * v + 0] = as_h2(wv.x);
+          xr[m][c][4 * v + 1] = as_h2(wv.y);
+          xr[m][c][4 * v + 2] = as_h2(wv.z);
+          xr[m][c][4 * v + 3] = as_h2(wv.w);
+        } else {
+          pair_x4(wv.x, wv.y, wv.z, wv.w, &xr[m][c][4 * v]);
+        }
+        if constexpr (FMT == FMT_A4)
+          sum += half_lo(wv.x) + half_hi(wv.x) + half_lo(wv.y) + half_hi(wv.y) +
+                 half_lo(wv.z) + half_hi(wv.z) + half_lo(wv.w) + half_hi(wv.w);
       }
+      xs[m][c] = sum;
     }
   }
-
-  // two passes in flight: b0 holds even passes, b1 odd ones
-  PassData<FMT, CPL> b0, b1;
-  load_pass<FMT, CPL>(b0, qw, scales, zeros, min(row0 + rs, N - 1), K, group, kc);
-  for (int p = 0; p < npass; p += 2) {
-    if (p + 1 < npass)
-      load_pass<FMT, CPL>(b1, qw, scales, zeros, min(row0 + (p + 1) * RPW + rs, N - 1), K,
-                          group, kc);
-    gemv_pass<FMT, LPR, CPL, MT>(b0, xr, xs, y, part, p, row0, RB, w, SK, rs, li, Mrows, N);
-    if (p + 1 < npass) {
-      if (p + 2 < npass)
-        load_pass<FMT, CPL>(b0, qw, scales, zeros, min(row0 + (p + 2) * RPW + rs, N - 1),
-                            K, group, kc);
-      gemv_pass<FMT, LPR, CPL, MT>(b1, xr, xs, y, part, p + 1, row0, RB, w, SK, rs, li,
-                                   Mrows, N);
+  // 4. multiply, row by row
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; m++) acc[m] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      float sc, t = 0.0f;
+      if constexpr (FMT == FMT_A4) {
+        const int j = ((kc[c] * CPC) % SUPERBLOCK) / SB_GROUP;
+        sc = record_value(sr[p][c].s, j);
+        t = record_value(sr[p][c].z, j);
+      } else {
+        sc = half_lo(sr[p][c].s.x);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; m++) {
+        const float d = chunk_dot<FMT>(code[p][c], xr[m][c]);
+        acc[m] = __builtin_fmaf(d, sc, acc[m]);
+        if (FMT == FMT_A4) acc[m] = __builtin_fmaf(-t, xs[m][c], acc[m]);
+      }
+    }
+    const int n = row0 + p * RPW + rs;
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      const float v = group_sum<LPR>(acc[m]);
+      if (li == 0) {
+        if (SK == 1) {
+          if (m < Mrows && n < N) y[(u32)m * (u32)N + (u32)n] = v;
+        } else {
+          part[(w * RB + p * RPW + rs) * MT + m] = v;
+        }
+      }
     }
   }
 
@@ -219,9 +322,9 @@ k_gemv(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
     for (int idx = threadIdx.x; idx < RB * Mrows; idx += blockDim.x) {
       const int r = idx / Mrows, m = idx % Mrows;
       float v = 0.0f;
-      for (int ww = 0; ww < SK; ww++) v += part[((size_t)ww * RB + r) * MT + m];
+      for (int ww = 0; ww < SK; ww++) v += part[(ww * RB + r) * MT + m];
       const int n = row0 + r;
-      if (n < N) y[(size_t)m * N + n] = v;
+      if (n < N) y[(u32)m * (u32)N + (u32)n] = v;
     }
   }
 }
@@ -271,100 +374,196 @@ k_gemv_generic(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : dflt;
+static int ilog2(int v) {
+  int r = 0;
+  while ((1 << (r + 1)) <= v) r++;
+  return r;
 }
 
+
+// Launch shapes.  A lane streams NP rows x CPL chunks; a wave covers 64/LPR
+// rows and one K-slice of LPR*CPL chunks; a workgroup stacks the K-slices of
+// a row block.  The table lists (LPR, CPL, NP) per activation-row count in
+// order of preference; the first that splits the row into at most the
+// allowed number of waves and gives at least 256 workgroups (or the most) wins.
 GemvCfg choose_gemv(int fmt, int M, int N, int K) {
   GemvCfg c{};
   // activation rows per launch: the smallest of 1, 2, 4, 8 covering M (or 8)
   c.mt = M <= 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));
   const int chunks = (fmt == FMT_S8) ? K / 16 : K / 32;
-  // Lane splits tried in order; the first whose wave count fits is taken.
-  static const int pref[][2] = {{16, 1}, {32, 1}, {64, 1}, {8, 1},
-                                {16, 2}, {32, 2}, {64, 2}, {8, 2}};
-  c.lpr = 0;
-  const int max_waves = (c.mt >= 2) ? 8 : 16;  // GemvMax
-  for (auto& pr : pref) {
-    const int lpr = pr[0], cpl = pr[1];
-    if (c.mt >= 8 && cpl > 1) continue;  // keep x registers bounded
+  // measured on MI355X (C4 shapes, cold): one 16-byte chunk per lane and four
+  // rows per lane beat wider per-lane slices, whose extra registers cost
+  // occupancy
+  static const int cand1[][3] = {{16, 1, 4}, {32, 1, 4}, {64, 1, 4}, {16, 1, 8},
+                                 {32, 1, 8}, {64, 1, 8}, {16, 2, 4}, {8, 1, 4},
+                                 {8, 1, 8}, {16, 1, 2}, {32, 1, 2}, {64, 1, 2},
+                                 {8, 1, 2}, {8, 2, 4}, {8, 4, 2}, {16, 1, 1},
+                                 {32, 1, 1}, {64, 1, 1}, {8, 1, 1}};
+  static const int cand2[][3] = {{16, 1, 4}, {32, 1, 4}, {8, 1, 4}, {64, 1, 4},
+                                 {16, 1, 2}, {32, 1, 2}, {8, 1, 2}, {64, 1, 2},
+                                 {16, 1, 1}, {32, 1, 1}, {8, 1, 1}, {64, 1, 1}};
+  int best = -1, best_blocks = 0;
+  const int (*cand)[3] = (c.mt == 1) ? cand1 : cand2;
+  const int ncand = (c.mt == 1) ? (int)(sizeof(cand1) / sizeof(cand1[0]))
+                                : (int)(sizeof(cand2) / sizeof(cand2[0]));
+  for (int i = 0; i < ncand; i++) {
+    const int lpr = cand[i][0], cpl = cand[i][1], np = cand[i][2];
     if (chunks % (lpr * cpl)) continue;
     const int sk = chunks / (lpr * cpl);
-    if (sk < 1 || sk > max_waves) continue;
-    c.lpr = lpr;
-    c.cpl = cpl;
-    break;
+    if (sk < 1 || sk > gemv_max_threads(c.mt, cpl) / 64) continue;
+    const int blocks = (N + (64 / lpr) * np - 1) / ((64 / lpr) * np);
+    if (blocks >= 256) { best = i; break; }
+    if (blocks > best_blocks) { best = i; best_blocks = blocks; }
   }
-  const int forced = env_int("RQ_GEMV_LPR", 0);
-  if (forced < 0) c.lpr = 0;  // force the generic kernel (testing)
-  if (c.lpr == 0) {
+  const Tuning& tu = tuning();
+  const int forced = tu.gemv_lpr;
+  if (best < 0 || forced < 0) {  // no usable split: the generic kernel
+    c.lpr = 0;
     c.cpl = 1;
     c.npass = 1;
     return c;
   }
-  // Rows per workgroup: enough workgroups to fill the chip twice over.
-  const int rpw = 64 / c.lpr;
-  int npass = N / (rpw * 512);
-  npass = npass < 1 ? 1 : (npass > 8 ? 8 : npass);
-  c.npass = env_int("RQ_GEMV_NPASS", npass);
+  c.lpr = cand[best][0];
+  c.cpl = cand[best][1];
+  c.npass = cand[best][2];
+  if (forced > 0) {  // tuning: RQ_GEMV_LPR / RQ_GEMV_CPL / RQ_GEMV_NPASS
+    const int cpl = tu.gemv_cpl ? tu.gemv_cpl : c.cpl;
+    if (chunks % (forced * cpl) == 0 &&
+        chunks / (forced * cpl) <= gemv_max_threads(c.mt, cpl) / 64) {
+      c.lpr = forced;
+      c.cpl = cpl;
+    }
+  }
+  const int np = tu.gemv_npass ? tu.gemv_npass : c.npass;
+  if (np == 1 || np == 2 || np == 4 || np == 8) c.npass = np;
+  if (c.mt >= 4 && c.npass > 4) c.npass = 4;
   return c;
 }
 
-template <int FMT, int LPR, int CPL, int MT>
-static void launch_t(const Problem& p, const GemvCfg& c, const _Float16* x, float* y,
-                     int mrows, hipStream_t s) {
-  const int chunks = (FMT == FMT_S8) ? p.K / 16 : p.K / 32;
+// One launch over up to B problems sharing K (x and y already offset to the
+// activation rows of this launch).
+struct Launch {
+  const Problem* p[GEMV_BATCH];
+  const _Float16* x[GEMV_BATCH];
+  float* y[GEMV_BATCH];
+  int count;
+  int K, group, mrows;
+};
+
+template <int FMT, int LPR, int CPL, int MT, int NP>
+static void launch_t(const Launch& L, hipStream_t s) {
+  const int chunks = (FMT == FMT_S8) ? L.K / 16 : L.K / 32;
   const int sk = chunks / (LPR * CPL);
-  const int rb = (64 / LPR) * c.npass;
-  const int blocks = (p.N + rb - 1) / rb;
+  constexpr int rb = (64 / LPR) * NP;
   const size_t lds = (sk > 1) ? (size_t)sk * rb * MT * sizeof(float) : 0;
-  hipLaunchKernelGGL((k_gemv<FMT, LPR, CPL, MT>), dim3(blocks), dim3(64 * sk), lds, s,
-                     static_cast<const uint8_t*>(p.qweight), p.scales, p.zeros, x, y,
-                     mrows, p.N, p.K, p.group, c.npass);
+  const int gsh = ilog2(L.group);
+  // code bytes per row : scale bytes per row = 2^ssh
+  //   int4 sym: (K/2)/(2K/G) = G/4; int8 sym: K/(2K/G) = G/2; asym: (K/2)/(K/32) = 16
+  const int ssh = (FMT == FMT_A4) ? 4 : (FMT == FMT_S8 ? gsh - 1 : gsh - 2);
+  auto fill = [&](GemvEntry* e, int* blocks) {
+    int b = 0;
+    for (int i = 0; i < L.count; i++) {
+      e[i] = GemvEntry{static_cast<const uint8_t*>(L.p[i]->qweight),
+                       static_cast<const uint8_t*>(L.p[i]->scales),
+                       static_cast<const uint8_t*>(L.p[i]->zeros), L.x[i], L.y[i],
+                       L.p[i]->N, b};
+      b += (L.p[i]->N + rb - 1) / rb;
+    }
+    *blocks = b;
+  };
+  int blocks = 0;
+  if (L.count == 1) {
+    GemvBatch<1> bt{};
+    fill(bt.e, &blocks);
+    bt.count = 1;
+    hipLaunchKernelGGL((k_gemv<FMT, LPR, CPL, MT, NP, 1>), dim3(blocks), dim3(64 * sk), lds,
+                       s, bt, L.mrows, L.K, gsh, ssh);
+  } else {
+    GemvBatch<GEMV_BATCH> bt{};
+    fill(bt.e, &blocks);
+    bt.count = L.count;
+    hipLaunchKernelGGL((k_gemv<FMT, LPR, CPL, MT, NP, GEMV_BATCH>), dim3(blocks),
+                       dim3(64 * sk), lds, s, bt, L.mrows, L.K, gsh, ssh);
+  }
+}
+
+template <int FMT, int LPR, int CPL, int MT>
+static void launch_np(const Launch& L, const GemvCfg& c, hipStream_t s) {
+  switch (c.npass) {
+    case 1: return launch_t<FMT, LPR, CPL, MT, 1>(L, s);
+    case 2: return launch_t<FMT, LPR, CPL, MT, 2>(L, s);
+    case 4: return launch_t<FMT, LPR, CPL, MT, 4>(L, s);
+    default:
+      if constexpr (MT < 4 && CPL == 1) return launch_t<FMT, LPR, CPL, MT, 8>(L, s);
+      else return launch_t<FMT, LPR, CPL, MT, 4>(L, s);
+  }
 }
 
 template <int FMT, int MT>
-static void launch_mt(const Problem& p, const GemvCfg& c, const _Float16* x, float* y,
-                      int mrows, hipStream_t s) {
-  if (c.lpr == 0) {
+static void launch_generic(const Launch& L, hipStream_t s) {
+  for (int i = 0; i < L.count; i++) {
+    const Problem& p = *L.p[i];
     const int blocks = (p.N * 16 + 255) / 256;
     hipLaunchKernelGGL((k_gemv_generic<FMT, MT>), dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(p.qweight), p.scales, p.zeros, x, y,
-                       mrows, p.N, p.K, p.group);
-    return;
+                       static_cast<const uint8_t*>(p.qweight), p.scales, p.zeros, L.x[i],
+                       L.y[i], L.mrows, p.N, p.K, p.group);
   }
-#define RQ_L(L, C) \
-  if (c.lpr == L && c.cpl == C) return launch_t<FMT, L, C, MT>(p, c, x, y, mrows, s)
-  RQ_L(16, 1); RQ_L(32, 1); RQ_L(64, 1); RQ_L(8, 1);
-  if constexpr (MT < 8) { RQ_L(16, 2); RQ_L(32, 2); RQ_L(64, 2); RQ_L(8, 2); }
+}
+
+template <int FMT, int MT>
+static void launch_mt(const Launch& L, const GemvCfg& c, hipStream_t s) {
+  if (c.lpr == 0) return launch_generic<FMT, MT>(L, s);
+#define RQ_L(LP, C) \
+  if (c.lpr == LP && c.cpl == C) return launch_np<FMT, LP, C, MT>(L, c, s)
+  RQ_L(8, 1); RQ_L(16, 1); RQ_L(32, 1); RQ_L(64, 1);
+  if constexpr (MT == 1) { RQ_L(8, 2); RQ_L(16, 2); RQ_L(8, 4); }
 #undef RQ_L
+  // a forced combination that is not instantiated: the generic kernel
+  launch_generic<FMT, MT>(L, s);
 }
 
 template <int FMT>
-static void launch_fmt(const Problem& p, const GemvCfg& c, const _Float16* x, float* y,
-                       int mrows, hipStream_t s) {
+static void launch_fmt(const Launch& L, const GemvCfg& c, hipStream_t s) {
   switch (c.mt) {
-    case 1: return launch_mt<FMT, 1>(p, c, x, y, mrows, s);
-    case 2: return launch_mt<FMT, 2>(p, c, x, y, mrows, s);
-    case 4: return launch_mt<FMT, 4>(p, c, x, y, mrows, s);
-    default: return launch_mt<FMT, 8>(p, c, x, y, mrows, s);
+    case 1: return launch_mt<FMT, 1>(L, c, s);
+    case 2: return launch_mt<FMT, 2>(L, c, s);
+    case 4: return launch_mt<FMT, 4>(L, c, s);
+    default: return launch_mt<FMT, 8>(L, c, s);
   }
 }
 
-hipError_t launch_gemv(const Problem& p, const GemvCfg& c, hipStream_t s) {
-  const _Float16* x = static_cast<const _Float16*>(p.x);
-  for (int m0 = 0; m0 < p.M; m0 += c.mt) {
-    const int mrows = (p.M - m0 < c.mt) ? p.M - m0 : c.mt;
-    const _Float16* xm = x + (size_t)m0 * p.K;
-    float* ym = p.y + (size_t)m0 * p.N;
-    if (p.fmt == FMT_S4) launch_fmt<FMT_S4>(p, c, xm, ym, mrows, s);
-    else if (p.fmt == FMT_S8) launch_fmt<FMT_S8>(p, c, xm, ym, mrows, s);
-    else launch_fmt<FMT_A4>(p, c, xm, ym, mrows, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+// Problems p[0..count) share fmt, K, group and M; launches cover up to
+// GEMV_BATCH of them each, in passes of c.mt activation rows.
+hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c,
+                            hipStream_t s) {
+  const int M = p[0]->M, K = p[0]->K;
+  for (int first = 0; first < count; first += GEMV_BATCH) {
+    const int n = (count - first < GEMV_BATCH) ? count - first : GEMV_BATCH;
+    for (int m0 = 0; m0 < M; m0 += c.mt) {
+      Launch L{};
+      L.count = n;
+      L.K = K;
+      L.group = p[0]->group;
+      L.mrows = (M - m0 < c.mt) ? M - m0 : c.mt;
+      for (int i = 0; i < n; i++) {
+        const Problem* q = p[first + i];
+        L.p[i] = q;
+        L.x[i] = static_cast<const _Float16*>(q->x) + (size_t)m0 * K;
+        L.y[i] = q->y + (size_t)m0 * q->N;
+      }
+      if (p[0]->fmt == FMT_S4) launch_fmt<FMT_S4>(L, c, s);
+      else if (p[0]->fmt == FMT_S8) launch_fmt<FMT_S8>(L, c, s);
+      else launch_fmt<FMT_A4>(L, c, s);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemv(const Problem& p, const GemvCfg& c, hipStream_t s) {
+  const Problem* one = &p;
+  return launch_gemv_many(&one, 1, c, s);
 }
 
 }  // namespace rq

@@ -6,6 +6,14 @@
 
 namespace rq {
 
+// Launch-shape overrides for measurements and tests, read from the
+// environment once (RQ_GEMV_LPR, RQ_GEMV_CPL, RQ_GEMV_NPASS, RQ_GEMM_NT,
+// RQ_GEMM_SPLITS; 0 = no override) and again on rq_tuning_reload().
+struct Tuning {
+  int gemv_lpr, gemv_cpl, gemv_npass, gemm_nt, gemm_splits;
+};
+const Tuning& tuning();
+
 struct Problem {
   const void* qweight;
   const void* scales;
@@ -24,8 +32,15 @@ struct GemvCfg {
   int mt;     // activation rows per launch (1, 2, 4, 8)
 };
 
+// Problems per GEMV launch of a batch.
+constexpr int GEMV_BATCH = 16;
+
+// N is the largest row count of the problems sharing the launch.
 GemvCfg choose_gemv(int fmt, int M, int N, int K);
 hipError_t launch_gemv(const Problem& p, const GemvCfg& c, hipStream_t s);
+// count problems sharing fmt, K, group and M
+hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c,
+                            hipStream_t s);
 
 struct GemmCfg {
   int nt;      // 16-row N-tiles per wave (4 waves per workgroup)
@@ -34,15 +49,12 @@ struct GemmCfg {
 };
 
 // The matrix-core kernel needs K to be a whole number of its LDS chunks.
-bool gemm_supports(int fmt, int M, int K);
+bool gemm_supports(int fmt, int M, int K, int group);
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group);
-// ws: float workspace of at least splits*M*N entries; counters: zeroed
-// unsigned array with at least ceil(N / (64*nt)) entries.  Both unused when
-// splits == 1.
-hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws,
-                       unsigned* counters, hipStream_t s);
+// ws: float workspace of at least splits*M*N entries (unused when
+// splits == 1).
+hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s);
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N);
-int gemm_counters(const GemmCfg& c, int N);
 
 hipError_t launch_dequant(const void* qweight, const void* scales, const void* zeros,
                           void* out, int N, int K, int group, int fmt, int out_kind,

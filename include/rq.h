@@ -38,8 +38,10 @@
  * the products are grouped, so there is exactly one right answer.
  *
  * Pointers.  Every pointer is device memory owned by the caller and must be
- * 16-byte aligned.  The library does not free or retain caller memory, never
- * copies to the host and never synchronizes: work is enqueued on `stream`
+ * 16-byte aligned.  Each operand (packed codes, scales, x, y) must be smaller
+ * than 2 GiB (RQ_ERR_SHAPE otherwise).  The library does not free or retain
+ * caller memory, never copies to the host and never synchronizes: work is
+ * enqueued on `stream`
  * (a hipStream_t; NULL means the null stream) and the call returns after the
  * enqueue.  Outputs must not overlap any input.
  *
@@ -76,8 +78,22 @@ typedef enum {
                            -128..127 (8-bit), 0..15 (asymmetric)                 */
 } rq_out_kind;
 
-/* Largest M accepted by rq_gemv and rq_gemm_smallm. */
+/* Largest M accepted by rq_gemv, rq_gemv_batched and rq_gemm_smallm. */
 #define RQ_MAX_M 64
+
+/* Largest number of problems in one rq_gemv_batched call. */
+#define RQ_MAX_BATCH 64
+
+/* One product y = x W^T of rq_gemv_batched (pointers as for rq_gemv). */
+typedef struct {
+    const void* qweight;
+    const void* scales;
+    const void* zeros;
+    const void* x; /* binary16 [M][K] */
+    float* y;      /* float [M][N], overwritten */
+    int N;
+    int K;
+} rq_problem;
 
 /*
  * rq_dequant -- unpack the codes of W, or dequantize W to binary32.
@@ -106,6 +122,21 @@ rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
 rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
                   const void* x, float* y, int M, int N, int K, int bits,
                   int group, int layout, void* stream);
+
+/*
+ * rq_gemv_batched -- `count` independent products, as `count` rq_gemv calls
+ * would compute them, issued as few kernel launches as possible: problems
+ * with the same K share one launch (up to 16 per launch).  This is the
+ * grouped form of the decode step's independent projections -- the package
+ * page "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization
+ * Details") computes the receptance, key and value projections of a layer in
+ * a single kernel.  All problems share M, bits, group and layout; N, K and the
+ * pointers are per problem.  `problems` is a host array the call reads before
+ * it returns.  No output may overlap another output or any input.
+ * Errors as for rq_gemv; a failed call enqueues nothing.
+ */
+rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits,
+                          int group, int layout, void* stream);
 
 /*
  * rq_gemm_smallm -- the same product and contract as rq_gemv, computed on the

@@ -149,3 +149,40 @@ def test_binding_rejects_host_tensors():
     t = torch.zeros(16, dtype=torch.uint8)
     with pytest.raises(ValueError):
         rq.rq_dequant(t, t, None, t, 1, 32, 4, 32, 0)
+
+
+class Prob(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+def _probs(*kws):
+    arr = (rq.RqProblem * len(kws))()
+    for i, kw in enumerate(kws):
+        a = dict(qw=A + (i << 32), sc=A + (i << 32) + (1 << 30), z=None,
+                 x=A + (i << 32) + (2 << 30), y=A + (i << 32) + (3 << 30), N=64, K=256)
+        a.update(kw)
+        arr[i] = rq.RqProblem(a["qw"], a["sc"], a["z"], a["x"], a["y"], a["N"], a["K"])
+    return arr
+
+
+@pytest.mark.parametrize("what,probs,count,M,status", [
+    ("null array", None, 1, 1, rq.RQ_ERR_NULL),
+    ("zero count", [{}], 0, 1, rq.RQ_ERR_SHAPE),
+    ("count above RQ_MAX_BATCH", [{}], 65, 1, rq.RQ_ERR_SHAPE),
+    ("M above 64", [{}, {}], 2, 65, rq.RQ_ERR_SHAPE),
+    ("second problem bad K", [{}, {"K": 96}], 2, 1, rq.RQ_ERR_SHAPE),
+    ("second problem null x", [{}, {"x": None}], 2, 1, rq.RQ_ERR_NULL),
+    ("outputs overlap", [{}, {"y": A + (3 << 30) + 64}], 2, 1, rq.RQ_ERR_ALIAS),
+    ("output overlaps another's x", [{}, {"y": A + (2 << 30) + 32}], 2, 1, rq.RQ_ERR_ALIAS),
+    ("misaligned y", [{}, {"y": A + (1 << 32) + (3 << 30) + 4}], 2, 1, rq.RQ_ERR_ALIGN),
+])
+def test_batched_rejects(L, what, probs, count, M, status):
+    arr = None if probs is None else _probs(*probs)
+    assert L.rq_gemv_batched(arr, count, M, 4, 64, 0, None) == status, what
+
+
+def test_codes_of_2gib_rejected(L):
+    # 65536 x 65536 int4 codes are exactly 2 GiB: beyond the 32-bit offsets
+    assert L.rq_gemv(*gemv_args(N=65536, K=65536)) == rq.RQ_ERR_SHAPE

@@ -27,6 +27,18 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+@pytest.fixture
+def tune(monkeypatch):
+    """Set launch-shape overrides for one test; restored (and re-read) after."""
+    def set_(**kv):
+        for k, v in kv.items():
+            monkeypatch.setenv(k, str(v))
+        rq.tuning_reload()
+    yield set_
+    monkeypatch.undo()
+    rq.tuning_reload()
+
+
 def small(fmt, N, K, tag=0):
     p = S.gen_matrix(90 + tag, 0, 0, N, K, fmt)
     return T.to_dev(p)
@@ -137,9 +149,9 @@ def test_product_parity_odd_k(N, K, f, entry):
         T.assert_close(y, yr, b, f"{entry} {f.tag} M={M} N={N} K={K}")
 
 
-def test_generic_kernel_forced(monkeypatch):
+def test_generic_kernel_forced(tune):
     """The generic kernel also serves shapes the tuned one handles."""
-    monkeypatch.setenv("RQ_GEMV_LPR", "-1")
+    tune(RQ_GEMV_LPR=-1)
     for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
         p = small(f, 45, 1024, tag=4)
         for M in (1, 5):
@@ -150,24 +162,28 @@ def test_generic_kernel_forced(monkeypatch):
             T.assert_close(y, yr, b, f"generic {f.tag} M={M}")
 
 
-@pytest.mark.parametrize("npass", ["1", "3", "8"])
-def test_gemv_pass_counts(monkeypatch, npass):
-    """Row passes per workgroup (odd and even counts, ragged last block)."""
-    monkeypatch.setenv("RQ_GEMV_NPASS", npass)
-    for f in (S.INT4_G64, S.ASYM4_G32):
+@pytest.mark.parametrize("lpr,cpl,npass", [(16, 1, 1), (16, 1, 2), (32, 1, 8), (8, 4, 2),
+                                           (16, 2, 4), (64, 1, 4), (8, 1, 8)])
+def test_gemv_launch_shapes(tune, lpr, cpl, npass):
+    """Every instantiated launch shape, with a ragged last row block."""
+    tune(RQ_GEMV_LPR=lpr, RQ_GEMV_CPL=cpl, RQ_GEMV_NPASS=npass)
+    for f in (S.INT4_G64, S.ASYM4_G32, S.INT8_G16):
         p = small(f, 1000, 512, tag=5)
         x = x_for(2, 512, seed=7)
-        T.say(f"npass={npass} {f.tag}")
+        T.say(f"lpr={lpr} cpl={cpl} npass={npass} {f.tag}")
         y = T.run("gemv", p, x)
         yr, b = T.oracle_y(p, x)
-        T.assert_close(y, yr, b, f"npass={npass} {f.tag}")
+        T.assert_close(y, yr, b, f"lpr={lpr} cpl={cpl} npass={npass} {f.tag}")
+        x1 = x_for(1, 512, seed=8)
+        y1 = T.run("gemv", p, x1)
+        yr1, b1 = T.oracle_y(p, x1)
+        T.assert_close(y1, yr1, b1, f"M=1 lpr={lpr} cpl={cpl} npass={npass} {f.tag}")
 
 
 @pytest.mark.parametrize("splits", ["1", "2", "4", "16"])
 @pytest.mark.parametrize("nt", ["1", "2"])
-def test_gemm_split_and_tiles(monkeypatch, splits, nt):
-    monkeypatch.setenv("RQ_GEMM_SPLITS", splits)
-    monkeypatch.setenv("RQ_GEMM_NT", nt)
+def test_gemm_split_and_tiles(tune, splits, nt):
+    tune(RQ_GEMM_SPLITS=splits, RQ_GEMM_NT=nt)
     for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
         p = small(f, 300, 4096, tag=6)
         for M in (16, 33, 64):
@@ -269,3 +285,53 @@ def test_side_stream():
     yr, b = T.oracle_y(p, x)
     T.assert_close(y1, yr, b, "side stream gemv")
     T.assert_close(y2, yr, b, "side stream gemm")
+
+
+# ------------------------------------------------------------ batched ---
+@pytest.mark.parametrize("f", [S.INT4_G64, S.INT8_G16, S.ASYM4_G32], ids=lambda f: f.tag)
+@pytest.mark.parametrize("M", [1, 3, 8, 17])
+def test_batched_matches_oracle(f, M):
+    """Mixed N and K in one call (K groups share launches), more problems than
+    one launch holds, and a K the tuned kernel cannot split."""
+    shapes = [(256, 1024), (100, 1024), (300, 2048), (64, 1024)] * 5 + [(40, 768)]
+    if f.layout == S.LAYOUT_SYM and f.bits == 4:
+        shapes.append((33, 64 * 7))  # 14 chunks: generic kernel
+    mats = [small(f, N, K, tag=20 + i) for i, (N, K) in enumerate(shapes)]
+    xs = [x_for(M, K, seed=100 + i) for i, (_, K) in enumerate(shapes)]
+    ys = [torch.full((M, N), float("nan"), device="cuda") for (N, _) in shapes]
+    T.say(f"batched {f.tag} M={M} count={len(shapes)}")
+    rq.rq_gemv_batched([(p.qweight, p.scales, p.zeros, x, y, p.N, p.K)
+                        for p, x, y in zip(mats, xs, ys)], M, f.bits, f.group, f.layout)
+    for i, (p, x, y) in enumerate(zip(mats, xs, ys)):
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"batched {f.tag} M={M} problem {i} {p.N}x{p.K}")
+
+
+def test_batched_rejects_overlapping_outputs():
+    p = small(S.INT4_G64, 64, 256, tag=40)
+    x = x_for(1, 256, seed=4)
+    y = torch.zeros(200, device="cuda")
+    with pytest.raises(rq.RqError) as e:
+        rq.rq_gemv_batched([(p.qweight, p.scales, None, x, y[:64], 64, 256),
+                            (p.qweight, p.scales, None, x, y[32:96], 64, 256)], 1, 4, 64, 0)
+    assert e.value.status == rq.RQ_ERR_ALIAS
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_prepared_calls_match_direct_calls():
+    f = S.INT4_G64
+    p = small(f, 512, 4096, tag=41)
+    x = x_for(1, 4096, seed=5)
+    x32 = x_for(32, 4096, seed=6)
+    y1 = torch.empty((1, 512), device="cuda")
+    y2 = torch.empty((32, 512), device="cuda")
+    c1 = rq.prepare("rq_gemv", p.qweight, p.scales, None, x, y1, 1, 512, 4096, 4, 64, 0)
+    c2 = rq.prepare("rq_gemm_smallm", p.qweight, p.scales, None, x32, y2, 32, 512, 4096, 4,
+                    64, 0)
+    c3 = rq.prepare("rq_gemv_batched", [(p.qweight, p.scales, None, x, y1, 512, 4096)], 1, 4,
+                    64, 0)
+    for c, y, xx in ((c1, y1, x), (c2, y2, x32), (c3, y1, x)):
+        y.fill_(float("nan"))
+        c()
+        yr, b = T.oracle_y(p, xx)
+        T.assert_close(y, yr, b, "prepared")
