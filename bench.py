@@ -2,12 +2,14 @@
 13.3B-shaped RWKV-7 model (61 layers x 6 quantized matrices at width 4096,
 FFN 16384), on one MI355X.
 
-One step = one pass of the decode hot path: every one of the 366 matrices is
-multiplied by its own activation row (M = 1) through rq_gemv, in layer order,
-on one stream.  Inputs (6.5 GB of packed codes and scales, the activations)
-are generated on the GPU from their seeds and are resident in HBM before the
-timed region.  The same step at M = 32 (rq_gemm_smallm, matrix cores) gives
-the TFLOP/s figure.
+One step = one pass of the decode hot path: every one of the 367 matrices (366
+layer matrices and the 65536x4096 head) is multiplied by its own activation
+row (M = 1), in dependency order, on one stream (gemm_rwkv_decode_amd.step,
+kind "layer": receptance/key/value of a layer in one rq_gemv_batched launch,
+the rest through rq_gemv).  Inputs (6.67 GB of packed codes and scales, the
+activations) are generated on the GPU from their seeds and are resident in HBM
+before the timed region.  The same step at M = 16, 32 and 64 (rq_gemm_smallm,
+matrix cores) gives the TFLOP/s figures; M = 32 is the headline one.
 
 Prints one JSON line (rank 0):
   value       algorithmic bytes per step / step time, GB/s (M = 1)
@@ -89,6 +91,7 @@ def main():
 
     import torch
     import gemm_rwkv_decode_amd as rq
+    from gemm_rwkv_decode_amd import step as ST
     from gemm_rwkv_decode_amd import synth as S
 
     dev = torch.device("cuda:0")
@@ -101,20 +104,21 @@ def main():
                                    torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         del a, b
-    cfg = S.CONFIGS[4]
+    cfg = S.CONFIGS["rwkv7-13.3b"]
     fmt = S.INT4_G64
     mats = cfg.matrices()
     if args.layers is not None:
         mats = [m for m in mats if m[0] < args.layers]
-    nlayers = len({m[0] for m in mats})
+    nlayers = len({m[0] for m in mats if m[1] != ST.HEAD})
+    mfma_ms = [16, 32, 64]
 
     # ---- inputs, resident in HBM --------------------------------------------
     t0 = time.time()
-    W = [S.gen_matrix(cfg.cid, l, mi, N, K, fmt, device=dev) for (l, mi, N, K) in mats]
-    X1 = [S.gen_x(cfg, l, mi, 1, K, device=dev) for (l, mi, N, K) in mats]
-    X32 = [S.gen_x(cfg, l, mi, 32, K, device=dev) for (l, mi, N, K) in mats]
-    Y1 = [torch.empty((1, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
-    Y32 = [torch.empty((32, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
+    W = [S.gen_matrix(cfg.key, l, mi, N, K, fmt, device=dev) for (l, mi, N, K) in mats]
+    X = {M: [S.gen_x(cfg, l, mi, M, K, device=dev) for (l, mi, N, K) in mats]
+         for M in [1] + mfma_ms}
+    Y = {M: [torch.empty((M, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
+         for M in [1] + mfma_ms}
     torch.cuda.synchronize()
     log(f"generated {len(mats)} matrices in {time.time() - t0:.1f}s")
 
@@ -124,49 +128,13 @@ def main():
         return weight_bytes + sum(2 * M * K + 4 * M * N for (_, _, N, K) in mats)
 
     flops_per_m = sum(2 * N * K for (_, _, N, K) in mats)
-    B, G, LAY = 4, 64, 0
-
-    def prob(i, M):  # noqa: E306
-        p = W[i]
-        (_, _, N, K) = mats[i]
-        x, y = (X1[i], Y1[i]) if M == 1 else (X32[i], Y32[i])
-        return (p.qweight, p.scales, None, x, y, N, K)
-
-    def schedule(kind, M, stream=None):
-        """Prepared calls of one step, in execution order, on `stream`."""
-        calls = []
-        prep = lambda *a: rq.prepare(*a, stream=stream)  # noqa: E731
-        entry = "rq_gemv" if M < 16 else "rq_gemm_smallm"
-        if kind == "layer" and M < 16:
-            # per layer: receptance/key/value in one launch, then output,
-            # FFN key, FFN value -- the dependency order of a decode step
-            by_layer = {}
-            for i, (l, mi, N, K) in enumerate(mats):
-                by_layer.setdefault(l, {})[mi] = i
-            for l in sorted(by_layer):
-                ix = by_layer[l]
-                calls.append(prep("rq_gemv_batched", [prob(ix[m], M) for m in (0, 1, 2)],
-                                  M, B, G, LAY))
-                for m in (3, 4, 5):
-                    q = prob(ix[m], M)
-                    calls.append(prep(entry, *q[:5], M, q[5], q[6], B, G, LAY))
-        elif kind == "batched":
-            # every product of the step through the grouped entry point
-            ps = [prob(i, M) for i in range(len(mats))]
-            for k in range(0, len(ps), rq.RQ_MAX_BATCH):
-                calls.append(prep("rq_gemv_batched", ps[k:k + rq.RQ_MAX_BATCH], M, B, G, LAY))
-        else:  # one launch per matrix
-            for i in range(len(mats)):
-                q = prob(i, M)
-                calls.append(prep(entry, *q[:5], M, q[5], q[6], B, G, LAY))
-        return calls
 
     def timed(kind, M, steps, warmup, graph):
         """Seconds per step.  Graph mode prepares the calls on a side stream,
         captures one step there and replays it."""
         if graph:
             s = torch.cuda.Stream()
-            calls = schedule(kind, M, stream=s)
+            calls = ST.step_calls(mats, W, X[M], Y[M], kind, stream=s)
             with torch.cuda.stream(s):
                 for _ in range(warmup):
                     for c in calls:
@@ -179,7 +147,7 @@ def main():
             torch.cuda.synchronize()
             run = g.replay
         else:
-            calls = schedule(kind, M)
+            calls = ST.step_calls(mats, W, X[M], Y[M], kind)
 
             def run():
                 for c in calls:
@@ -195,7 +163,7 @@ def main():
 
     # ---- M = 1: the headline (dependency-ordered decode step) ---------------
     scheds = {}
-    for kind in ("layer", "matrix", "batched"):
+    for kind in ST.KINDS:
         log(f"timing M=1 schedule {kind}")
         sec, ncalls = timed(kind, 1, args.steps, args.warmup, args.graph)
         scheds[kind] = {"launch_calls": ncalls, "ms_per_step": round(sec * 1e3, 4),
@@ -207,28 +175,41 @@ def main():
     # shape over all layers (distinct, cold matrices), same stream -----------
     log("per-shape events")
     per_kernel = {}
-    groups = {"rkv batched 3x(4096x4096)": [], "4096x4096": [], "16384x4096": [],
-              "4096x16384": []}
+    groups = {}
+    nbytes = {}
+
+    def add(key, call, b):
+        groups.setdefault(key, []).append(call)
+        nbytes[key] = b
+
     by_layer = {}
     for i, (l, mi, N, K) in enumerate(mats):
         by_layer.setdefault(l, {})[mi] = i
+
+    def mbytes(i):
+        _, _, N, K = mats[i]
+        return fmt.weight_bytes(N, K) + 2 * K + 4 * N
+
     for l in sorted(by_layer):
         ix = by_layer[l]
-        groups["rkv batched 3x(4096x4096)"].append(
-            rq.prepare("rq_gemv_batched", [prob(ix[m], 1) for m in (0, 1, 2)], 1, B, G, LAY))
-        for m, key in ((3, "4096x4096"), (4, "16384x4096"), (5, "4096x16384")):
-            q = prob(ix[m], 1)
-            groups[key].append(rq.prepare("rq_gemv", *q[:5], 1, q[5], q[6], B, G, LAY))
-    nbytes = {"rkv batched 3x(4096x4096)": 3 * (fmt.weight_bytes(4096, 4096) + 2 * 4096 + 4 * 4096),
-              "4096x4096": fmt.weight_bytes(4096, 4096) + 2 * 4096 + 4 * 4096,
-              "16384x4096": fmt.weight_bytes(16384, 4096) + 2 * 4096 + 4 * 16384,
-              "4096x16384": fmt.weight_bytes(4096, 16384) + 2 * 16384 + 4 * 4096}
+        if ST.RECEPTANCE in ix:
+            rkv = [ix[m] for m in (ST.RECEPTANCE, ST.KEY, ST.VALUE)]
+            add("rkv batched 3x(4096x4096)",
+                ST.step_calls([mats[i] for i in rkv], [W[i] for i in rkv],
+                              [X[1][i] for i in rkv], [Y[1][i] for i in rkv], "layer")[0],
+                sum(mbytes(i) for i in rkv))
+        for m in (ST.OUTPUT, ST.FFN_KEY, ST.FFN_VALUE, ST.HEAD):
+            if m in ix:
+                i = ix[m]
+                _, _, N, K = mats[i]
+                add(f"{N}x{K}", ST.step_calls([mats[i]], [W[i]], [X[1][i]], [Y[1][i]],
+                                               "matrix")[0], mbytes(i))
     stream = torch.cuda.current_stream()
     for key, calls in groups.items():
         for c in calls[:4]:
             c()
         ts = []
-        for _ in range(3):
+        for _ in range(3 if len(calls) > 1 else 20):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -243,10 +224,18 @@ def main():
     dom_name, dom_v = max(per_kernel.items(),
                           key=lambda kv: kv[1]["us_per_launch"] * kv[1]["launches_per_step"])
 
-    # ---- M = 32 (matrix cores) ---------------------------------------------
-    log("timing M=32")
-    sec32, _ = timed("matrix", 32, args.m32_steps, 2, args.graph)
-    tflops32 = 32 * flops_per_m / sec32 / 1e12
+    # ---- M = 16, 32, 64 (matrix cores) ---------------------------------------
+    mfma = {}
+    for M in mfma_ms:
+        log(f"timing M={M}")
+        sec, ncalls = timed("layer", M, args.m32_steps, 2, args.graph)
+        tf = M * flops_per_m / sec / 1e12
+        mfma[str(M)] = {"entry": "rq_gemm_smallm", "launch_calls": ncalls,
+                        "ms_per_step": round(sec * 1e3, 4), "tflops": round(tf, 2),
+                        "pct_of_fp16_mfma_peak": round(100 * tf / FP16_MFMA_PEAK_TFLOPS, 2),
+                        "GBps": round(step_bytes(M) / sec / 1e9, 2),
+                        "pct_of_hbm_peak": round(100 * step_bytes(M) / sec / 1e9 / HBM_PEAK_GBS,
+                                                 2)}
 
     # ---- CPU oracle on a bounded sample of the same step --------------------
     cpu = None
@@ -255,7 +244,7 @@ def main():
         sample = [i for i, m in enumerate(mats) if m[0] < args.cpu_layers]
         log(f"cpu oracle on {len(sample)} matrices")
         host = [(W[i].qweight.cpu().numpy(), W[i].scales.cpu().numpy(),
-                 X1[i].cpu().numpy(), mats[i]) for i in sample]
+                 X[1][i].cpu().numpy(), mats[i]) for i in sample]
         t = time.perf_counter()
         for q, s, x, (_, _, N, K) in host:
             oracle.gemv_ref(q, s, None, x, N, K, 4, 64, 0, threads=1)
@@ -283,16 +272,16 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "launch_mode": "graph" if args.graph else "stream",
         "schedule": "per layer: one grouped launch for receptance/key/value, then output, "
-                    "FFN key, FFN value (244 launches per step)",
+                    f"FFN key, FFN value; the head last ({scheds['layer']['launch_calls']} "
+                    "launches per step)",
         "schedules_m1": scheds,
-        "config": {"workload": "RWKV-7 13.3B-shaped decode weight stream, int4 sym g64",
+        "config": {"workload": "RWKV-7 13.3B-shaped decode weight stream, int4 sym g64: "
+                               "61 layers x (4 x 4096x4096, 16384x4096, 4096x16384) "
+                               "+ head 65536x4096",
                    "layers": nlayers, "matrices": len(mats), "M": 1,
-                   "shapes": "per layer 4x(4096x4096), 16384x4096, 4096x16384",
                    "bytes_per_step": step_bytes(1)},
-        "m32": {"entry": "rq_gemm_smallm", "ms_per_step": round(sec32 * 1e3, 4),
-                "tflops": round(tflops32, 2),
-                "pct_of_fp16_mfma_peak": round(100 * tflops32 / FP16_MFMA_PEAK_TFLOPS, 2),
-                "GBps": round(step_bytes(32) / sec32 / 1e9, 2)},
+        "m32": mfma["32"],
+        "mfma_m": mfma,
         "per_shape_m1": per_kernel,
         "roofline": {"bound": "hbm", "kernel": f"int4 g64 GEMV {dom_name}, M=1",
                      "achieved": dom_v["GBps"], "peak": HBM_PEAK_GBS,

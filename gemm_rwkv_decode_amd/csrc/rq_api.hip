@@ -27,7 +27,7 @@ static int env_or_zero(const char* name) {
 
 static void read_tuning() {
   g_tuning = Tuning{env_or_zero("RQ_GEMV_LPR"), env_or_zero("RQ_GEMV_CPL"),
-                    env_or_zero("RQ_GEMV_NPASS"), env_or_zero("RQ_GEMM_NT"),
+                    env_or_zero("RQ_GEMV_NPASS"), env_or_zero("RQ_GEMM_PLAN"),
                     env_or_zero("RQ_GEMM_SPLITS")};
 }
 

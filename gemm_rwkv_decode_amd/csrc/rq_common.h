@@ -78,6 +78,27 @@ __device__ __forceinline__ void unpack4(u32 d, h2 q[4]) {
   q[3] = __builtin_elementwise_fma(as_h2(t3), sixteenth, bias1);
 }
 
+// The same dword, pairs in k order: (q0,q1) (q2,q3) (q4,q5) (q6,q7).  A byte
+// perm copies byte j of d into both half-words next to the exponent byte of
+// 1024.0; the AND keeps the low nibble in the low half and the high nibble in
+// the high half (there worth 16u), the XOR flips the sign bits; one packed
+// FMA scales the high half by 1/16 and removes both offsets.
+template <bool SIGNED>
+__device__ __forceinline__ void unpack4n(u32 d, h2 q[4]) {
+  const u32 flip = SIGNED ? 0x00800008u : 0u;
+  const _Float16 b0 = SIGNED ? (_Float16)-1032.0f : (_Float16)-1024.0f;
+  const _Float16 b1 = SIGNED ? (_Float16)-72.0f : (_Float16)-64.0f;
+  const h2 mul = {(_Float16)1.0f, (_Float16)0.0625f};
+  const h2 add = {b0, b1};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    // bytes (high to low): 0x64, d.byte j, 0x64, d.byte j
+    const u32 w = __builtin_amdgcn_perm(0x64646464u, d, 0x04000400u | (j << 16) | j);
+    const u32 t = (w & 0xFFF0FF0Fu) ^ flip;  // 1024 + u_lo | 1024 + 16 u_hi
+    q[j] = __builtin_elementwise_fma(as_h2(t), mul, add);
+  }
+}
+
 // One dword of int8 codes, k = 0..3 in bytes 0..3.  Returns (q0,q1) (q2,q3).
 // A byte u = q + 128 placed in the low 8 mantissa bits of 0x6400 is 1024 + u.
 __device__ __forceinline__ void unpack8(u32 d, h2 q[2]) {

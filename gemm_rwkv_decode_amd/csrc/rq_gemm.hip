@@ -18,39 +18,38 @@
 // lane takes the G/4 consecutive codes of its row that fall in its quarter of
 // the group (one 4-, 8- or 16-byte load per group) and the matching x.
 //
-// Work split.  A workgroup of 4 waves owns 64*NT rows and one K-range (the
-// K dimension is split across workgroups when the rows alone would not fill
-// the chip).  Wave w owns N-tiles w*NT .. w*NT+NT-1.  The x tile of the
-// K-range passes through LDS in chunks of KC k (double buffered, one barrier
-// per chunk), shared by the four waves; codes and scales of chunk c+1 are
-// loaded into registers while chunk c is multiplied.
+// Work split (MI355X: 256 CUs, 64 B/clk per CU from L2, ~160 B/clk of LDS
+// reads).  A workgroup owns WR*NT*16 rows and the whole K range (or one
+// K-range when K is split across workgroups).  Its W = WR*WK waves form WR
+// row groups of NT 16-row tiles times WK K-slices.  K advances in rounds of
+// WK*KC k: in a round, K-slice w multiplies the w-th KC-wide chunk.  The
+// round's x tile [M][WK*KC] is staged once per workgroup into LDS (double
+// buffered, one barrier per round) with coalesced 16-byte loads; every wave
+// reads its MFMA fragments from there.  Codes and scales are prefetched D
+// rounds ahead into registers.  At the end the WK K-slices of a row group
+// are added in a fixed order through LDS, so no other workgroup and no
+// second kernel is involved.  Every workgroup of a launch on a small-N
+// matrix reads all of x, so staging x (M*K*2 bytes per workgroup at up to
+// 64 B/clk) bounds those launches; splitting K over workgroups shortens it at
+// the price of a partial-sum workspace and a reduce kernel, used only where
+// that wins.
 //
 // Split-K reduction.  When the K dimension is split, every K-range writes its
 // partial tile to a workspace with plain stores and a second, small kernel
 // adds the partials in K-range order into y.  Results are deterministic; no
 // workgroup waits for another and no device-wide fence is needed (a fence per
-// workgroup would write the whole L2 back each time).
+// workgroup costs tens of microseconds: it writes the L2 back).
 #include "rq_common.h"
 #include "rq_internal.h"
+
+#include <type_traits>
 
 
 namespace rq {
 
-constexpr int GEMM_WAVES = 4;
-
-// k per LDS chunk of x.  Larger chunks put more code bytes in flight per
-// wave (the next chunk is loaded while this one is multiplied); the double
-// buffered x tile is 2 * 16*MT * (KC+8) halves.
-// At most 8 groups per chunk: every group of a chunk is unrolled.
-constexpr int gemm_kc(int fmt, int mt, int g) {
-  const int base = fmt == FMT_S8 ? (mt >= 3 ? 128 : 256) : (mt >= 3 ? 256 : 512);
-  return base < 8 * g ? base : 8 * g;
-}
-
 template <int FMT>
 struct MfmaT {
   static constexpr int KS = (FMT == FMT_S8) ? 16 : 32;  // k per MFMA
-  static constexpr int EPL = (FMT == FMT_S8) ? 4 : 8;   // elements per lane
 };
 
 template <int FMT>
@@ -66,150 +65,283 @@ __device__ __forceinline__ f4 mfma_step(const u32* a, const u32* b, f4 c) {
   }
 }
 
-// Per-lane register image of one chunk of codes and scale material for NT
-// N-tiles: DPC dwords of codes per tile, one scale (sym) or record pair
-// (asym) per group.
-template <int FMT, int NT, int KC, int G>
-struct ChunkRegs {
-  static constexpr int GPC = KC / G;                                 // groups per chunk
-  static constexpr int DPG = (FMT == FMT_S8) ? G / 16 : G / 32;      // dwords per lane per group
-  static constexpr int DPC = GPC * DPG;
-  static constexpr int SCW = (GPC + 1) / 2;                         // dwords of scales
-  u32 code[NT][DPC];
-  u32 sc[NT][SCW];           // sym: binary16 scales of the chunk's groups, 2 per dword
-  u32x2 srec[NT], zrec[NT];  // asym: records of the chunk's superblock
+// Rounds are sized so one x round of the M-tile is about 32 KB (rd = 1) or
+// 16 KB (rd = 2): k per round 1024 / MT rounded down to a power of two, / rd.
+constexpr int mm_round_target(int mt) { return mt == 1 ? 1024 : (mt == 2 ? 512 : 256); }
+
+// k per wave chunk: whole groups, at least one MFMA K-step, at most 8 groups.
+constexpr int mm_kc(int fmt, int mt, int wk, int g, int rd) {
+  const int want = mm_round_target(mt) / rd / wk;
+  const int lo = g > 32 ? g : 32;
+  const int kc = want > lo ? want : lo;
+  return kc < 8 * g ? kc : 8 * g;
+}
+
+constexpr int LDS_LIMIT = 160 * 1024;
+constexpr int MM_XP = 3;           // waves copying x
+constexpr int MM_CP = 1;           // waves copying codes and scale material
+constexpr int MM_MAX_XDEPTH = 6;   // x rounds copied ahead (x comes from L2)
+constexpr int MM_MAX_CDEPTH = 13;  // code rounds copied ahead (codes come from HBM)
+constexpr int MM_CODE_AHEAD = 32 * 1024;  // code bytes to keep in flight, at least
+
+// Bytes of one x round slot ([MP][ROUND+8] halves) and of one code round
+// slot (the workgroup's code rows [ROWS][ROUND*bits/8], then its scale
+// material).
+constexpr int mm_round(int fmt, int mt, int wk, int g, int rd) {
+  return wk * mm_kc(fmt, mt, wk, g, rd);
+}
+constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd) {
+  return (16 * mt) * (mm_round(fmt, mt, wk, g, rd) + 8) * 2;
+}
+constexpr int mm_cslot(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int round = mm_round(fmt, mt, wk, g, rd);
+  const int rows = 16 * nt * wr;
+  const int codes = rows * (fmt == FMT_S8 ? round : round / 2);
+  const int scales = fmt == FMT_A4 ? 2 * rows * (round / SUPERBLOCK) * 8 : rows * (round / g) * 2;
+  return codes + scales;
+}
+// copy instructions per round: x row segments; code pieces and scale dwords
+constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd) {
+  const int round = mm_round(fmt, mt, wk, g, rd);
+  const int seg = round * 2 < 1024 ? round * 2 : 1024;
+  return (16 * mt) * (round * 2 / seg);
+}
+constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int round = mm_round(fmt, mt, wk, g, rd);
+  const int rows = 16 * nt * wr;
+  const int cc = (rows * (fmt == FMT_S8 ? round : round / 2) / 16 + 63) / 64;
+  const int sd = fmt == FMT_A4 ? rows * (round / SUPERBLOCK) * 2 : rows * (round / g) / 2;
+  return cc + (fmt == FMT_A4 ? 2 : 1) * ((sd + 63) / 64);
+}
+// Rounds copied ahead.  Code slots to keep MM_CODE_AHEAD bytes in flight
+// come first (at least 2 rounds), then as many x rounds as fit (at most
+// MM_MAX_XDEPTH), then the rest of the LDS goes to more code rounds; each
+// copying wave's pending copies must fit its counter (63).
+constexpr int mm_xdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int xs = mm_xslot(fmt, mt, g, wk, rd), cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
+  const int xpp = (mm_xcopies(fmt, mt, g, wk, rd) + MM_XP - 1) / MM_XP;
+  int dcmin = (MM_CODE_AHEAD + cs - 1) / cs;
+  dcmin = dcmin < 2 ? 2 : (dcmin > MM_MAX_CDEPTH ? MM_MAX_CDEPTH : dcmin);
+  int d = MM_MAX_XDEPTH;
+  while (d > 0 && ((d + 1) * xs + (dcmin + 1) * cs > LDS_LIMIT || (d - 1) * xpp > 63)) d--;
+  return d;
+}
+constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int left = LDS_LIMIT - (mm_xdepth(fmt, mt, g, wr, wk, nt, rd) + 1) *
+                                   mm_xslot(fmt, mt, g, wk, rd);
+  const int cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
+  const int cpp = (mm_ccopies(fmt, mt, g, wr, wk, nt, rd) + MM_CP - 1) / MM_CP;
+  int d = MM_MAX_CDEPTH;
+  while (d > 0 && ((d + 1) * cs > left || (d - 1) * cpp > 63)) d--;
+  return d;
+}
+
+// Compile-time shape of one kernel instance.
+template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_>
+struct Mm {
+  static constexpr int FMT = FMT_, MT = MT_, NT = NT_, WR = WR_, WK = WK_, G = G_, RD = RD_;
+  static constexpr int W = WR * WK;                 // multiplying waves
+  static constexpr int THREADS = 64 * (W + MM_XP + MM_CP);
+  static constexpr int KC = mm_kc(FMT, MT, WK, G, RD);  // k per wave chunk
+  static constexpr int ROUND = WK * KC;             // k per round
+  static constexpr int DX = mm_xdepth(FMT, MT, G, WR, WK, NT, RD);  // x rounds ahead
+  static constexpr int DC = mm_cdepth(FMT, MT, G, WR, WK, NT, RD);  // code rounds ahead
+  static constexpr int MP = 16 * MT;                // padded activation rows
+  static constexpr int TR = 16 * NT;                // rows per wave
+  static constexpr int ROWS = TR * WR;              // rows per workgroup
+  static constexpr int XSTR = ROUND + 8;            // halves per LDS row of x
+  static constexpr int GPC = KC / G;                // groups per chunk
+  static constexpr int DPG = (FMT == FMT_S8) ? G / 16 : G / 32;  // dwords per lane per group
+  static constexpr int BPL = DPG * 4;               // code bytes per lane per group
+  static constexpr int GB = (FMT == FMT_S8) ? G : G / 2;  // code bytes per group of a row
+  static constexpr int RS = (FMT == FMT_S8) ? ROUND : ROUND / 2;  // code bytes per row and round
+  static constexpr int PR = RS / 16;                // 16-byte code pieces per row and round
+  static constexpr int NSB = ROUND / SUPERBLOCK;    // superblocks per round (asym)
+  // scale dwords per row and round: sym, the round's binary16 scales; asym,
+  // per kind (scale records, zero records) two dwords per superblock
+  static constexpr int SRD = (FMT == FMT_A4) ? 2 * NSB : ROUND / G / 2;
+  // LDS: x ring (DX+1 slots), then code ring (DC+1 slots)
+  static constexpr int XSLOT = mm_xslot(FMT, MT, G, WK, RD);
+  static constexpr int CSLOT = mm_cslot(FMT, MT, G, WR, WK, NT, RD);
+  static constexpr int CRING = (DX + 1) * XSLOT;    // byte offset of the code ring
+  static constexpr int C_OFF = 0;                   // within a code slot
+  static constexpr int S_OFF = ROWS * RS;
+  static constexpr int Z_OFF = S_OFF + ROWS * SRD * 4;  // asym zero records
+  // copies of one round
+  static constexpr int SEG = ROUND * 2 < 1024 ? ROUND * 2 : 1024;  // x bytes per copy
+  static constexpr int SEG_LANES = SEG / 16;
+  static constexpr int SEGS_PER_ROW = ROUND * 2 / SEG;
+  static constexpr int XN = MP * SEGS_PER_ROW;
+  static constexpr int CPIECES = ROWS * PR;
+  static constexpr int CN = (CPIECES + 63) / 64;
+  static constexpr int SDK = ROWS * SRD;            // scale dwords per kind
+  static constexpr int SNK = (SDK + 63) / 64;
+  static constexpr int SN = (FMT == FMT_A4 ? 2 : 1) * SNK;
+  static constexpr int COPIES = XN + CN + SN;
+  static constexpr int XPP = (XN + MM_XP - 1) / MM_XP;         // per x-copying wave
+  static constexpr int CPP = (CN + SN + MM_CP - 1) / MM_CP;    // per code-copying wave
+  static constexpr int RED = (WK > 1) ? W * 64 * NT * MT * 4 : 0;  // floats
+  static constexpr int LDS_BYTES = CRING + (DC + 1) * CSLOT;
+  // structural conditions (the host's plan_fits checks the same)
+  static constexpr bool VALID =
+      GPC >= 1 && GPC <= 8 && KC % G == 0 &&
+      (FMT != FMT_A4 || (SUPERBLOCK % KC == 0 && ROUND % SUPERBLOCK == 0)) &&
+      (FMT == FMT_A4 || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
+      SEG_LANES <= 64 && ROUND * 2 % SEG == 0;
+  static constexpr bool FITS = VALID && DX >= 1 && DC >= 1 && LDS_BYTES <= LDS_LIMIT &&
+                               RED * 4 <= LDS_LIMIT;
+  static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
+                          CN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
+                "copy counts");
+  static_assert(!FITS || ((DX - 1) * XPP <= 63 && (DC - 1) * CPP <= 63),
+                "wait counts fit the counter");
 };
 
-template <int FMT, int NT, int KC, int G>
-__device__ __forceinline__ void load_chunk(ChunkRegs<FMT, NT, KC, G>& r,
-                                           const uint8_t* __restrict__ qw,
-                                           const void* __restrict__ scales,
-                                           const void* __restrict__ zeros, const int* rows,
-                                           int K, int kb, int h) {
-  using R = ChunkRegs<FMT, NT, KC, G>;
-  constexpr int BPL = R::DPG * 4;  // bytes per lane per group
-  const size_t row_bytes = (FMT == FMT_S8) ? (size_t)K : (size_t)K / 2;
-  const int byte0 = (FMT == FMT_S8) ? kb : kb / 2;  // chunk start in the row
-  const int gbytes = (FMT == FMT_S8) ? G : G / 2;   // bytes per group in a row
-#pragma unroll
-  for (int nt = 0; nt < NT; nt++) {
-    const uint8_t* row = qw + (size_t)rows[nt] * row_bytes + byte0 + h * BPL;
-#pragma unroll
-    for (int g = 0; g < R::GPC; g++) {
-      const uint8_t* p = row + g * gbytes;
-      if constexpr (BPL == 16) {
-        const u32x4 v = load_stream16(p);
-        r.code[nt][g * 4 + 0] = v.x; r.code[nt][g * 4 + 1] = v.y;
-        r.code[nt][g * 4 + 2] = v.z; r.code[nt][g * 4 + 3] = v.w;
-      } else if constexpr (BPL == 8) {
-        const u32x2 v = load_stream8(p);
-        r.code[nt][g * 2 + 0] = v.x; r.code[nt][g * 2 + 1] = v.y;
-      } else {
-        r.code[nt][g] = load_stream4(p);
-      }
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean "do not wait").
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most k*STEP vector loads of this wave are pending, k in
+// [0, KMAX] (a switch: the counter takes an immediate).
+template <int STEP, int KMAX>
+__device__ __forceinline__ void wait_vm_rounds(int k) {
+  if constexpr (KMAX > 0) {
+    if (k >= KMAX) {
+      wait_vm<KMAX * STEP>();
+      return;
     }
-    if constexpr (FMT == FMT_A4) {
-      const size_t rec = (size_t)rows[nt] * (K / SUPERBLOCK) + kb / SUPERBLOCK;
-      r.srec[nt] = reinterpret_cast<const u32x2*>(scales)[rec];
-      r.zrec[nt] = reinterpret_cast<const u32x2*>(zeros)[rec];
-    } else {
-      // the chunk's GPC scales are contiguous and aligned to their size
-      const uint16_t* sp =
-          static_cast<const uint16_t*>(scales) + (size_t)rows[nt] * (K / G) + kb / G;
-      if constexpr (R::GPC == 1) {
-        r.sc[nt][0] = *sp;
-      } else if constexpr (R::GPC == 2) {
-        r.sc[nt][0] = *reinterpret_cast<const u32*>(sp);
-      } else if constexpr (R::GPC == 4) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
-        r.sc[nt][0] = v.x; r.sc[nt][1] = v.y;
-      } else {
-#pragma unroll
-        for (int i = 0; i < R::SCW / 4; i++) {
-          const u32x4 v = reinterpret_cast<const u32x4*>(sp)[i];
-          r.sc[nt][4 * i + 0] = v.x; r.sc[nt][4 * i + 1] = v.y;
-          r.sc[nt][4 * i + 2] = v.z; r.sc[nt][4 * i + 3] = v.w;
-        }
-      }
-    }
+    wait_vm_rounds<STEP, KMAX - 1>(k);
+  } else {
+    wait_vm<0>();
   }
 }
 
-// Stage x[0..M)[kb, kb+KC) into LDS as binary16 rows of stride KC+8 halves;
-// 4-bit formats store every aligned block of 8 as (x0,x4,x1,x5,x2,x6,x3,x7),
-// the order unpack4 delivers codes in.  Rows >= M are zero.  For the
-// asymmetric format also store the 32-wide group sums of x, [KC/32][MP].
-template <int FMT, int MP, int KC>
-struct Stage {
-  static constexpr int PER = MP * KC / 8 / (64 * GEMM_WAVES);  // 16-byte pieces per thread
-  u32x4 v[PER];
-};
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                   0);
+}
+__device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0,
+                                   0);
+}
 
-template <int FMT, int MP, int KC>
-__device__ __forceinline__ void stage_load(Stage<FMT, MP, KC>& st,
-                                           const _Float16* __restrict__ x, int M, int K,
-                                           int kb) {
-#pragma unroll
-  for (int i = 0; i < Stage<FMT, MP, KC>::PER; i++) {
-    const int piece = i * 64 * GEMM_WAVES + threadIdx.x;
-    const int m = piece / (KC / 8);
-    const int k = kb + (piece % (KC / 8)) * 8;
-    if (m < M) st.v[i] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k);
-    else st.v[i] = u32x4{0, 0, 0, 0};
+// Copy c of a round, c in [0, COPIES): x row segments first (rows >= M
+// repeat row M-1; they only feed outputs that are never stored), then code
+// pieces (row n's 16-byte piece p stored at position n*PR + (p ^ (n & 7)), so
+// that the 16 rows a fragment read touches spread over the banks), then scale
+// dwords (row n's dword d at n*SRD + d; asym: scale records, then zero
+// records).  copy_off gives this lane's byte offset from the copy's base,
+// which does not change from round to round; copy_src/copy_dst the uniform
+// parts.
+template <class S>
+__device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, int lane) {
+  if (c < S::XN) {
+    const int m = c / S::SEGS_PER_ROW, seg = c % S::SEGS_PER_ROW;
+    const int mr = m < M ? m : M - 1;
+    return ((u32)mr * (u32)K + (u32)(seg * (S::SEG / 2) + lane * 8)) * 2u;
+  } else if (c < S::XN + S::CN) {
+    const int pos = (c - S::XN) * 64 + lane;  // piece position in the slot
+    const int n = pos / S::PR, sp = pos % S::PR;
+    const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
+    const u32 row_bytes = (S::FMT == FMT_S8) ? (u32)K : (u32)K / 2;
+    return (u32)row * row_bytes + (u32)(sp ^ (n & 7)) * 16u;
+  } else {
+    const int j = (c - S::XN - S::CN) % S::SNK;
+    const int q = j * 64 + lane;
+    const int n = q / S::SRD, dw = q % S::SRD;
+    const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
+    if constexpr (S::FMT == FMT_A4)
+      return ((u32)row * (u32)(K / SUPERBLOCK) * 2u + (u32)dw) * 4u;
+    else  // K / G is even (host check): a row's scales start on a dword
+      return ((u32)row * (u32)(K / S::G) / 2u + (u32)dw) * 4u;
   }
 }
 
-template <int FMT, int MP, int KC>
-__device__ __forceinline__ void stage_store(const Stage<FMT, MP, KC>& st, _Float16* xl,
-                                            float* xsum) {
-  constexpr int XSTR = KC + 8;
-#pragma unroll
-  for (int i = 0; i < Stage<FMT, MP, KC>::PER; i++) {
-    const int piece = i * 64 * GEMM_WAVES + threadIdx.x;
-    const int m = piece / (KC / 8);
-    const int kk = (piece % (KC / 8)) * 8;
-    u32x4 v = st.v[i];
-    if (FMT != FMT_S8) {
-      h2 p[4];
-      pair_x4(v.x, v.y, v.z, v.w, p);
-      v = u32x4{as_u32(p[0]), as_u32(p[1]), as_u32(p[2]), as_u32(p[3])};
-    }
-    *reinterpret_cast<u32x4*>(xl + m * XSTR + kk) = v;
-    if (FMT == FMT_A4) {
-      // four consecutive threads hold one 32-wide group of one row
-      const u32x4 w = st.v[i];
-      float s = half_lo(w.x) + half_hi(w.x) + half_lo(w.y) + half_hi(w.y) +
-                half_lo(w.z) + half_hi(w.z) + half_lo(w.w) + half_hi(w.w);
-      s += __shfl_xor(s, 1, 4);
-      s += __shfl_xor(s, 2, 4);
-      if ((threadIdx.x & 3) == 0) xsum[(kk / 32) * MP + m] = s;
-    }
+// Source base of copy c in round t (k0: the round's first k).
+template <class S>
+__device__ __forceinline__ const char* copy_src(int c, int k0, const _Float16* x,
+                                                const uint8_t* qw, const void* scales,
+                                                const void* zeros) {
+  if (c < S::XN) return reinterpret_cast<const char*>(x) + (size_t)k0 * 2;
+  if (c < S::XN + S::CN)
+    return reinterpret_cast<const char*>(qw) + (size_t)(S::FMT == FMT_S8 ? k0 : k0 / 2);
+  if constexpr (S::FMT == FMT_A4) {
+    const bool zr = (c - S::XN - S::CN) >= S::SNK;
+    return reinterpret_cast<const char*>(zr ? zeros : scales) + (size_t)(k0 / SUPERBLOCK) * 8;
+  } else {
+    return reinterpret_cast<const char*>(scales) + (size_t)(k0 / S::G) * 2;
   }
 }
 
-// Multiply one chunk (x in LDS buffer `xb`, codes in `r`) into acc.
-template <int FMT, int MT, int NT, int KC, int G>
-__device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
-                                           const _Float16* xb, const float* xsb, int kb,
-                                           int h, int col, f4 (&acc)[NT][MT]) {
-  constexpr int MP = 16 * MT;
-  constexpr int XSTR = KC + 8;
+// Destination offset of copy c within its slot, and its active lanes.
+template <class S>
+__device__ __forceinline__ int copy_dst(int c) {
+  if (c < S::XN) {
+    const int m = c / S::SEGS_PER_ROW, seg = c % S::SEGS_PER_ROW;
+    return (m * S::XSTR + seg * (S::SEG / 2)) * 2;
+  }
+  if (c < S::XN + S::CN) return S::C_OFF + (c - S::XN) * 1024;
+  const int i = c - S::XN - S::CN;
+  return ((S::FMT == FMT_A4 && i >= S::SNK) ? S::Z_OFF : S::S_OFF) + (i % S::SNK) * 256;
+}
+template <class S>
+constexpr int copy_lanes(int c) {
+  if (c < S::XN) return S::SEG_LANES;
+  if (c < S::XN + S::CN) {
+    const int left = S::CPIECES - (c - S::XN) * 64;
+    return left < 64 ? left : 64;
+  }
+  const int left = S::SDK - ((c - S::XN - S::CN) % S::SNK) * 64;
+  return left < 64 ? left : 64;
+}
+
+// Multiply one chunk into acc from the LDS x slot `xsl` and code slot `sl`:
+// x of the chunk at column kx of the x tile, code bytes at cb0 of the rows'
+// round segments,
+// the chunk's groups j0 .. j0+GPC-1 of the round's scales.  kb is the
+// chunk's first k.
+template <class S>
+__device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
+                                         const char* __restrict__ sl, int kx, int cb0, int j0,
+                                         int kb, int wr, int h, int col,
+                                         f4 (&acc)[S::NT][S::MT]) {
+  constexpr int FMT = S::FMT, G = S::G, MT = S::MT, NT = S::NT, DPG = S::DPG;
   constexpr int KS = MfmaT<FMT>::KS;
-  using R = ChunkRegs<FMT, NT, KC, G>;
-  constexpr int GPC = R::GPC;
-  constexpr int DPG = R::DPG;  // dwords (= MFMA steps) per lane per group
-  constexpr int QPL = G / 4;   // k per lane group per group
+  constexpr int QPL = G / 4;  // k per lane group per group
+  const _Float16* xb = reinterpret_cast<const _Float16*>(xsl);
 #pragma unroll
-  for (int g = 0; g < GPC; g++) {
+  for (int g = 0; g < S::GPC; g++) {
+    // this lane's codes: row n, bytes [cb0 + g*GB + h*BPL, +BPL) of the row
+    u32 code[NT][DPG];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int n = wr * S::TR + nt * 16 + col;
+      const int byte = cb0 + g * S::GB + h * S::BPL;
+      const char* src =
+          sl + S::C_OFF + (n * S::PR + ((byte / 16) ^ (n & 7))) * 16 + byte % 16;
+      if constexpr (S::BPL == 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        code[nt][0] = v.x; code[nt][1] = v.y; code[nt][2] = v.z; code[nt][3] = v.w;
+      } else if constexpr (S::BPL == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+        code[nt][0] = v.x; code[nt][1] = v.y;
+      } else {
+        code[nt][0] = *reinterpret_cast<const u32*>(src);
+      }
+    }
     f4 P[NT][MT];
-    // A fragments of every K-step of the group and every M-tile, read from
-    // LDS before the first MFMA so the reads overlap each other
+    // A fragments of every K-step of the group and every M-tile
     u32 a[DPG][MT][4];
 #pragma unroll
     for (int s = 0; s < DPG; s++)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
-        const _Float16* src = xb + (mt * 16 + col) * XSTR + g * G + h * QPL + s * (KS / 4);
+        const _Float16* src =
+            xb + (mt * 16 + col) * S::XSTR + kx + g * G + h * QPL + s * (KS / 4);
         if constexpr (FMT == FMT_S8) {
           const u32x2 v = *reinterpret_cast<const u32x2*>(src);
           a[s][mt][0] = v.x; a[s][mt][1] = v.y;
@@ -223,14 +355,14 @@ __device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         u32 b[4];
-        const u32 d = r.code[nt][g * DPG + s];
+        const u32 d = code[nt][s];
         if constexpr (FMT == FMT_S8) {
           h2 q[2];
           unpack8(d, q);
           b[0] = as_u32(q[0]); b[1] = as_u32(q[1]);
         } else {
           h2 q[4];
-          unpack4<FMT == FMT_S4>(d, q);
+          unpack4n<FMT == FMT_S4>(d, q);
           b[0] = as_u32(q[0]); b[1] = as_u32(q[1]);
           b[2] = as_u32(q[2]); b[3] = as_u32(q[3]);
         }
@@ -239,23 +371,31 @@ __device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
           P[nt][mt] = mfma_step<FMT>(a[s][mt], b, s == 0 ? f4{0, 0, 0, 0} : P[nt][mt]);
       }
     }
-    // group epilogue in binary32
+    // asymmetric: the group sums of x, in the layout of P, from one more MFMA
+    // against codes that are all 1 (a group is one K-step)
     f4 xg[MT];
     if constexpr (FMT == FMT_A4) {
+      const u32 one2 = 0x3C003C00u;  // binary16 (1, 1)
+      const u32 ones[4] = {one2, one2, one2, one2};
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-        xg[mt] = *reinterpret_cast<const f4*>(&xsb[((g * G) / 32) * MP + mt * 16 + 4 * h]);
+      for (int mt = 0; mt < MT; mt++) xg[mt] = mfma_step<FMT>(a[0][mt], ones, f4{0, 0, 0, 0});
     }
+    // group epilogue in binary32
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
+      const int n = wr * S::TR + nt * 16 + col;
       float sc, t = 0.0f;
       if constexpr (FMT == FMT_A4) {
-        const int j = ((kb % SUPERBLOCK) + g * G) / SB_GROUP;
-        sc = record_value(r.srec[nt], j);
-        t = record_value(r.zrec[nt], j);
+        const int kin = (kb % S::ROUND) + g * G;  // k within the round
+        const int sb = kin / SUPERBLOCK, j = (kin % SUPERBLOCK) / SB_GROUP;
+        const u32* sr = reinterpret_cast<const u32*>(sl + S::S_OFF) + n * S::SRD + 2 * sb;
+        const u32* zr = reinterpret_cast<const u32*>(sl + S::Z_OFF) + n * S::SRD + 2 * sb;
+        sc = record_value(u32x2{sr[0], sr[1]}, j);
+        t = record_value(u32x2{zr[0], zr[1]}, j);
       } else {
-        const u32 pair = r.sc[nt][g / 2];
-        sc = (g & 1) ? half_hi(pair) : half_lo(pair);
+        const int j = j0 + g;  // group within the round
+        const u32 pair = reinterpret_cast<const u32*>(sl + S::S_OFF)[n * S::SRD + j / 2];
+        sc = (j & 1) ? half_hi(pair) : half_lo(pair);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
@@ -273,81 +413,150 @@ __device__ __forceinline__ void gemm_chunk(const ChunkRegs<FMT, NT, KC, G>& r,
   }
 }
 
-template <int FMT, int MT, int NT, int KC, int G>
-__global__ void __launch_bounds__(64 * GEMM_WAVES)
-k_gemm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
-       const void* __restrict__ zeros, const _Float16* __restrict__ x,
-       float* __restrict__ out, int M, int N, int K, int kr) {
-  constexpr int MP = 16 * MT;
-  constexpr int XSTR = KC + 8;
-  constexpr int XSN = (FMT == FMT_A4) ? (KC / 32) * MP : 4;
-  using R = ChunkRegs<FMT, NT, KC, G>;
+// The copying waves.  x waves take the round's x copies p, p+XP, ...; the
+// code wave takes its code and scale copies.  Each group runs its own number
+// of rounds ahead of the multiplying waves (x: DX, codes: DC); a wave's
+// copies complete in issue order, so before the barrier of round r it waits
+// until only rounds r+1 .. r+ahead-1 may be in flight.  After the barrier
+// the slots of round r-1 are free and take round r+ahead.  (A copy index
+// past the end repeats the last copy: every wave issues the same number.)
+template <class S, bool XW>
+__device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
+                                            const uint8_t* qw, const void* scales,
+                                            const void* zeros, int M, int K, int N, int row0,
+                                            int k_begin, int nrounds, int lane) {
+  constexpr int NC = XW ? S::XPP : S::CPP;
+  constexpr int AHEAD = XW ? S::DX : S::DC;
+  static_assert(MM_CP == 1, "the code wave's copies are compile-time");
+  // copy index of position i (uniform)
+  auto cidx = [&](int i) {
+    return XW ? min(i * MM_XP + p, S::XN - 1) : S::XN + min(i, S::CN + S::SN - 1);
+  };
+  u32 off[NC];
+#pragma unroll
+  for (int i = 0; i < NC; i++) off[i] = copy_off<S>(cidx(i), M, K, N, row0, lane);
+  auto issue = [&](int t) {
+    char* slot = XW ? lds + (t % (S::DX + 1)) * S::XSLOT
+                    : lds + S::CRING + (t % (S::DC + 1)) * S::CSLOT;
+    const int k0 = k_begin + t * S::ROUND;
+#pragma unroll
+    for (int i = 0; i < NC; i++) {
+      const int c = cidx(i);
+      const char* src = copy_src<S>(c, k0, x, qw, scales, zeros) + off[i];
+      char* dst = slot + copy_dst<S>(c);
+      if constexpr (XW) {
+        if (S::SEG_LANES == 64 || lane < S::SEG_LANES) lds_copy16(src, dst);
+      } else {
+        constexpr int dummy = 0;
+        (void)dummy;
+        const int cc = S::XN + (i < S::CN + S::SN ? i : S::CN + S::SN - 1);
+        const int lanes = copy_lanes<S>(cc);
+        if (lane < lanes) {
+          if (cc >= S::XN + S::CN) lds_copy4(src, dst);
+          else lds_copy16(src, dst);
+        }
+      }
+    }
+  };
+#pragma unroll 1
+  for (int t = 0; t < AHEAD; t++)
+    if (t < nrounds) issue(t);
+#pragma unroll 1
+  for (int r = 0; r < nrounds; r++) {
+    wait_vm_rounds<NC, AHEAD - 1>(min(AHEAD - 1, nrounds - 1 - r));
+    __builtin_amdgcn_s_barrier();
+    if (r + AHEAD < nrounds) issue(r + AHEAD);
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) _Float16 xl[2][MP * XSTR];
-  __shared__ __attribute__((aligned(16))) float xsum[2][XSN];
+template <class S>
+__global__ void __launch_bounds__(S::THREADS)
+k_mm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
+     const void* __restrict__ zeros, const _Float16* __restrict__ x,
+     float* __restrict__ out, int M, int N, int K, int kr) {
+  constexpr int NT = S::NT, MT = S::MT;
+  static_assert(S::FITS, "LDS budget and prefetch depth");
+  constexpr int LDS_BYTES = S::LDS_BYTES > S::RED * 4 ? S::LDS_BYTES : S::RED * 4;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = lane >> 4;
-  const int col = lane & 15;
   const int split = blockIdx.y;
   const int k_begin = split * kr;
   // y itself, or this K-range's slice of the partial-sum workspace
   float* __restrict__ y = out + (size_t)split * M * N;
-  const int nchunks = kr / KC;
-  const int row_base = blockIdx.x * (64 * NT) + wave * (16 * NT);
+  const int nrounds = kr / S::ROUND;
+  const int row0 = blockIdx.x * S::ROWS;
 
-  int rows[NT];
+  if (wave >= S::W) {
+    if (wave < S::W + MM_XP)
+      copy_rounds<S, true>(wave - S::W, lds, x, qw, scales, zeros, M, K, N, row0, k_begin,
+                           nrounds, lane);
+    else
+      copy_rounds<S, false>(wave - S::W - MM_XP, lds, x, qw, scales, zeros, M, K, N, row0,
+                            k_begin, nrounds, lane);
+  } else {
+    // ---- multiplying wave: row group wr, K-slice wk
+    const int wk = wave % S::WK;
+    const int wr = wave / S::WK;
+    const int h = lane >> 4;
+    const int col = lane & 15;
+    f4 acc[NT][MT];
 #pragma unroll
-  for (int nt = 0; nt < NT; nt++) rows[nt] = min(row_base + nt * 16 + col, N - 1);
-
-  f4 acc[NT][MT];
+    for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-  for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) acc[nt][mt] = f4{0, 0, 0, 0};
-
-  // Chunks alternate between (LDS buffer 0, registers r0) and (1, r1); the
-  // next chunk's x and codes are fetched while the current one is multiplied.
-  Stage<FMT, MP, KC> st;
-  R r0, r1;
-  stage_load<FMT, MP, KC>(st, x, M, K, k_begin);
-  load_chunk<FMT, NT, KC, G>(r0, qw, scales, zeros, rows, K, k_begin, h);
-  stage_store<FMT, MP, KC>(st, xl[0], xsum[0]);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; c += 2) {
-    const int kb = k_begin + c * KC;
-    const bool more1 = c + 1 < nchunks;
-    if (more1) {
-      stage_load<FMT, MP, KC>(st, x, M, K, kb + KC);
-      load_chunk<FMT, NT, KC, G>(r1, qw, scales, zeros, rows, K, kb + KC, h);
+      for (int mt = 0; mt < MT; mt++) acc[nt][mt] = f4{0, 0, 0, 0};
+    const int kx = wk * S::KC;  // chunk within the round
+    const int cb0 = (S::FMT == FMT_S8) ? kx : kx / 2;
+    const int j0 = kx / S::G;
+    for (int r = 0; r < nrounds; r++) {
+      __builtin_amdgcn_s_barrier();  // round r is in LDS
+      mm_chunk<S>(lds + (r % (S::DX + 1)) * S::XSLOT,
+                  lds + S::CRING + (r % (S::DC + 1)) * S::CSLOT, kx, cb0, j0,
+                  k_begin + r * S::ROUND + kx, wr, h, col, acc);
     }
-    gemm_chunk<FMT, MT, NT, KC, G>(r0, xl[0], xsum[0], kb, h, col, acc);
-    if (more1) stage_store<FMT, MP, KC>(st, xl[1], xsum[1]);
-    __syncthreads();
-    if (!more1) break;
-    const bool more2 = c + 2 < nchunks;
-    if (more2) {
-      stage_load<FMT, MP, KC>(st, x, M, K, kb + 2 * KC);
-      load_chunk<FMT, NT, KC, G>(r0, qw, scales, zeros, rows, K, kb + 2 * KC, h);
+    if constexpr (S::WK > 1) {
+      __syncthreads();  // every wave is done with the slots
+      float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            red[((wave * NT + nt) * MT + mt) * 256 + i * 64 + lane] = acc[nt][mt][i];
+      __syncthreads();
+      if (wk != 0) return;
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            float v = acc[nt][mt][i];
+#pragma unroll
+            for (int q = 1; q < S::WK; q++)
+              v += red[(((wave + q) * NT + nt) * MT + mt) * 256 + i * 64 + lane];
+            acc[nt][mt][i] = v;
+          }
     }
-    gemm_chunk<FMT, MT, NT, KC, G>(r1, xl[1], xsum[1], kb + KC, h, col, acc);
-    if (more2) stage_store<FMT, MP, KC>(st, xl[0], xsum[0]);
-    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int n = row0 + wr * S::TR + nt * 16 + col;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = mt * 16 + 4 * h + i;
+          if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i];
+        }
+    }
+    return;
   }
-
-  // ---- write out -----------------------------------------------------------
-#pragma unroll
-  for (int nt = 0; nt < NT; nt++) {
-    const int n = row_base + nt * 16 + col;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = mt * 16 + 4 * h + i;
-        if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i];
-      }
+  // copying waves join the reduction's two barriers
+  if constexpr (S::WK > 1) {
+    __syncthreads();
+    __syncthreads();
   }
 }
 
@@ -366,82 +575,159 @@ k_split_reduce(const float* __restrict__ ws, float* __restrict__ y, size_t count
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+
+// Workgroup arrangements: row groups x K-slices x 16-row tiles per wave, and
+// the round size (rd = 2: half the default round).
+struct Plan {
+  int wr, wk, nt, rd;
+};
+static constexpr Plan kPlans[] = {
+    {1, 4, 1, 1},  // 0: 16 rows, 4 K-slices
+    {1, 8, 1, 1},  // 1: 16 rows, 8 K-slices
+    {4, 1, 1, 1},  // 2: 64 rows, whole chunks per wave
+    {2, 4, 1, 1},  // 3: 32 rows, 4 K-slices
+    {2, 2, 1, 1},  // 4: 32 rows, 2 K-slices
+    {4, 2, 1, 1},  // 5: 64 rows, 2 K-slices
+    {1, 4, 1, 2},  // 6: as 0, half rounds
+    {4, 2, 1, 2},  // 7: as 5, half rounds
+    {2, 4, 1, 2},  // 8: as 3, half rounds
+    {4, 1, 1, 2},  // 9: as 2, half rounds
+};
+constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
+
+static int round_k(int fmt, int mt, int group, int plan) {
+  const Plan& q = kPlans[plan];
+  return mm_round(fmt, mt, q.wk, group, q.rd);
+}
+
+static bool plan_fits(int fmt, int mt, int g, const Plan& q) {
+  const int kc = mm_kc(fmt, mt, q.wk, g, q.rd);
+  const int round = q.wk * kc;
+  const int dx = mm_xdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
+  const int dc = mm_cdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
+  const int rs = fmt == FMT_S8 ? round : round / 2;
+  const int red = q.wk > 1 ? q.wr * q.wk * 64 * q.nt * mt * 4 * 4 : 0;
+  if (kc % g != 0 || kc / g > 8) return false;
+  if (fmt == FMT_A4 && (SUPERBLOCK % kc != 0 || round % SUPERBLOCK != 0)) return false;
+  if (fmt != FMT_A4 && (round / g) % 2 != 0) return false;
+  if (rs / 16 < 8 || ((rs / 16) & (rs / 16 - 1)) != 0) return false;
+  const int bytes = (dx + 1) * mm_xslot(fmt, mt, g, q.wk, q.rd) +
+                    (dc + 1) * mm_cslot(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
+  return dx >= 1 && dc >= 1 && bytes <= LDS_LIMIT && red * 4 <= LDS_LIMIT;
+}
+
+// The plan can run this problem: K is a whole number of rounds, a row's
+// scales are whole dwords, and the workgroup's layout fits the LDS.
+static bool plan_ok(int fmt, int mt, int group, int K, int plan) {
+  const int rk = round_k(fmt, mt, group, plan);
+  return K % rk == 0 && (K / group) % 2 == 0 && plan_fits(fmt, mt, group, kPlans[plan]);
+}
+
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
   return c.splits > 1 ? (size_t)c.splits * M * N : 0;
 }
 
-
 bool gemm_supports(int fmt, int M, int K, int group) {
   const int mt = (M + 15) / 16;
-  return K % gemm_kc(fmt, mt, group) == 0;
+  for (int p = 0; p < kNumPlans; p++)
+    if (plan_ok(fmt, mt, group, K, p)) return true;
+  return false;
 }
 
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
   GemmCfg c{};
   c.mt = (M + 15) / 16;
-  c.nt = 1;  // two N-tiles per wave measured slower (registers, occupancy)
+  c.splits = 1;
   const Tuning& tu = tuning();
-  if (tu.gemm_nt) c.nt = tu.gemm_nt == 1 ? 1 : 2;
-  if (c.mt > 2) c.nt = 1;
-  const int rowblocks = (N + 64 * c.nt - 1) / (64 * c.nt);
-  const int kc = gemm_kc(fmt, c.mt, group);
-  const int maxsplit = K / kc;  // the caller has checked K % kc == 0
-  // About 256 workgroups (512 for K >= 8192, whose rows are long enough to
-  // split further), measured best on MI355X for the RWKV-7 shapes; splits must
-  // divide K into whole chunks and the partial sums stay under 64 MiB.
-  const int target = (K >= 8192) ? 512 : 256;
-  int want = (target + rowblocks - 1) / rowblocks;
-  if (tu.gemm_splits) want = tu.gemm_splits;
+  // Preference order by row count: with few rows, more K-slices per
+  // workgroup keep one workgroup per CU busy; with many rows, whole chunks per
+  // wave and 64-row workgroups cut the x staging per row (measured on MI355X
+  // for the RWKV-7 shapes, weights cold in HBM).
+  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9};
+  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9};
+  static const int large_n[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1};
+  const int* order = N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n);
+  c.plan = -1;
+  if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
+      plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
+    c.plan = tu.gemm_plan - 1;
+  for (int i = 0; i < kNumPlans && c.plan < 0; i++)
+    if (plan_ok(fmt, c.mt, group, K, order[i])) c.plan = order[i];
+  // K is split over workgroups only on request (RQ_GEMM_SPLITS): measured on
+  // MI355X, the extra reduce launch costs more than the x staging it saves
+  // for every RWKV-7 shape up to M = 64.  Splits divide K into whole rounds
+  // and the partial sums stay under 64 MiB.
+  const int maxsplit = K / round_k(fmt, c.mt, group, c.plan);
+  int want = tu.gemm_splits ? tu.gemm_splits : 1;
   if (want > maxsplit) want = maxsplit;
   if (want < 1) want = 1;
   int s = want;
-  while (s > 1 && (maxsplit % s != 0 || (size_t)s * M * N * 4 > ((size_t)64 << 20))) s--;
+  const int nr = K / round_k(fmt, c.mt, group, c.plan);
+  while (s > 1 && (nr % s != 0 || (size_t)s * M * N * 4 > ((size_t)64 << 20))) s--;
   c.splits = s;
   return c;
 }
 
-template <int FMT, int MT, int NT, int G>
-static void launch_g(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
-  constexpr int KC = gemm_kc(FMT, MT, G);
-  const int rowblocks = (p.N + 64 * NT - 1) / (64 * NT);
+template <class S>
+static void launch_s(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+  if constexpr (!S::FITS) {
+    return;  // never chosen (plan_ok)
+  } else {
+  const int blocks = (p.N + S::ROWS - 1) / S::ROWS;
   const int kr = p.K / c.splits;
   float* out = (c.splits > 1) ? ws : p.y;
-  hipLaunchKernelGGL((k_gemm<FMT, MT, NT, KC, G>), dim3(rowblocks, c.splits),
-                     dim3(64 * GEMM_WAVES), 0, s, static_cast<const uint8_t*>(p.qweight),
-                     p.scales, p.zeros, static_cast<const _Float16*>(p.x), out, p.M, p.N,
-                     p.K, kr);
+  hipLaunchKernelGGL((k_mm<S>), dim3(blocks, c.splits), dim3(S::THREADS), 0, s,
+                     static_cast<const uint8_t*>(p.qweight), p.scales, p.zeros,
+                     static_cast<const _Float16*>(p.x), out, p.M, p.N, p.K, kr);
   if (c.splits > 1) {
     const size_t count = (size_t)p.M * p.N;
-    size_t blocks = (count + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, ws, p.y,
-                       count, c.splits);
+    size_t rb = (count + 255) / 256;
+    if (rb > 1024) rb = 1024;
+    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)rb), dim3(256), 0, s, ws, p.y, count,
+                       c.splits);
+  }
   }
 }
 
-template <int FMT, int MT, int NT>
+template <int FMT, int MT, int G>
+static void launch_plan(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+  switch (c.plan) {
+    case 0: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 1>>(p, c, ws, s);
+    case 1: return launch_s<Mm<FMT, MT, 1, 1, 8, G, 1>>(p, c, ws, s);
+    case 2: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 1>>(p, c, ws, s);
+    case 3: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 1>>(p, c, ws, s);
+    case 4: return launch_s<Mm<FMT, MT, 1, 2, 2, G, 1>>(p, c, ws, s);
+    case 5: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 1>>(p, c, ws, s);
+    case 6: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 2>>(p, c, ws, s);
+    case 7: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 2>>(p, c, ws, s);
+    case 8: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 2>>(p, c, ws, s);
+    default: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, c, ws, s);
+  }
+}
+
+template <int FMT, int MT>
 static void launch_group(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
   if constexpr (FMT == FMT_S8) {
-    if (p.group == 16) return launch_g<FMT, MT, NT, 16>(p, c, ws, s);
-    if (p.group == 32) return launch_g<FMT, MT, NT, 32>(p, c, ws, s);
-    return launch_g<FMT, MT, NT, 64>(p, c, ws, s);
+    if (p.group == 16) return launch_plan<FMT, MT, 16>(p, c, ws, s);
+    if (p.group == 32) return launch_plan<FMT, MT, 32>(p, c, ws, s);
+    return launch_plan<FMT, MT, 64>(p, c, ws, s);
   } else if constexpr (FMT == FMT_A4) {
-    return launch_g<FMT, MT, NT, 32>(p, c, ws, s);
+    return launch_plan<FMT, MT, 32>(p, c, ws, s);
   } else {
-    if (p.group == 32) return launch_g<FMT, MT, NT, 32>(p, c, ws, s);
-    if (p.group == 64) return launch_g<FMT, MT, NT, 64>(p, c, ws, s);
-    return launch_g<FMT, MT, NT, 128>(p, c, ws, s);
+    if (p.group == 32) return launch_plan<FMT, MT, 32>(p, c, ws, s);
+    if (p.group == 64) return launch_plan<FMT, MT, 64>(p, c, ws, s);
+    return launch_plan<FMT, MT, 128>(p, c, ws, s);
   }
 }
 
 template <int FMT>
 static void launch_fmt(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
-#define RQ_G(MT_, NT_) \
-  if (c.mt == MT_ && c.nt == NT_) return launch_group<FMT, MT_, NT_>(p, c, ws, s)
-  // two N-tiles per wave only up to M = 32 (above, the registers run out)
-  RQ_G(1, 2); RQ_G(2, 2);
-  RQ_G(1, 1); RQ_G(2, 1); RQ_G(3, 1); RQ_G(4, 1);
-#undef RQ_G
+  switch (c.mt) {
+    case 1: return launch_group<FMT, 1>(p, c, ws, s);
+    case 2: return launch_group<FMT, 2>(p, c, ws, s);
+    case 3: return launch_group<FMT, 3>(p, c, ws, s);
+    default: return launch_group<FMT, 4>(p, c, ws, s);
+  }
 }
 
 hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {

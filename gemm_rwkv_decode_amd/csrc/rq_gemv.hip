@@ -391,7 +391,7 @@ GemvCfg choose_gemv(int fmt, int M, int N, int K) {
   // activation rows per launch: the smallest of 1, 2, 4, 8 covering M (or 8)
   c.mt = M <= 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));
   const int chunks = (fmt == FMT_S8) ? K / 16 : K / 32;
-  // measured on MI355X (C4 shapes, cold): one 16-byte chunk per lane and four
+  // measured on MI355X (width-4096 shapes, weights cold in HBM): one 16-byte chunk per lane and four
   // rows per lane beat wider per-lane slices, whose extra registers cost
   // occupancy
   static const int cand1[][3] = {{16, 1, 4}, {32, 1, 4}, {64, 1, 4}, {16, 1, 8},

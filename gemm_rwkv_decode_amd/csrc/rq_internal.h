@@ -7,10 +7,10 @@
 namespace rq {
 
 // Launch-shape overrides for measurements and tests, read from the
-// environment once (RQ_GEMV_LPR, RQ_GEMV_CPL, RQ_GEMV_NPASS, RQ_GEMM_NT,
+// environment once (RQ_GEMV_LPR, RQ_GEMV_CPL, RQ_GEMV_NPASS, RQ_GEMM_PLAN,
 // RQ_GEMM_SPLITS; 0 = no override) and again on rq_tuning_reload().
 struct Tuning {
-  int gemv_lpr, gemv_cpl, gemv_npass, gemm_nt, gemm_splits;
+  int gemv_lpr, gemv_cpl, gemv_npass, gemm_plan, gemm_splits;
 };
 const Tuning& tuning();
 
@@ -43,12 +43,12 @@ hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c
                             hipStream_t s);
 
 struct GemmCfg {
-  int nt;      // 16-row N-tiles per wave (4 waves per workgroup)
   int mt;      // 16-row M-tiles (1..4)
+  int plan;    // workgroup arrangement (index into the kernel's plan table)
   int splits;  // K split across workgroups
 };
 
-// The matrix-core kernel needs K to be a whole number of its LDS chunks.
+// The matrix-core kernel needs K to be a whole number of its rounds.
 bool gemm_supports(int fmt, int M, int K, int group);
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group);
 // ws: float workspace of at least splits*M*N entries (unused when

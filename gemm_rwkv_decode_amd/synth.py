@@ -23,7 +23,7 @@ Shapes and statistics follow the pages:
 
 Every random tensor comes from its own ``torch.Generator`` whose seed is the
 first 8 bytes (little endian, masked to 63 bits) of
-``sha256("rq/c{config}/l{layer}/m{matrix}/{role}/{format}/M{M}")``.  The same
+``sha256("rq/{workload}/l{layer}/m{matrix}/{role}/{format}/M{M}")``.  The same
 seed on a CPU generator and on a GPU generator gives different (but equally
 seeded) streams; a test compares a GPU result with the oracle on the very
 tensors the GPU consumed.
@@ -85,7 +85,7 @@ class XSpec:
 
 @dataclass(frozen=True)
 class Config:
-    cid: int
+    key: str                  # short workload name, also part of every seed
     name: str
     width: int
     layers: int
@@ -93,9 +93,14 @@ class Config:
     ms: Tuple[int, ...]
     x: XSpec
     single: bool = False      # one matrix only (N = K = width)
+    head: bool = False        # the step includes the 65536 x width head
 
-    def matrices(self, with_head: bool = False) -> List[Tuple[int, int, int, int]]:
-        """(layer, mat, N, K) for one decode step, in execution order."""
+    def matrices(self, with_head: Optional[bool] = None) -> List[Tuple[int, int, int, int]]:
+        """(layer, mat, N, K) for one decode step, in execution order; the head
+        (mat 6) is listed as layer `layers` when included (default: the
+        workload's own choice)."""
+        if with_head is None:
+            with_head = self.head
         D = self.width
         if self.single:
             return [(0, 0, D, D)]
@@ -106,30 +111,31 @@ class Config:
             out.append((self.layers, 6, 65536, D))
         return out
 
-    def step_weight_bytes(self, fmt: Fmt, with_head: bool = False) -> int:
+    def step_weight_bytes(self, fmt: Fmt, with_head: Optional[bool] = None) -> int:
         return sum(fmt.weight_bytes(n, k) for _, _, n, k in self.matrices(with_head))
 
 
-CONFIGS: Dict[int, Config] = {
-    0: Config(0, "single int4-g64 GEMV, 768x768", 768, 1, (INT4_G64,), (1,),
-              XSpec("plain"), single=True),
-    1: Config(1, "RWKV-7 0.1B-shaped decode sweep", 768, 12, (INT4_G64,), (1,),
-              XSpec("fixed", channel=300, factor=50.0)),
-    2: Config(2, "RWKV-7 1.5B-shaped projections", 2048, 24, (INT8_G16, INT4_G64),
-              (1, 4, 16, 32), XSpec("fixed", channel=1202, factor=50.0)),
-    3: Config(3, "RWKV-7 2.9B-shaped projections, asymmetric", 2560, 32,
-              (ASYM4_G32,), (1, 8, 32),
-              XSpec("energy", forced=(517,), count=8, share=0.98)),
-    4: Config(4, "RWKV-7 13.3B-shaped projections", 4096, 61, (INT4_G64,),
-              (1, 16, 32, 64), XSpec("energy", count=8, share=0.99)),
-}
+_WORKLOADS = (
+    Config("gemv768", "single int4-g64 GEMV, 768x768", 768, 1, (INT4_G64,), (1,),
+           XSpec("plain"), single=True),
+    Config("rwkv7-0.1b", "RWKV-7 0.1B-shaped decode sweep", 768, 12, (INT4_G64,), (1,),
+           XSpec("fixed", channel=300, factor=50.0)),
+    Config("rwkv7-1.5b", "RWKV-7 1.5B-shaped projections", 2048, 24, (INT8_G16, INT4_G64),
+           (1, 4, 16, 32), XSpec("fixed", channel=1202, factor=50.0)),
+    Config("rwkv7-2.9b", "RWKV-7 2.9B-shaped projections, asymmetric", 2560, 32,
+           (ASYM4_G32,), (1, 8, 32), XSpec("energy", forced=(517,), count=8, share=0.98)),
+    Config("rwkv7-13.3b", "RWKV-7 13.3B-shaped projections and head", 4096, 61,
+           (INT4_G64,), (1, 16, 32, 64), XSpec("energy", count=8, share=0.99), head=True),
+)
+# the workloads by name, smallest first
+CONFIGS: Dict[str, Config] = {c.key: c for c in _WORKLOADS}
 
 
 # --------------------------------------------------------------------------
 # seeds
 # --------------------------------------------------------------------------
-def seed_for(cid: int, layer: int, mat: int, role: str, fmt_tag: str, M: int) -> int:
-    key = f"rq/c{cid}/l{layer}/m{mat}/{role}/{fmt_tag}/M{M}".encode()
+def seed_for(wkey: str, layer: int, mat: int, role: str, fmt_tag: str, M: int) -> int:
+    key = f"rq/{wkey}/l{layer}/m{mat}/{role}/{fmt_tag}/M{M}".encode()
     return int.from_bytes(hashlib.sha256(key).digest()[:8], "little") & ((1 << 63) - 1)
 
 
@@ -209,14 +215,14 @@ def encode(codes: torch.Tensor, fmt: Fmt, scales=None, d=None, sc=None, m=None,
     return Packed(qw, pack_records(d, sc), pack_records(m, mn), N, K, fmt)
 
 
-def gen_matrix(cid: int, layer: int, mat: int, N: int, K: int, fmt: Fmt,
+def gen_matrix(wkey: str, layer: int, mat: int, N: int, K: int, fmt: Fmt,
                device="cpu", keep_codes: bool = False):
     """Seeded packed weights for one matrix.  Returns ``Packed`` (and the
     unpacked int8 codes when ``keep_codes``)."""
     dev = torch.device(device)
-    gc = generator(seed_for(cid, layer, mat, "codes", fmt.tag, 0), dev)
+    gc = generator(seed_for(wkey, layer, mat, "codes", fmt.tag, 0), dev)
     codes = gen_codes(N, K, fmt, gc, dev)
-    gs = generator(seed_for(cid, layer, mat, "scales", fmt.tag, 0), dev)
+    gs = generator(seed_for(wkey, layer, mat, "scales", fmt.tag, 0), dev)
     if fmt.layout == LAYOUT_SYM:
         scales = log_uniform_half((N, K // fmt.group), 1e-3, 1e-1, gs, dev)
         p = encode(codes, fmt, scales=scales)
@@ -225,7 +231,7 @@ def gen_matrix(cid: int, layer: int, mat: int, N: int, K: int, fmt: Fmt,
         d = log_uniform_half((N, B), 1e-4, 2e-3, gs, dev)
         sc = torch.randint(0, 64, (N, B, 8), generator=gs, device=dev,
                            dtype=torch.int16).to(torch.uint8)
-        gz = generator(seed_for(cid, layer, mat, "zeros", fmt.tag, 0), dev)
+        gz = generator(seed_for(wkey, layer, mat, "zeros", fmt.tag, 0), dev)
         m = log_uniform_half((N, B), 1e-4, 2e-3, gz, dev)
         mn = torch.randint(0, 64, (N, B, 8), generator=gz, device=dev,
                            dtype=torch.int16).to(torch.uint8)
@@ -243,7 +249,7 @@ def massive_channels(cfg: Config, layer: int, mat: int, K: int) -> Tuple[List[in
         return [], 1.0
     if xs.kind == "fixed":
         return [xs.channel], xs.factor
-    g = generator(seed_for(cfg.cid, layer, mat, "channels", "x", 0), "cpu")
+    g = generator(seed_for(cfg.key, layer, mat, "channels", "x", 0), "cpu")
     chosen = [c for c in xs.forced]
     for c in torch.randperm(K, generator=g).tolist():
         if len(chosen) == xs.count:
@@ -261,7 +267,7 @@ def gen_x(cfg: Config, layer: int, mat: int, M: int, K: int, device="cpu",
     """fp16 activations [M][K]: N(0,1) in fp32, massive channels multiplied in
     fp32, then one rounding to binary16.  All M rows share the channel set."""
     dev = torch.device(device)
-    g = generator(seed_for(cfg.cid, layer, mat, "x", fmt_tag, M), dev)
+    g = generator(seed_for(cfg.key, layer, mat, "x", fmt_tag, M), dev)
     x = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32)
     chans, mult = massive_channels(cfg, layer, mat, K)
     if chans:

@@ -33,7 +33,8 @@ int rq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 int rq_probe_empty(void* stream);
 
 /* Re-read the launch-shape override variables (RQ_GEMV_LPR, RQ_GEMV_CPL,
- * RQ_GEMV_NPASS, RQ_GEMM_NT, RQ_GEMM_SPLITS; unset or 0 = the library's own
+ * RQ_GEMV_NPASS, RQ_GEMM_PLAN (1-based index of a workgroup arrangement of
+ * the matrix-core kernel), RQ_GEMM_SPLITS; unset or 0 = the library's own
  * choice).  They are read once, at the first call, otherwise.  For tuning
  * sweeps and tests; not thread-safe against concurrent products. */
 int rq_tuning_reload(void);

@@ -40,7 +40,7 @@ def tune(monkeypatch):
 
 
 def small(fmt, N, K, tag=0):
-    p = S.gen_matrix(90 + tag, 0, 0, N, K, fmt)
+    p = S.gen_matrix(f"t{90 + tag}", 0, 0, N, K, fmt)
     return T.to_dev(p)
 
 
@@ -88,7 +88,7 @@ def test_dequant_subnormal_and_extreme_values(f):
     -128 (8-bit): still bit-exact."""
     N, K = 16, 512
     T.say(f"dequant extremes {f.tag}")
-    p, codes = S.gen_matrix(77, 0, 0, N, K, f, keep_codes=True)
+    p, codes = S.gen_matrix("t77", 0, 0, N, K, f, keep_codes=True)
     if f.layout == S.LAYOUT_SYM:
         lo = -8 if f.bits == 4 else -128
         codes[:, ::5] = lo
@@ -180,18 +180,36 @@ def test_gemv_launch_shapes(tune, lpr, cpl, npass):
         T.assert_close(y1, yr1, b1, f"M=1 lpr={lpr} cpl={cpl} npass={npass} {f.tag}")
 
 
+GEMM_PLANS = [str(i) for i in range(1, 11)]  # every workgroup arrangement
+
+
 @pytest.mark.parametrize("splits", ["1", "2", "4", "16"])
-@pytest.mark.parametrize("nt", ["1", "2"])
-def test_gemm_split_and_tiles(tune, splits, nt):
-    tune(RQ_GEMM_SPLITS=splits, RQ_GEMM_NT=nt)
+@pytest.mark.parametrize("plan", GEMM_PLANS)
+def test_gemm_split_and_plans(tune, splits, plan):
+    """Every workgroup arrangement of the matrix-core kernel, with and without
+    K split over workgroups, ragged N."""
+    tune(RQ_GEMM_SPLITS=splits, RQ_GEMM_PLAN=plan)
     for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
         p = small(f, 300, 4096, tag=6)
         for M in (16, 33, 64):
-            T.say(f"gemm splits={splits} nt={nt} {f.tag} M={M}")
+            T.say(f"gemm splits={splits} plan={plan} {f.tag} M={M}")
             x = x_for(M, 4096, seed=M)
             y = T.run("gemm", p, x)
             yr, b = T.oracle_y(p, x)
-            T.assert_close(y, yr, b, f"splits={splits} nt={nt} {f.tag} M={M}")
+            T.assert_close(y, yr, b, f"splits={splits} plan={plan} {f.tag} M={M}")
+
+
+@pytest.mark.parametrize("plan", GEMM_PLANS)
+@pytest.mark.parametrize("f", T.ALL_FORMATS, ids=lambda f: f.tag)
+def test_gemm_plans_all_formats(tune, plan, f):
+    tune(RQ_GEMM_PLAN=plan)
+    p = small(f, 130, 2048, tag=9)
+    for M in (17, 48):
+        T.say(f"gemm plan={plan} {f.tag} M={M}")
+        x = x_for(M, 2048, seed=M + 1)
+        y = T.run("gemm", p, x)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"plan={plan} {f.tag} M={M}")
 
 
 # ------------------------------------------------------ exact cases ---
@@ -217,7 +235,7 @@ def test_integer_inputs_are_exact(f, entry):
     """Unit scales and small integer x: every partial sum is an exact integer
     in binary32, so y must equal the integer matmul of the unpacked codes."""
     N, K = 96, 2048
-    p, codes = S.gen_matrix(91, 0, 0, N, K, f, keep_codes=True)
+    p, codes = S.gen_matrix("t91", 0, 0, N, K, f, keep_codes=True)
     if f.layout == S.LAYOUT_SYM:
         p = S.encode(codes, f, scales=torch.ones((N, K // f.group), dtype=torch.float16))
         W = codes.to(torch.int64)

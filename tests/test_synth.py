@@ -34,7 +34,7 @@ def test_pack_records_matches_oracle_packer():
 @pytest.mark.parametrize("fmt", [S.INT4_G64, S.INT8_G16, S.ASYM4_G32])
 def test_gen_matrix_decodes_to_its_codes(fmt):
     N, K = 24, 512
-    p, codes = S.gen_matrix(9, 0, 0, N, K, fmt, keep_codes=True)
+    p, codes = S.gen_matrix("t9", 0, 0, N, K, fmt, keep_codes=True)
     got = O.unpack_codes(p.qweight.numpy(), N, K, fmt.bits, fmt.layout)
     assert np.array_equal(got, codes.numpy())
     lo, hi = fmt.code_range()
@@ -56,20 +56,20 @@ def test_gen_matrix_decodes_to_its_codes(fmt):
 
 
 def test_seeds_are_reproducible_and_distinct():
-    a = S.gen_matrix(4, 3, 1, 8, 256, S.INT4_G64)
-    b = S.gen_matrix(4, 3, 1, 8, 256, S.INT4_G64)
-    c = S.gen_matrix(4, 3, 2, 8, 256, S.INT4_G64)
+    a = S.gen_matrix("rwkv7-13.3b", 3, 1, 8, 256, S.INT4_G64)
+    b = S.gen_matrix("rwkv7-13.3b", 3, 1, 8, 256, S.INT4_G64)
+    c = S.gen_matrix("rwkv7-13.3b", 3, 2, 8, 256, S.INT4_G64)
     assert torch.equal(a.qweight, b.qweight) and torch.equal(a.scales, b.scales)
     assert not torch.equal(a.qweight, c.qweight)
-    s = {S.seed_for(4, l, m, r, "int4g64", 1) for l in range(3) for m in range(7)
+    s = {S.seed_for("rwkv7-13.3b", l, m, r, "int4g64", 1) for l in range(3) for m in range(7)
          for r in ("codes", "scales", "x")}
     assert len(s) == 3 * 7 * 3
 
 
 def test_massive_channels_fixed():
-    cfg = S.CONFIGS[2]
+    cfg = S.CONFIGS["rwkv7-1.5b"]
     x = S.gen_x(cfg, 0, 0, 4, 2048)
-    plain = S.gen_x(S.CONFIGS[2], 0, 0, 4, 2048).float()
+    plain = S.gen_x(S.CONFIGS["rwkv7-1.5b"], 0, 0, 4, 2048).float()
     chans, mult = S.massive_channels(cfg, 0, 0, 2048)
     assert chans == [1202] and mult == 50.0
     assert torch.equal(x.float(), plain)
@@ -79,13 +79,15 @@ def test_massive_channels_fixed():
     assert big > 10 * rest
 
 
-@pytest.mark.parametrize("cid,K,share", [(3, 2560, 0.98), (3, 10240, 0.98),
-                                         (4, 4096, 0.99), (4, 16384, 0.99)])
-def test_massive_channels_energy_share(cid, K, share):
-    cfg = S.CONFIGS[cid]
+@pytest.mark.parametrize("wkey,K,share", [("rwkv7-2.9b", 2560, 0.98),
+                                          ("rwkv7-2.9b", 10240, 0.98),
+                                          ("rwkv7-13.3b", 4096, 0.99),
+                                          ("rwkv7-13.3b", 16384, 0.99)])
+def test_massive_channels_energy_share(wkey, K, share):
+    cfg = S.CONFIGS[wkey]
     chans, alpha = S.massive_channels(cfg, 5, 3, K)
     assert len(chans) == 8 and len(set(chans)) == 8 and max(chans) < K
-    if cid == 3:
+    if wkey == "rwkv7-2.9b":
         assert 517 in chans
     x = S.gen_x(cfg, 5, 3, 64, K).double()
     e = (x ** 2).sum(dim=1)
@@ -96,10 +98,17 @@ def test_massive_channels_energy_share(cid, K, share):
 
 def test_step_sizes_match_the_configs():
     # 13.3B shape: 61 layers x (4 x 4096^2 + 2 x 16384x4096) int4 g64
-    assert S.CONFIGS[4].step_weight_bytes(S.INT4_G64) == 61 * (4 * 4096 * 4096 + 2 * 16384 * 4096) * 17 // 32
-    assert len(S.CONFIGS[4].matrices()) == 366
-    assert len(S.CONFIGS[1].matrices()) == 72
-    assert S.CONFIGS[0].matrices() == [(0, 0, 768, 768)]
+    c = S.CONFIGS["rwkv7-13.3b"]
+    assert c.step_weight_bytes(S.INT4_G64, with_head=False) == \
+        61 * (4 * 4096 * 4096 + 2 * 16384 * 4096) * 17 // 32
+    assert len(c.matrices(with_head=False)) == 366
+    # with the 65536 x 4096 head: about 6.7 GB per step
+    assert len(c.matrices()) == 367 and c.matrices()[-1] == (61, 6, 65536, 4096)
+    assert c.step_weight_bytes(S.INT4_G64) == \
+        (61 * (4 * 4096 * 4096 + 2 * 16384 * 4096) + 65536 * 4096) * 17 // 32
+    assert 6.6e9 < c.step_weight_bytes(S.INT4_G64) < 6.7e9
+    assert len(S.CONFIGS["rwkv7-0.1b"].matrices()) == 72
+    assert S.CONFIGS["gemv768"].matrices() == [(0, 0, 768, 768)]
     # int8 g16 carries 9 bits per weight, asym 4.5
     assert S.INT8_G16.weight_bytes(2048, 2048) * 8 == 2048 * 2048 * 9
     assert S.ASYM4_G32.weight_bytes(2560, 2560) * 8 == 2560 * 2560 * 9 // 2
