@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["rq_api.hip", "rq_dequant.hip", "rq_gemv.hip", "rq_gemm.hip", "rq_probe.hip"]
+SOURCES = ["rq_api.hip", "rq_dequant.hip", "rq_gemv.hip", "rq_gemm.hip", "rq_mv.hip",
+           "rq_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -28,7 +28,7 @@ static int env_or_zero(const char* name) {
 static void read_tuning() {
   g_tuning = Tuning{env_or_zero("RQ_GEMV_LPR"), env_or_zero("RQ_GEMV_CPL"),
                     env_or_zero("RQ_GEMV_NPASS"), env_or_zero("RQ_GEMM_PLAN"),
-                    env_or_zero("RQ_GEMM_SPLITS")};
+                    env_or_zero("RQ_GEMM_SPLITS"), env_or_zero("RQ_GEMV_KERNEL")};
 }
 
 const Tuning& tuning() {
@@ -223,8 +223,14 @@ rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
   st = check_device(&dev);
   if (st != RQ_OK) return st;
   rq::Problem p{qweight, scales, zeros, x, y, M, N, K, group, fmt};
-  const rq::GemvCfg c = rq::choose_gemv(fmt, M, N, K);
-  const hipError_t e = rq::launch_gemv(p, c, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (rq::use_mv(fmt, M, K, group)) {
+    const rq::Problem* one = &p;
+    e = rq::launch_mv_many(&one, 1, s);
+  } else {
+    e = rq::launch_gemv(p, rq::choose_gemv(fmt, M, N, K), s);
+  }
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 
@@ -274,8 +280,12 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
         done[j] = true;
       }
     }
-    const rq::GemvCfg c = rq::choose_gemv(fmt, M, rows, pb[i].K);
-    if (rq::launch_gemv_many(order, n, c, s) != hipSuccess) return RQ_ERR_LAUNCH;
+    hipError_t e;
+    if (rq::use_mv(fmt, M, pb[i].K, group))
+      e = rq::launch_mv_many(order, n, s);
+    else
+      e = rq::launch_gemv_many(order, n, rq::choose_gemv(fmt, M, rows, pb[i].K), s);
+    if (e != hipSuccess) return RQ_ERR_LAUNCH;
   }
   return RQ_OK;
 }

@@ -8,9 +8,11 @@ namespace rq {
 
 // Launch-shape overrides for measurements and tests, read from the
 // environment once (RQ_GEMV_LPR, RQ_GEMV_CPL, RQ_GEMV_NPASS, RQ_GEMM_PLAN,
-// RQ_GEMM_SPLITS; 0 = no override) and again on rq_tuning_reload().
+// RQ_GEMM_SPLITS, RQ_GEMV_KERNEL; 0 = no override) and again on
+// rq_tuning_reload().
 struct Tuning {
   int gemv_lpr, gemv_cpl, gemv_npass, gemm_plan, gemm_splits;
+  int gemv_kernel;  // M <= 4: 0 automatic, 1 vector-unit kernel, 2 matrix-core kernel
 };
 const Tuning& tuning();
 
@@ -41,6 +43,14 @@ hipError_t launch_gemv(const Problem& p, const GemvCfg& c, hipStream_t s);
 // count problems sharing fmt, K, group and M
 hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c,
                             hipStream_t s);
+
+// Matrix-core kernel for M = 1..4 (rq_mv.hip): problems sharing fmt, K,
+// group and M, up to MV_BATCH per launch.
+constexpr int MV_BATCH = 16;
+bool mv_supports(int fmt, int M, int K, int group);
+// whether rq_gemv / rq_gemv_batched take the matrix-core kernel
+bool use_mv(int fmt, int M, int K, int group);
+hipError_t launch_mv_many(const Problem* const* p, int count, hipStream_t s);
 
 struct GemmCfg {
   int mt;      // 16-row M-tiles (1..4)

@@ -151,7 +151,7 @@ def test_product_parity_odd_k(N, K, f, entry):
 
 def test_generic_kernel_forced(tune):
     """The generic kernel also serves shapes the tuned one handles."""
-    tune(RQ_GEMV_LPR=-1)
+    tune(RQ_GEMV_LPR=-1, RQ_GEMV_KERNEL=1)
     for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
         p = small(f, 45, 1024, tag=4)
         for M in (1, 5):
@@ -166,7 +166,7 @@ def test_generic_kernel_forced(tune):
                                            (16, 2, 4), (64, 1, 4), (8, 1, 8)])
 def test_gemv_launch_shapes(tune, lpr, cpl, npass):
     """Every instantiated launch shape, with a ragged last row block."""
-    tune(RQ_GEMV_LPR=lpr, RQ_GEMV_CPL=cpl, RQ_GEMV_NPASS=npass)
+    tune(RQ_GEMV_LPR=lpr, RQ_GEMV_CPL=cpl, RQ_GEMV_NPASS=npass, RQ_GEMV_KERNEL=1)
     for f in (S.INT4_G64, S.ASYM4_G32, S.INT8_G16):
         p = small(f, 1000, 512, tag=5)
         x = x_for(2, 512, seed=7)
@@ -178,6 +178,45 @@ def test_gemv_launch_shapes(tune, lpr, cpl, npass):
         y1 = T.run("gemv", p, x1)
         yr1, b1 = T.oracle_y(p, x1)
         T.assert_close(y1, yr1, b1, f"M=1 lpr={lpr} cpl={cpl} npass={npass} {f.tag}")
+
+
+# ---------------------------------------------- decode kernels, M <= 4 ---
+def chunk_k(f):
+    """k per chunk of the matrix-core decode kernel (8 groups, or a superblock)."""
+    return 256 if f.layout == S.LAYOUT_ASYM_SB else 8 * f.group
+
+
+@pytest.mark.parametrize("f", T.ALL_FORMATS, ids=lambda f: f.tag)
+@pytest.mark.parametrize("kern", ["vector", "matrix"])
+def test_decode_kernels(tune, f, kern):
+    """Both M <= 4 kernels of rq_gemv, forced: one chunk per wave, waves with
+    unequal chunk counts, several chunks per wave, a ragged last row block
+    and a single row.  Outputs start as NaN."""
+    tune(RQ_GEMV_KERNEL=1 if kern == "vector" else 2)
+    ck = chunk_k(f)
+    for N, K in [(37, 8 * ck), (300, 13 * ck), (129, 32 * ck), (1, 9 * ck)]:
+        p = small(f, N, K, tag=7)
+        for M in (1, 2, 3, 4):
+            what = f"{kern} {f.tag} M={M} N={N} K={K}"
+            T.say(what)
+            x = x_for(M, K, seed=M * 31 + N)
+            y = torch.full((M, N), float("nan"), device="cuda")
+            T.run("gemv", p, x, y)
+            yr, b = T.oracle_y(p, x)
+            T.assert_close(y, yr, b, what)
+
+
+def test_matrix_decode_kernel_falls_back(tune):
+    """Forcing the matrix-core decode kernel where K holds fewer than eight
+    chunks leaves the vector-unit kernel in charge (still correct)."""
+    tune(RQ_GEMV_KERNEL=2)
+    for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
+        K = 4 * chunk_k(f)
+        p = small(f, 70, K, tag=8)
+        x = x_for(2, K, seed=5)
+        y = T.run("gemv", p, x)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"fallback {f.tag}")
 
 
 GEMM_PLANS = [str(i) for i in range(1, 11)]  # every workgroup arrangement
@@ -312,6 +351,7 @@ def test_batched_matches_oracle(f, M):
     """Mixed N and K in one call (K groups share launches), more problems than
     one launch holds, and a K the tuned kernel cannot split."""
     shapes = [(256, 1024), (100, 1024), (300, 2048), (64, 1024)] * 5 + [(40, 768)]
+    shapes += [(130, 4096), (64, 4096), (17, 4096)] * 7  # matrix-core decode kernel at M <= 4
     if f.layout == S.LAYOUT_SYM and f.bits == 4:
         shapes.append((33, 64 * 7))  # 14 chunks: generic kernel
     mats = [small(f, N, K, tag=20 + i) for i, (N, K) in enumerate(shapes)]
