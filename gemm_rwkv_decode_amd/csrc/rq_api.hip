@@ -281,7 +281,11 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
       }
     }
     hipError_t e;
-    if (rq::use_mv(fmt, M, pb[i].K, group))
+    if (M >= rq::MFMA_MIN_M && rq::gemm_supports(fmt, M, pb[i].K, group)) {
+      rq::GemmCfg c = rq::choose_gemm(fmt, M, rows, pb[i].K, group);
+      c.splits = 1;
+      e = rq::launch_gemm_many(order, n, c, nullptr, s);
+    } else if (rq::use_mv(fmt, M, pb[i].K, group))
       e = rq::launch_mv_many(order, n, s);
     else
       e = rq::launch_gemv_many(order, n, rq::choose_gemv(fmt, M, rows, pb[i].K), s);

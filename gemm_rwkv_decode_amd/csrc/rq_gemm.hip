@@ -469,24 +469,50 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
   }
 }
 
+// Problems of one launch (they share the format, M, K and the group size):
+// workgroups [block_begin, next block_begin) along x belong to entry i.
+struct MmEntry {
+  const uint8_t* qw;
+  const void* sc;
+  const void* zr;
+  const _Float16* x;
+  float* out;  // y, or the partial-sum workspace when K is split
+  int N;
+  int block_begin;
+};
+struct MmBatch {
+  MmEntry e[MM_BATCH];
+  int count;
+};
+
 template <class S>
 __global__ void __launch_bounds__(S::THREADS)
-k_mm(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
-     const void* __restrict__ zeros, const _Float16* __restrict__ x,
-     float* __restrict__ out, int M, int N, int K, int kr) {
+k_mm(const MmBatch bt, int M, int K, int kr) {
   constexpr int NT = S::NT, MT = S::MT;
   static_assert(S::FITS, "LDS budget and prefetch depth");
   constexpr int LDS_BYTES = S::LDS_BYTES > S::RED * 4 ? S::LDS_BYTES : S::RED * 4;
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+
+  // this workgroup's problem (uniform scan of the table)
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < MM_BATCH; i++)
+    if (i < bt.count && (int)blockIdx.x >= bt.e[i].block_begin) pi = i;
+  const MmEntry& e = bt.e[pi];
+  const uint8_t* __restrict__ qw = e.qw;
+  const void* __restrict__ scales = e.sc;
+  const void* __restrict__ zeros = e.zr;
+  const _Float16* __restrict__ x = e.x;
+  const int N = e.N;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int split = blockIdx.y;
   const int k_begin = split * kr;
   // y itself, or this K-range's slice of the partial-sum workspace
-  float* __restrict__ y = out + (size_t)split * M * N;
+  float* __restrict__ y = e.out + (size_t)split * M * N;
   const int nrounds = kr / S::ROUND;
-  const int row0 = blockIdx.x * S::ROWS;
+  const int row0 = ((int)blockIdx.x - e.block_begin) * S::ROWS;
 
   if (wave >= S::W) {
     if (wave < S::W + MM_XP)
@@ -668,73 +694,99 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
   return c;
 }
 
+// One launch over p[0..count), count <= MM_BATCH; K is split (c.splits > 1,
+// partial sums in ws) only for a single problem.
 template <class S>
-static void launch_s(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+static void launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
+                     hipStream_t s) {
   if constexpr (!S::FITS) {
     return;  // never chosen (plan_ok)
   } else {
-  const int blocks = (p.N + S::ROWS - 1) / S::ROWS;
-  const int kr = p.K / c.splits;
-  float* out = (c.splits > 1) ? ws : p.y;
-  hipLaunchKernelGGL((k_mm<S>), dim3(blocks, c.splits), dim3(S::THREADS), 0, s,
-                     static_cast<const uint8_t*>(p.qweight), p.scales, p.zeros,
-                     static_cast<const _Float16*>(p.x), out, p.M, p.N, p.K, kr);
+  MmBatch bt{};
+  int blocks = 0;
+  for (int i = 0; i < count; i++) {
+    bt.e[i] = MmEntry{static_cast<const uint8_t*>(p[i]->qweight), p[i]->scales, p[i]->zeros,
+                      static_cast<const _Float16*>(p[i]->x), c.splits > 1 ? ws : p[i]->y,
+                      p[i]->N, blocks};
+    blocks += (p[i]->N + S::ROWS - 1) / S::ROWS;
+  }
+  bt.count = count;
+  const int M = p[0]->M, K = p[0]->K;
+  hipLaunchKernelGGL((k_mm<S>), dim3(blocks, c.splits), dim3(S::THREADS), 0, s, bt, M, K,
+                     K / c.splits);
   if (c.splits > 1) {
-    const size_t count = (size_t)p.M * p.N;
-    size_t rb = (count + 255) / 256;
+    const size_t n = (size_t)M * p[0]->N;
+    size_t rb = (n + 255) / 256;
     if (rb > 1024) rb = 1024;
-    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)rb), dim3(256), 0, s, ws, p.y, count,
+    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)rb), dim3(256), 0, s, ws, p[0]->y, n,
                        c.splits);
   }
   }
 }
 
 template <int FMT, int MT, int G>
-static void launch_plan(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+static void launch_plan(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                        hipStream_t s) {
   switch (c.plan) {
-    case 0: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 1>>(p, c, ws, s);
-    case 1: return launch_s<Mm<FMT, MT, 1, 1, 8, G, 1>>(p, c, ws, s);
-    case 2: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 1>>(p, c, ws, s);
-    case 3: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 1>>(p, c, ws, s);
-    case 4: return launch_s<Mm<FMT, MT, 1, 2, 2, G, 1>>(p, c, ws, s);
-    case 5: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 1>>(p, c, ws, s);
-    case 6: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 2>>(p, c, ws, s);
-    case 7: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 2>>(p, c, ws, s);
-    case 8: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 2>>(p, c, ws, s);
-    default: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, c, ws, s);
+    case 0: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 1>>(p, n, c, ws, s);
+    case 1: return launch_s<Mm<FMT, MT, 1, 1, 8, G, 1>>(p, n, c, ws, s);
+    case 2: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 1>>(p, n, c, ws, s);
+    case 3: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 1>>(p, n, c, ws, s);
+    case 4: return launch_s<Mm<FMT, MT, 1, 2, 2, G, 1>>(p, n, c, ws, s);
+    case 5: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 1>>(p, n, c, ws, s);
+    case 6: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 2>>(p, n, c, ws, s);
+    case 7: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 2>>(p, n, c, ws, s);
+    case 8: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 2>>(p, n, c, ws, s);
+    default: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, n, c, ws, s);
   }
 }
 
 template <int FMT, int MT>
-static void launch_group(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+static void launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                         hipStream_t s) {
+  const int g = p[0]->group;
   if constexpr (FMT == FMT_S8) {
-    if (p.group == 16) return launch_plan<FMT, MT, 16>(p, c, ws, s);
-    if (p.group == 32) return launch_plan<FMT, MT, 32>(p, c, ws, s);
-    return launch_plan<FMT, MT, 64>(p, c, ws, s);
+    if (g == 16) return launch_plan<FMT, MT, 16>(p, n, c, ws, s);
+    if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
   } else if constexpr (FMT == FMT_A4) {
-    return launch_plan<FMT, MT, 32>(p, c, ws, s);
+    return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
   } else {
-    if (p.group == 32) return launch_plan<FMT, MT, 32>(p, c, ws, s);
-    if (p.group == 64) return launch_plan<FMT, MT, 64>(p, c, ws, s);
-    return launch_plan<FMT, MT, 128>(p, c, ws, s);
+    if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
+    if (g == 64) return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 128>(p, n, c, ws, s);
   }
 }
 
 template <int FMT>
-static void launch_fmt(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
+static void launch_fmt(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                       hipStream_t s) {
   switch (c.mt) {
-    case 1: return launch_group<FMT, 1>(p, c, ws, s);
-    case 2: return launch_group<FMT, 2>(p, c, ws, s);
-    case 3: return launch_group<FMT, 3>(p, c, ws, s);
-    default: return launch_group<FMT, 4>(p, c, ws, s);
+    case 1: return launch_group<FMT, 1>(p, n, c, ws, s);
+    case 2: return launch_group<FMT, 2>(p, n, c, ws, s);
+    case 3: return launch_group<FMT, 3>(p, n, c, ws, s);
+    default: return launch_group<FMT, 4>(p, n, c, ws, s);
   }
 }
 
+hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c, float* ws,
+                            hipStream_t s) {
+  if (count > 1 && c.splits > 1) return hipErrorInvalidValue;
+  for (int first = 0; first < count; first += MM_BATCH) {
+    const int n = count - first < MM_BATCH ? count - first : MM_BATCH;
+    const Problem* const* q = p + first;
+    if (q[0]->fmt == FMT_S4) launch_fmt<FMT_S4>(q, n, c, ws, s);
+    else if (q[0]->fmt == FMT_S8) launch_fmt<FMT_S8>(q, n, c, ws, s);
+    else launch_fmt<FMT_A4>(q, n, c, ws, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s) {
-  if (p.fmt == FMT_S4) launch_fmt<FMT_S4>(p, c, ws, s);
-  else if (p.fmt == FMT_S8) launch_fmt<FMT_S8>(p, c, ws, s);
-  else launch_fmt<FMT_A4>(p, c, ws, s);
-  return hipGetLastError();
+  const Problem* one = &p;
+  return launch_gemm_many(&one, 1, c, ws, s);
 }
 
 }  // namespace rq

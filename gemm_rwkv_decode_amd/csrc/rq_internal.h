@@ -58,12 +58,20 @@ struct GemmCfg {
   int splits;  // K split across workgroups
 };
 
+// Smallest M that rq_gemv_batched computes on the matrix-core kernel.
+constexpr int MFMA_MIN_M = 16;
+
 // The matrix-core kernel needs K to be a whole number of its rounds.
 bool gemm_supports(int fmt, int M, int K, int group);
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group);
 // ws: float workspace of at least splits*M*N entries (unused when
 // splits == 1).
 hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s);
+// count problems sharing fmt, M, K and group, MM_BATCH per launch (splits must
+// be 1 when count > 1)
+constexpr int MM_BATCH = 8;
+hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c, float* ws,
+                            hipStream_t s);
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N);
 
 hipError_t launch_dequant(const void* qweight, const void* scales, const void* zeros,

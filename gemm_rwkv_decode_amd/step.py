@@ -48,10 +48,10 @@ def step_calls(mats: Sequence[Tuple[int, int, int, int]], W: Sequence, X: Sequen
 
     kinds:
       "layer"   -- per layer: receptance, key and value in one grouped launch
-                   (rq_gemv_batched) when M < 16, then output, FFN key, FFN
-                   value; the head last.  Matrix-core M (>= 16) has no grouped
-                   entry point and launches per matrix.
-      "matrix"  -- one launch per matrix, in order.
+                   (rq_gemv_batched, which takes the matrix cores from M = 16
+                   on), then output, FFN key, FFN value; the head last.
+      "matrix"  -- one launch per matrix, in order (rq_gemv below M = 16,
+                   rq_gemm_smallm from M = 16 on).
       "batched" -- every product through rq_gemv_batched, up to RQ_MAX_BATCH
                    per call, ignoring the order between layers (a bound on
                    what grouping could reach, not a valid decode order).
@@ -73,13 +73,11 @@ def step_calls(mats: Sequence[Tuple[int, int, int, int]], W: Sequence, X: Sequen
 
     calls = []
     if kind == "batched":
-        if M >= MFMA_MIN_M:
-            raise ValueError("the grouped entry point is the vector-unit path (M < 16)")
         ix = list(range(len(mats)))
         for k in range(0, len(ix), rq.RQ_MAX_BATCH):
             calls.append(grouped(ix[k:k + rq.RQ_MAX_BATCH]))
         return calls
-    if kind == "matrix" or M >= MFMA_MIN_M:
+    if kind == "matrix":
         return [single(i) for i in range(len(mats))]
     by_layer: Dict[int, Dict[int, int]] = {}
     for i, (l, mi, _, _) in enumerate(mats):

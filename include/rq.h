@@ -124,13 +124,16 @@ rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
                   int group, int layout, void* stream);
 
 /*
- * rq_gemv_batched -- `count` independent products, as `count` rq_gemv calls
- * would compute them, issued as few kernel launches as possible: problems
- * with the same K share one launch (up to 16 per launch).  This is the
- * grouped form of the decode step's independent projections -- the package
- * page "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization
- * Details") computes the receptance, key and value projections of a layer in
- * a single kernel.  All problems share M, bits, group and layout; N, K and the
+ * rq_gemv_batched -- `count` independent products, issued as few kernel
+ * launches as possible: problems with the same K share one launch (up to 16
+ * per launch below M = 16, up to 8 from M = 16 on).  Below M = 16 each
+ * product is computed as rq_gemv would compute it; from M = 16 on, as
+ * rq_gemm_smallm would (matrix cores; K is never split in a grouped launch),
+ * except where K does not suit the matrix-core kernel.  This is the grouped
+ * form of the decode step's independent projections -- the package page
+ * "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization Details")
+ * computes the receptance, key and value projections of a layer in a single
+ * kernel.  All problems share M, bits, group and layout; N, K and the
  * pointers are per problem.  `problems` is a host array the call reads before
  * it returns.  No output may overlap another output or any input.
  * Errors as for rq_gemv; a failed call enqueues nothing.

@@ -53,9 +53,14 @@ def test_matrix_cores_from_m16(recorded):
     cfg = S.CONFIGS["rwkv7-2.9b"]
     mats, W, X, Y = fake_step(cfg, 16)
     ST.step_calls(mats, W, X, Y, "layer")
+    # per layer: grouped receptance/key/value, then three matrix-core launches
+    assert [n for n, _ in recorded] == (["rq_gemv_batched"] + ["rq_gemm_smallm"] * 3) * 32
+    assert all(a[1] == 16 for n, a in recorded if n == "rq_gemv_batched")
+    assert all(a[5] == 16 for n, a in recorded if n == "rq_gemm_smallm")
+    assert recorded[1][1][10] == S.LAYOUT_ASYM_SB and recorded[1][1][9] == 32
+    del recorded[:]
+    ST.step_calls(mats, W, X, Y, "matrix")
     assert [n for n, _ in recorded] == ["rq_gemm_smallm"] * len(mats)
-    assert all(a[5] == 16 for _, a in recorded)
-    assert recorded[0][1][10] == S.LAYOUT_ASYM_SB and recorded[0][1][9] == 32
 
 
 def test_matrix_and_batched_kinds(recorded):
@@ -65,8 +70,9 @@ def test_matrix_and_batched_kinds(recorded):
     del recorded[:]
     calls = ST.step_calls(mats, W, X, Y, "batched")
     assert len(calls) == 2 and [len(a[0]) for _, a in recorded] == [64, 8]
-    with pytest.raises(ValueError):
-        ST.step_calls(mats, W, [torch.empty((16, 1))] * 72, Y, "batched")
+    del recorded[:]
+    ST.step_calls(mats, W, [torch.empty((16, 1))] * 72, Y, "batched")
+    assert [(n, a[1]) for n, a in recorded] == [("rq_gemv_batched", 16)] * 2
     with pytest.raises(ValueError):
         ST.step_calls(mats, W, X, Y, "fused")
     assert ST.step_calls([], [], [], [], "layer") == []
