@@ -666,31 +666,44 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
   c.splits = 1;
   const Tuning& tu = tuning();
   // Preference order by row count: with few rows, more K-slices per
-  // workgroup keep one workgroup per CU busy; with many rows, whole chunks per
-  // wave and 64-row workgroups cut the x staging per row (measured on MI355X
-  // for the RWKV-7 shapes, weights cold in HBM).
+  // workgroup keep one workgroup per CU busy; with many rows, 64-row
+  // workgroups cut the x staging per row (every workgroup stages all of x,
+  // M*K*2 bytes, from L2).  Measured on MI355X for the RWKV-7 shapes, int4
+  // g64, weights cold in HBM.
   static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9};
   static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9};
-  static const int large_n[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1};
-  const int* order = N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n);
+  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1};
+  // Few rows and long rows (K >= 16384) or a full M-tile stack (M > 48): the
+  // x staging of 16-row workgroups dominates, so 64-row workgroups with K
+  // split four ways (a second, small kernel adds the partial sums) -- at
+  // 4096x16384: 16.2 -> 15.0 us (M=16), 23.0 -> 18.8 us (M=32),
+  // 45.8 -> 25.0 us (M=64).
+  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1};
+  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1};
+  const bool split_k = N < 8192 && (K >= 16384 || c.mt >= 4);
+  const int* order = split_k ? (c.mt == 1 ? split_n_m16 : split_n)
+                             : (N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n));
   c.plan = -1;
   if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
       plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
     c.plan = tu.gemm_plan - 1;
   for (int i = 0; i < kNumPlans && c.plan < 0; i++)
     if (plan_ok(fmt, c.mt, group, K, order[i])) c.plan = order[i];
-  // K is split over workgroups only on request (RQ_GEMM_SPLITS): measured on
-  // MI355X, the extra reduce launch costs more than the x staging it saves
-  // for every RWKV-7 shape up to M = 64.  Splits divide K into whole rounds
-  // and the partial sums stay under 64 MiB.
-  const int maxsplit = K / round_k(fmt, c.mt, group, c.plan);
-  int want = tu.gemm_splits ? tu.gemm_splits : 1;
-  if (want > maxsplit) want = maxsplit;
-  if (want < 1) want = 1;
-  int s = want;
+  // Splits divide K into whole rounds and the partial sums stay under 64 MiB.
+  // Automatic only in the case above, enough row blocks x K-ranges for 256
+  // CUs (at most 4); RQ_GEMM_SPLITS overrides.
+  const int rows = kPlans[c.plan].wr * kPlans[c.plan].nt * 16;
+  const int blocks = (N + rows - 1) / rows;
+  int want = 1;
+  if (split_k && rows == 64 && blocks < 256) want = (256 + blocks - 1) / blocks;
+  if (want > 4) want = 4;
+  if (tu.gemm_splits) want = tu.gemm_splits;
   const int nr = K / round_k(fmt, c.mt, group, c.plan);
-  while (s > 1 && (nr % s != 0 || (size_t)s * M * N * 4 > ((size_t)64 << 20))) s--;
-  c.splits = s;
+  if (want > nr) want = nr;
+  if (want < 1) want = 1;
+  int sp = want;
+  while (sp > 1 && (nr % sp != 0 || (size_t)sp * M * N * 4 > ((size_t)64 << 20))) sp--;
+  c.splits = sp;
   return c;
 }
 
