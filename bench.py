@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured graph instead of direct launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=2,
+    ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers of the step the CPU oracle times")
     ap.add_argument("--layers", type=int, default=None, help="(testing) fewer layers")
     ap.add_argument("--copy-probe", action="store_true",
