@@ -115,8 +115,10 @@ rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
  * the model card reports against fp16, section "Speed").
  *   x: binary16 [M][K] row-major.  y: float [M][N] row-major, overwritten.
  * Each output is within 1e-3 * sum_k |x[m][k] * w[n][k]| of the exact value
- * (fp32 accumulation).  Tuned for M <= 8 (the per-token decode shape); larger M
- * is processed in passes of up to 8 rows.
+ * (fp32 accumulation).  Tuned for M <= 8 (the per-token decode shape): vector
+ * units at M <= 2; at M = 3..4 a matrix-core kernel where K holds at least
+ * eight of its chunks (8 groups, or one 256-weight superblock, each); larger M
+ * is processed on the vector units in passes of up to 8 rows.
  * Shape rules as for rq_dequant, plus 1 <= M <= RQ_MAX_M.
  */
 rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
