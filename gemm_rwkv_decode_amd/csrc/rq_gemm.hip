@@ -156,6 +156,9 @@ struct Mm {
   static constexpr int GB = (FMT == FMT_S8) ? G : G / 2;  // code bytes per group of a row
   static constexpr int RS = (FMT == FMT_S8) ? ROUND : ROUND / 2;  // code bytes per row and round
   static constexpr int PR = RS / 16;                // 16-byte code pieces per row and round
+  // piece swizzle: row n's piece p sits at n*PR + (p ^ (n & SWZ)); 16 rows of
+  // a fragment read then start in 16 (PR >= 16) or 8 different bank groups
+  static constexpr int SWZ = PR >= 16 ? 15 : 7;
   static constexpr int NSB = ROUND / SUPERBLOCK;    // superblocks per round (asym)
   // scale dwords per row and round: sym, the round's binary16 scales; asym,
   // per kind (scale records, zero records) two dwords per superblock
@@ -188,8 +191,11 @@ struct Mm {
       (FMT != FMT_A4 || (SUPERBLOCK % KC == 0 && ROUND % SUPERBLOCK == 0)) &&
       (FMT == FMT_A4 || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
       SEG_LANES <= 64 && ROUND * 2 % SEG == 0;
-  static constexpr bool FITS = VALID && DX >= 1 && DC >= 1 && LDS_BYTES <= LDS_LIMIT &&
-                               RED * 4 <= LDS_LIMIT;
+  // accumulator tiles per wave the register file holds without spilling:
+  // 12 waves per workgroup leave 168 registers a lane
+  static constexpr bool REGS = NT * MT <= (THREADS > 512 ? 4 : 8);
+  static constexpr bool FITS = VALID && REGS && DX >= 1 && DC >= 1 &&
+                               LDS_BYTES <= LDS_LIMIT && RED * 4 <= LDS_LIMIT;
   static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
                           CN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
                 "copy counts");
@@ -231,7 +237,7 @@ __device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
 
 // Copy c of a round, c in [0, COPIES): x row segments first (rows >= M
 // repeat row M-1; they only feed outputs that are never stored), then code
-// pieces (row n's 16-byte piece p stored at position n*PR + (p ^ (n & 7)), so
+// pieces (row n's 16-byte piece p stored at position n*PR + (p ^ (n & SWZ)), so
 // that the 16 rows a fragment read touches spread over the banks), then scale
 // dwords (row n's dword d at n*SRD + d; asym: scale records, then zero
 // records).  copy_off gives this lane's byte offset from the copy's base,
@@ -248,7 +254,7 @@ __device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, in
     const int n = pos / S::PR, sp = pos % S::PR;
     const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
     const u32 row_bytes = (S::FMT == FMT_S8) ? (u32)K : (u32)K / 2;
-    return (u32)row * row_bytes + (u32)(sp ^ (n & 7)) * 16u;
+    return (u32)row * row_bytes + (u32)(sp ^ (n & S::SWZ)) * 16u;
   } else {
     const int j = (c - S::XN - S::CN) % S::SNK;
     const int q = j * 64 + lane;
@@ -322,7 +328,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
       const int n = wr * S::TR + nt * 16 + col;
       const int byte = cb0 + g * S::GB + h * S::BPL;
       const char* src =
-          sl + S::C_OFF + (n * S::PR + ((byte / 16) ^ (n & 7))) * 16 + byte % 16;
+          sl + S::C_OFF + (n * S::PR + ((byte / 16) ^ (n & S::SWZ))) * 16 + byte % 16;
       if constexpr (S::BPL == 16) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src);
         code[nt][0] = v.x; code[nt][1] = v.y; code[nt][2] = v.z; code[nt][3] = v.w;
@@ -618,6 +624,12 @@ static constexpr Plan kPlans[] = {
     {4, 2, 1, 2},  // 7: as 5, half rounds
     {2, 4, 1, 2},  // 8: as 3, half rounds
     {4, 1, 1, 2},  // 9: as 2, half rounds
+    // two 16-row tiles per wave: each A fragment read from LDS feeds two MFMAs
+    {2, 2, 2, 1},  // 10: 64 rows, 2 K-slices
+    {2, 4, 2, 1},  // 11: 64 rows, 4 K-slices
+    {1, 8, 2, 1},  // 12: 32 rows, 8 K-slices
+    {1, 4, 2, 1},  // 13: 32 rows, 4 K-slices
+    {4, 2, 2, 1},  // 14: 128 rows, 2 K-slices
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -634,6 +646,7 @@ static bool plan_fits(int fmt, int mt, int g, const Plan& q) {
   const int rs = fmt == FMT_S8 ? round : round / 2;
   const int red = q.wk > 1 ? q.wr * q.wk * 64 * q.nt * mt * 4 * 4 : 0;
   if (kc % g != 0 || kc / g > 8) return false;
+  if (q.nt * mt > (64 * (q.wr * q.wk + MM_XP + MM_CP) > 512 ? 4 : 8)) return false;
   if (fmt == FMT_A4 && (SUPERBLOCK % kc != 0 || round % SUPERBLOCK != 0)) return false;
   if (fmt != FMT_A4 && (round / g) % 2 != 0) return false;
   if (rs / 16 < 8 || ((rs / 16) & (rs / 16 - 1)) != 0) return false;
@@ -670,16 +683,16 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
   // workgroups cut the x staging per row (every workgroup stages all of x,
   // M*K*2 bytes, from L2).  Measured on MI355X for the RWKV-7 shapes, int4
   // g64, weights cold in HBM.
-  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9};
-  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9};
-  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1};
+  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14};
+  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14};
+  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14};
   // Few rows and long rows (K >= 16384) or a full M-tile stack (M > 48): the
   // x staging of 16-row workgroups dominates, so 64-row workgroups with K
   // split four ways (a second, small kernel adds the partial sums) -- at
   // 4096x16384: 16.2 -> 15.0 us (M=16), 23.0 -> 18.8 us (M=32),
   // 45.8 -> 25.0 us (M=64).
-  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1};
-  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1};
+  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14};
+  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14};
   const bool split_k = N < 8192 && (K >= 16384 || c.mt >= 4);
   const int* order = split_k ? (c.mt == 1 ? split_n_m16 : split_n)
                              : (N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n));
@@ -750,7 +763,12 @@ static void launch_plan(const Problem* const* p, int n, const GemmCfg& c, float*
     case 6: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 2>>(p, n, c, ws, s);
     case 7: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 2>>(p, n, c, ws, s);
     case 8: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 2>>(p, n, c, ws, s);
-    default: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, n, c, ws, s);
+    case 9: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, n, c, ws, s);
+    case 10: return launch_s<Mm<FMT, MT, 2, 2, 2, G, 1>>(p, n, c, ws, s);
+    case 11: return launch_s<Mm<FMT, MT, 2, 2, 4, G, 1>>(p, n, c, ws, s);
+    case 12: return launch_s<Mm<FMT, MT, 2, 1, 8, G, 1>>(p, n, c, ws, s);
+    case 13: return launch_s<Mm<FMT, MT, 2, 1, 4, G, 1>>(p, n, c, ws, s);
+    default: return launch_s<Mm<FMT, MT, 2, 4, 2, G, 1>>(p, n, c, ws, s);
   }
 }
 
