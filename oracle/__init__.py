@@ -10,8 +10,9 @@ C++ file, whose header states the formats, the readings of the pages and the
 passages they follow.  Arrays are numpy arrays in host memory:
 
 * ``qweight``: uint8 ``[N][K/2]`` (4-bit) or int8/uint8 ``[N][K]`` (8-bit);
-* ``scales``: float16 ``[N][K/group]`` (symmetric) or uint8 ``[N][K/256][8]``
-  superblock records (asymmetric); ``zeros``: ``None`` or uint8 records;
+* ``scales``: float16 ``[N][K/group]`` (symmetric), uint8 ``[N][K/256][8]``
+  superblock records (asymmetric) or one float32 (FP8, the matrix scale);
+  ``zeros``: ``None`` or uint8 records;
 * ``x``: float16 ``[M][K]``.
 """
 import ctypes
@@ -22,6 +23,7 @@ import numpy as np
 
 LAYOUT_SYM = 0
 LAYOUT_ASYM_SB = 1
+LAYOUT_FP8_TENSOR = 2
 RTOL = 1e-3  # per-output tolerance: |y - y_ref| <= RTOL * sum_k |x w|
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +44,8 @@ def _bind(L):
     """Declare the C signatures on a loaded oracle library."""
     L.rqo_half_to_double.argtypes = [ctypes.c_uint16]
     L.rqo_half_to_double.restype = ctypes.c_double
+    L.rqo_fp8_to_double.argtypes = [ctypes.c_uint8]
+    L.rqo_fp8_to_double.restype = ctypes.c_double
     L.rqo_code_at.argtypes = [_u8p, _i, _i, _i, _i, _i, _i]
     L.rqo_code_at.restype = _i
     L.rqo_unpack_codes.argtypes = [_u8p, _i, _i, _i, _i, _i8p]
@@ -113,6 +117,10 @@ def _scales_arg(scales):
 
 def half_to_double(bits: int) -> float:
     return lib().rqo_half_to_double(bits)
+
+
+def fp8_to_double(byte: int) -> float:
+    return lib().rqo_fp8_to_double(byte)
 
 
 def code_at(qweight, N, K, bits, layout, n, k) -> int:

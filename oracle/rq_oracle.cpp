@@ -20,6 +20,11 @@
  *   - 4-bit asymmetric codes in superblocks of 32-wide groups, each group
  *     with its own scale and shift: the projection format of the COMPRESSION
  *     preset (same article and section).
+ *   - 8-bit floating-point codes, FP8 E4M3 ("float8_e4m3fn"), one binary32
+ *     scale for the whole matrix: w = fp8 * scale (package page "RWKV-7 FP8
+ *     Quantized Inference", sections "Core Approach: Full FP8, No Residuals"
+ *     and "Quantization Principle"; the scale dtype is fp32 per the metadata
+ *     table of section "Quantization Metadata Format").
  *   - Weight matrices are stored [out][in]: the FFN key of a width-4096 model
  *     is 16384x4096 and the FFN value 4096x16384 (package page
  *     "RWKV-7 FP8 Quantized Inference", section "Operator Optimization
@@ -41,6 +46,11 @@
  *     value; the model card's accuracy paragraph reports that its kernel
  *     reproduces the offline dequantization bit for bit, so the dequantized
  *     weights have one right answer;
+ *   - FP8 E4M3 is the OCP encoding: exponent bias 7, 3 fraction bits,
+ *     subnormals, no infinities, S.1111.111 is NaN (max finite 448, the value
+ *     the page's per-tensor scale divides by).  The weight is the binary32
+ *     product fp8 * scale, rounded once (both factors are exact binary64s and
+ *     their product has at most 4 + 24 significant bits);
  *   - the matvec accumulates x*w in binary64, in k order, and also returns
  *     bound = sum_k |x*w|, against which results are judged:
  *     |y - y_ref| <= rtol * bound.
@@ -55,7 +65,7 @@
 #include <string.h>
 
 /* Layout and status values of the interface the oracle checks. */
-enum { LAYOUT_SYM = 0, LAYOUT_ASYM_SB = 1 };
+enum { LAYOUT_SYM = 0, LAYOUT_ASYM_SB = 1, LAYOUT_FP8_TENSOR = 2 };
 enum { OK = 0, BAD_ARG = 1 };
 
 static const int SUPERBLOCK = 256; /* k per asymmetric superblock  */
@@ -84,6 +94,28 @@ double rqo_half_to_double(uint16_t h) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* OCP FP8 E4M3 -> binary64, exact.                                          */
+/* 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; no infinities.     */
+/* Normal:    (-1)^s * (8 + f) * 2^(e - 10)                                  */
+/* Subnormal: (-1)^s * f * 2^-9                                             */
+/* e = 15 with f = 7 is NaN.                                                */
+/* ------------------------------------------------------------------------ */
+double rqo_fp8_to_double(uint8_t b) {
+    int s = (b >> 7) & 1;
+    int e = (b >> 3) & 0x0F;
+    int f = b & 0x07;
+    double v;
+    if (e == 15 && f == 7) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexp((double)f, -9);
+    } else {
+        v = ldexp((double)(8 + f), e - 10);
+    }
+    return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Code decode: the integer code q[n][k].                                    */
 /* ------------------------------------------------------------------------ */
 int rqo_code_at(const uint8_t* qweight, int N, int K, int bits, int layout,
@@ -106,12 +138,13 @@ int rqo_code_at(const uint8_t* qweight, int N, int K, int bits, int layout,
 static int valid_format(int bits, int group, int layout) {
     if (layout == LAYOUT_SYM) return (bits == 4 || bits == 8) && group > 0;
     if (layout == LAYOUT_ASYM_SB) return bits == 4 && group == SB_GROUP;
+    if (layout == LAYOUT_FP8_TENSOR) return bits == 8 && group == 0;
     return 0;
 }
 
 static int valid_shape(int N, int K, int bits, int group, int layout) {
     if (N < 1 || K < 1 || !valid_format(bits, group, layout)) return 0;
-    if (K % group != 0) return 0;
+    if (group > 0 && K % group != 0) return 0;
     if (bits == 4 && K % 2 != 0) return 0;
     if (layout == LAYOUT_ASYM_SB && K % SUPERBLOCK != 0) return 0;
     return 1;
@@ -123,6 +156,7 @@ int rqo_unpack_codes(const uint8_t* qweight, int N, int K, int bits, int layout,
     if (N < 1 || K < 1 || !(bits == 4 || bits == 8)) return BAD_ARG;
     if (bits == 4 && K % 2 != 0) return BAD_ARG;
     if (layout == LAYOUT_ASYM_SB && bits != 4) return BAD_ARG;
+    if (layout == LAYOUT_FP8_TENSOR) return BAD_ARG; /* codes are not integers */
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++)
             codes[(size_t)n * K + k] =
@@ -136,6 +170,7 @@ int rqo_pack_codes(const int8_t* codes, int N, int K, int bits, int layout,
     if (N < 1 || K < 1 || !(bits == 4 || bits == 8)) return BAD_ARG;
     if (bits == 4 && K % 2 != 0) return BAD_ARG;
     if (layout == LAYOUT_ASYM_SB && bits != 4) return BAD_ARG;
+    if (layout == LAYOUT_FP8_TENSOR) return BAD_ARG; /* codes are not integers */
     if (bits == 8) {
         for (size_t i = 0; i < (size_t)N * K; i++) qweight[i] = (uint8_t)codes[i];
         return OK;
@@ -186,10 +221,16 @@ int rqo_unpack_record(const uint8_t rec[8], uint16_t* base_bits, uint8_t sub[8])
 /* Scale s and shift t that apply to weight (n, k), as exact binary64 values. */
 /* SYM:  s = scales[n][k/group] (binary16), t = 0.                           */
 /* ASYM: b = k/256, j = (k%256)/32; s = d*sc_j, t = m*mn_j.                  */
+/* FP8:  s = scales[0] (binary32, the whole matrix), t = 0.                  */
 /* ------------------------------------------------------------------------ */
 static void scale_shift_at(const void* scales, const void* zeros, int K,
                            int group, int layout, int n, int k, double* s,
                            double* t) {
+    if (layout == LAYOUT_FP8_TENSOR) {
+        *s = (double)((const float*)scales)[0];
+        *t = 0.0;
+        return;
+    }
     if (layout == LAYOUT_SYM) {
         const uint16_t* sc = (const uint16_t*)scales;
         *s = rqo_half_to_double(sc[(size_t)n * (K / group) + k / group]);
@@ -211,14 +252,18 @@ static void scale_shift_at(const void* scales, const void* zeros, int K,
 
 /* w[n][k] as the binary32 nearest the exact value s*q - t (ties to even).
  * For every binary16 s, t and the code ranges here, s*q - t is an exact
- * binary64 (at most 50 significant bits), so one conversion rounds once. */
+ * binary64 (at most 50 significant bits), so one conversion rounds once.
+ * For FP8 codes q is the code's value and s the binary32 matrix scale
+ * (product: at most 28 significant bits, exact in binary64). */
 static float weight_at(const uint8_t* qweight, const void* scales,
                        const void* zeros, int N, int K, int bits, int group,
                        int layout, int n, int k) {
     double s, t;
     scale_shift_at(scales, zeros, K, group, layout, n, k, &s, &t);
-    int q = rqo_code_at(qweight, N, K, bits, layout, n, k);
-    double exact = s * (double)q - t;
+    double q = (layout == LAYOUT_FP8_TENSOR)
+                   ? rqo_fp8_to_double(qweight[(size_t)n * K + k])
+                   : (double)rqo_code_at(qweight, N, K, bits, layout, n, k);
+    double exact = s * q - t;
     return (float)exact;
 }
 

@@ -4,7 +4,9 @@
  * Every pointer is host memory owned by the caller.  Functions return 0 on
  * success and 1 on a bad argument.  Nothing here is used by the GPU library.
  * Layout values: 0 = symmetric, 1 = asymmetric superblock (groups of 32,
- * superblocks of 256).  Binary16 values are passed as their raw uint16 bits.
+ * superblocks of 256), 2 = FP8 E4M3 codes with one binary32 scale for the
+ * matrix (bits 8, group 0).  Binary16 values are passed as their raw uint16
+ * bits.
  */
 #ifndef RQ_ORACLE_H
 #define RQ_ORACLE_H
@@ -16,6 +18,7 @@ extern "C" {
 #endif
 
 double rqo_half_to_double(uint16_t h);
+double rqo_fp8_to_double(uint8_t b);
 int rqo_code_at(const uint8_t* qweight, int N, int K, int bits, int layout,
                 int n, int k);
 int rqo_unpack_codes(const uint8_t* qweight, int N, int K, int bits, int layout,

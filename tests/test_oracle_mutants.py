@@ -42,11 +42,11 @@ MUTANTS = {
         "int j = (k % SUPERBLOCK) / SB_GROUP;",
         "int j = (k % SUPERBLOCK) / 64;"),
     "asym_shift_dropped": (
-        "double exact = s * (double)q - t;",
-        "double exact = s * (double)q;"),
+        "double exact = s * q - t;",
+        "double exact = s * q;"),
     "asym_shift_sign": (
-        "double exact = s * (double)q - t;",
-        "double exact = s * (double)q + t;"),
+        "double exact = s * q - t;",
+        "double exact = s * q + t;"),
     "asym_scale_for_shift": (
         "*t = rqo_half_to_double(m_bits) * (double)mn[j];",
         "*t = rqo_half_to_double(m_bits) * (double)sc[j];"),
@@ -81,6 +81,21 @@ MUTANTS = {
     "check_relative_to_y": (
         "ok = (err <= rtol * bound[i]);",
         "ok = (err <= rtol * fabs(y_ref[i]) + rtol);"),
+    "fp8_exponent_bias": (
+        "v = ldexp((double)(8 + f), e - 10);",
+        "v = ldexp((double)(8 + f), e - 11);"),
+    "fp8_subnormal_as_normal": (
+        "v = ldexp((double)f, -9);",
+        "v = ldexp((double)(8 + f), -10);"),
+    "fp8_nan_as_number": (
+        "if (e == 15 && f == 7) {",
+        "if (e == 16) {"),
+    "fp8_sign_dropped": (
+        "int s = (b >> 7) & 1;",
+        "int s = 0;"),
+    "fp8_scale_ignored": (
+        "*s = (double)((const float*)scales)[0];",
+        "*s = 1.0;"),
     "check_zero_bound_lenient": (
         "ok = (yi == 0.0);",
         "ok = (fabs(yi) < 1e-20);"),

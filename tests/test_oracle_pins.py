@@ -417,3 +417,84 @@ def test_check_catches_bf16_rounded_activations():
     rounded = np.array([[7.0 * 1.0]], dtype=np.float32)
     assert O.check(exact, y_ref, bound)[0] == 0
     assert O.check(rounded, y_ref, bound)[0] == 1
+
+
+# ------------------------------------------------------------------- FP8 ---
+FP8 = O.LAYOUT_FP8_TENSOR
+
+
+def f32_bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def test_fp8_literals(lit):
+    for e in lit["fp8_e4m3"]:
+        v = O.fp8_to_double(hx(e["byte"]))
+        if e["value"] == "nan":
+            assert np.isnan(v), e
+        else:
+            assert v == float(e["value"]) and np.signbit(v) == e["value"].startswith("-"), e
+
+
+def test_fp8_every_code_matches_torch():
+    """All 256 bytes against torch's float8_e4m3fn decoding (an independent
+    implementation of the same OCP encoding)."""
+    import torch
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    got = np.array([O.fp8_to_double(b) for b in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got)) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_dequant_literal(lit):
+    for c in lit["dequant_fp8"]:
+        q = np.array([[hx(c["code"])] * 16], dtype=np.uint8)
+        s = np.array([hx(c["scale_bits"])], dtype=np.uint32).view(np.float32)
+        w = O.dequant(q, s, None, 1, 16, 8, 0, FP8)
+        assert np.all(f32_bits(w) == hx(c["w_bits"])), c
+
+
+def test_fp8_dequant_matches_the_page_recipe():
+    """Quantize with the page's per-tensor recipe in torch (scale = max|W|/448,
+    clamp, cast to float8_e4m3fn) and dequantize as it does (fp8 * scale in
+    binary32): the oracle agrees bit for bit."""
+    import torch
+    g = torch.Generator().manual_seed(8)
+    W = torch.randn(37, 96, generator=g) * torch.exp(2 * torch.randn(37, 1, generator=g))
+    scale = W.abs().max() / 448.0
+    q = (W / scale).clamp(-448, 448).to(torch.float8_e4m3fn)
+    ref = (q.to(torch.float32) * scale).numpy()
+    got = O.dequant(q.view(torch.uint8).numpy(), np.array([scale.item()], np.float32), None,
+                    37, 96, 8, 0, FP8)
+    assert np.array_equal(f32_bits(got), f32_bits(ref))
+
+
+def test_fp8_gemv_matches_dense_float64():
+    import torch
+    rng = np.random.default_rng(81)
+    N, K, M = 29, 160, 3
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    scale = np.array([0.0123], np.float32)
+    wv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    w = (wv * scale[0]).astype(np.float32)  # binary32 product, as the page dequantizes
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    y, b = O.gemv_ref(codes, scale, None, x, N, K, 8, 0, FP8)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(b, np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T,
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_rejects_groups_and_integer_views():
+    q = np.zeros((2, 32), dtype=np.uint8)
+    s = np.ones(1, np.float32)
+    with pytest.raises(ValueError):
+        O.dequant(q, s, None, 2, 32, 8, 16, FP8)
+    with pytest.raises(ValueError):
+        O.dequant(q, s, None, 2, 32, 4, 0, FP8)
+    with pytest.raises(ValueError):
+        O.unpack_codes(q, 2, 32, 8, FP8)
