@@ -21,7 +21,8 @@ import os
 import threading
 
 __all__ = [
-    "RQ_OK", "RQ_LAYOUT_SYM", "RQ_LAYOUT_ASYM_SB", "RQ_OUT_F32", "RQ_OUT_CODES_I8",
+    "RQ_OK", "RQ_LAYOUT_SYM", "RQ_LAYOUT_ASYM_SB", "RQ_LAYOUT_FP8_TENSOR", "RQ_OUT_F32",
+    "RQ_OUT_CODES_I8",
     "RQ_MAX_M", "RQ_MAX_BATCH", "RqError", "RqLibraryMissing", "rq_dequant", "rq_gemv",
     "rq_gemv_batched", "rq_gemm_smallm", "rq_status_string", "rq_version", "prepare",
     "lib", "LIB_PATH",
@@ -30,7 +31,7 @@ __all__ = [
 RQ_OK = 0
 RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED, RQ_ERR_ALIGN = 1, 2, 3, 4
 RQ_ERR_LAUNCH, RQ_ERR_ALIAS, RQ_ERR_DEVICE = 5, 6, 7
-RQ_LAYOUT_SYM, RQ_LAYOUT_ASYM_SB = 0, 1
+RQ_LAYOUT_SYM, RQ_LAYOUT_ASYM_SB, RQ_LAYOUT_FP8_TENSOR = 0, 1, 2
 RQ_OUT_F32, RQ_OUT_CODES_I8 = 0, 1
 RQ_MAX_M = 64
 RQ_MAX_BATCH = 64

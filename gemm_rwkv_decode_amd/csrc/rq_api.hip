@@ -41,6 +41,7 @@ const Tuning& tuning() {
 namespace {
 
 using rq::FMT_A4;
+using rq::FMT_F8;
 using rq::FMT_S4;
 using rq::FMT_S8;
 
@@ -51,6 +52,7 @@ int format_of(int layout, int bits, int group) {
   if (layout == RQ_LAYOUT_SYM && bits == 8 && (group == 16 || group == 32 || group == 64))
     return FMT_S8;
   if (layout == RQ_LAYOUT_ASYM_SB && bits == 4 && group == 32) return FMT_A4;
+  if (layout == RQ_LAYOUT_FP8_TENSOR && bits == 8 && group == 0) return FMT_F8;
   return -1;
 }
 
@@ -69,6 +71,7 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 size_t code_bytes(int N, int K, int bits) { return (size_t)N * K * bits / 8; }
 size_t scale_bytes(int N, int K, int group, int layout) {
+  if (layout == RQ_LAYOUT_FP8_TENSOR) return 4;  // one binary32
   return layout == RQ_LAYOUT_ASYM_SB ? (size_t)N * (K / 256) * 8
                                      : (size_t)N * (K / group) * 2;
 }
@@ -77,12 +80,14 @@ size_t scale_bytes(int N, int K, int group, int layout) {
 rq_status check_weights(const void* qweight, const void* scales, const void* zeros, int N,
                         int K, int bits, int group, int layout, int* fmt) {
   if (!qweight || !scales) return RQ_ERR_NULL;
-  if (layout != RQ_LAYOUT_SYM && layout != RQ_LAYOUT_ASYM_SB) return RQ_ERR_UNSUPPORTED;
+  if (layout != RQ_LAYOUT_SYM && layout != RQ_LAYOUT_ASYM_SB && layout != RQ_LAYOUT_FP8_TENSOR)
+    return RQ_ERR_UNSUPPORTED;
   const int f = format_of(layout, bits, group);
   if (f < 0) return RQ_ERR_UNSUPPORTED;
   if (layout == RQ_LAYOUT_ASYM_SB && !zeros) return RQ_ERR_NULL;
-  if (layout == RQ_LAYOUT_SYM && zeros) return RQ_ERR_UNSUPPORTED;
-  if (N < 1 || K < group || K % group != 0) return RQ_ERR_SHAPE;
+  if (layout != RQ_LAYOUT_ASYM_SB && zeros) return RQ_ERR_UNSUPPORTED;
+  if (N < 1 || K < 1) return RQ_ERR_SHAPE;
+  if (group > 0 && (K < group || K % group != 0)) return RQ_ERR_SHAPE;
   if (((size_t)K * bits / 8) % 16 != 0) return RQ_ERR_SHAPE;
   // kernels index within an operand with 32-bit offsets
   if (code_bytes(N, K, bits) >= ((size_t)1 << 31)) return RQ_ERR_SHAPE;
@@ -200,6 +205,7 @@ rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
   rq_status st = check_weights(qweight, scales, zeros, N, K, bits, group, layout, &fmt);
   if (st != RQ_OK) return st;
   if (out_kind != RQ_OUT_F32 && out_kind != RQ_OUT_CODES_I8) return RQ_ERR_UNSUPPORTED;
+  if (out_kind == RQ_OUT_CODES_I8 && fmt == FMT_F8) return RQ_ERR_UNSUPPORTED;
   if (!aligned16(out)) return RQ_ERR_ALIGN;
   const size_t ob = (size_t)N * K * (out_kind == RQ_OUT_F32 ? 4 : 1);
   st = check_output(out, ob, qweight, scales, zeros, nullptr, N, K, bits, group, layout, 0);

@@ -17,7 +17,7 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 
 // Format ids of the kernels (a function of layout and bits).
-enum Fmt { FMT_S4 = 0, FMT_S8 = 1, FMT_A4 = 2 };
+enum Fmt { FMT_S4 = 0, FMT_S8 = 1, FMT_A4 = 2, FMT_F8 = 3 };
 
 constexpr int SUPERBLOCK = 256;  // k per asymmetric superblock
 constexpr int SB_GROUP = 32;     // k per asymmetric group
@@ -25,7 +25,7 @@ constexpr int SB_GROUP = 32;     // k per asymmetric group
 // Codes in one 16-byte chunk of a row.
 template <int FMT>
 struct Chunk {
-  static constexpr int codes = (FMT == FMT_S8) ? 16 : 32;
+  static constexpr int codes = (FMT == FMT_S8 || FMT == FMT_F8) ? 16 : 32;
 };
 
 __device__ __forceinline__ h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
@@ -108,6 +108,14 @@ __device__ __forceinline__ void unpack8(u32 d, h2 q[2]) {
   const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   q[0] = as_h2(t0) + bias;
   q[1] = as_h2(t1) + bias;
+}
+
+// One dword of FP8 E4M3 codes, k = 0..3 in bytes 0..3.  Returns (q0,q1)
+// (q2,q3) in binary16, exactly: every E4M3 value, subnormals included, is a
+// binary16 (the conversion's scale operand is 1).
+__device__ __forceinline__ void unpack_fp8(u32 d, h2 q[2]) {
+  q[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false);
+  q[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true);
 }
 
 // Activation pairs matching unpack4: from the 8 halves x0..x7 held in four

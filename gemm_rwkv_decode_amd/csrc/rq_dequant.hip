@@ -8,7 +8,8 @@
 // Arithmetic: symmetric w = s * q is exact in binary32 (at most 11 + 8
 // significant bits).  Asymmetric s_j = d * sc_j and t_j = m * mn_j are exact
 // (at most 17 bits) and w = fma(s_j, q, -t_j) rounds the exact s_j*q - t_j
-// once, to nearest even -- the correctly rounded value of the formula.
+// once, to nearest even -- the correctly rounded value of the formula.  FP8:
+// the code converts exactly to binary32 and w = code * scale rounds once.
 #include "rq_common.h"
 #include "rq_internal.h"
 
@@ -24,6 +25,19 @@ k_dequant(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
        o += (long long)gridDim.x * blockDim.x) {
     const int n = (int)(o / oct_per_row);
     const int k0 = (int)(o % oct_per_row) * 8;
+    if constexpr (FMT == FMT_F8) {
+      const u32x2 d = *reinterpret_cast<const u32x2*>(qw + (size_t)n * K + k0);
+      const float s = *static_cast<const float*>(scales);
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(d.x, false);
+      const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(d.x, true);
+      const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(d.y, false);
+      const f2 e = __builtin_amdgcn_cvt_pk_f32_fp8(d.y, true);
+      f4* dst = reinterpret_cast<f4*>(static_cast<float*>(out) + (size_t)n * K + k0);
+      dst[0] = f4{a.x * s, a.y * s, b.x * s, b.y * s};
+      dst[1] = f4{c.x * s, c.y * s, e.x * s, e.y * s};
+      continue;
+    }
     int q[8];
     if (FMT == FMT_S8) {
       const u32x2 d = *reinterpret_cast<const u32x2*>(qw + (size_t)n * K + k0);
@@ -88,6 +102,8 @@ hipError_t launch_dequant(const void* qweight, const void* scales, const void* z
     if (codes) RQ_DQ(FMT_S4, true); else RQ_DQ(FMT_S4, false);
   } else if (fmt == FMT_S8) {
     if (codes) RQ_DQ(FMT_S8, true); else RQ_DQ(FMT_S8, false);
+  } else if (fmt == FMT_F8) {
+    RQ_DQ(FMT_F8, false);  // codes output is rejected by the caller
   } else {
     if (codes) RQ_DQ(FMT_A4, true); else RQ_DQ(FMT_A4, false);
   }

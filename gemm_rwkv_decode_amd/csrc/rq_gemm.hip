@@ -667,6 +667,7 @@ size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
 }
 
 bool gemm_supports(int fmt, int M, int K, int group) {
+  if (fmt == FMT_F8) return false;  // FP8 weights run on the vector-unit kernel
   const int mt = (M + 15) / 16;
   for (int p = 0; p < kNumPlans; p++)
     if (plan_ok(fmt, mt, group, K, p)) return true;

@@ -28,7 +28,7 @@ namespace rq {
 template <int FMT>
 struct RowBytes {
   static __device__ __forceinline__ size_t of(int K) {
-    return (FMT == FMT_S8) ? (size_t)K : (size_t)K / 2;
+    return (FMT == FMT_S8 || FMT == FMT_F8) ? (size_t)K : (size_t)K / 2;
   }
 };
 
@@ -43,7 +43,7 @@ __device__ __forceinline__ void load_x_chunk(const _Float16* __restrict__ xrow, 
 #pragma unroll
   for (int v = 0; v < CPC / 8; v++) {
     const u32x4 w = src[v];
-    if (FMT == FMT_S8) {
+    if (FMT == FMT_S8 || FMT == FMT_F8) {
       dst[4 * v + 0] = as_h2(w.x);
       dst[4 * v + 1] = as_h2(w.y);
       dst[4 * v + 2] = as_h2(w.z);
@@ -64,11 +64,12 @@ template <int FMT>
 __device__ __forceinline__ float chunk_dot(const u32x4 code, const h2* xp) {
   float a = 0.0f;
   const u32 d[4] = {code.x, code.y, code.z, code.w};
-  if (FMT == FMT_S8) {
+  if (FMT == FMT_S8 || FMT == FMT_F8) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       h2 q[2];
-      unpack8(d[i], q);
+      if (FMT == FMT_F8) unpack_fp8(d[i], q);
+      else unpack8(d[i], q);
       a = __builtin_amdgcn_fdot2(q[0], xp[2 * i + 0], a, false);
       a = __builtin_amdgcn_fdot2(q[1], xp[2 * i + 1], a, false);
     }
@@ -104,7 +105,10 @@ __device__ __forceinline__ void load_pass(PassData<FMT, CPL>& pd,
 #pragma unroll
   for (int c = 0; c < CPL; c++) {
     const int k0 = kc[c] * CPC;
-    if (FMT == FMT_A4) {
+    if (FMT == FMT_F8) {  // one scale for the matrix, applied to the row sum
+      pd.s[c] = 1.0f;
+      pd.t[c] = 0.0f;
+    } else if (FMT == FMT_A4) {
       const size_t rec = (size_t)n * (K / SUPERBLOCK) + k0 / SUPERBLOCK;
       const int j = (k0 % SUPERBLOCK) / SB_GROUP;
       pd.s[c] = record_value(reinterpret_cast<const u32x2*>(scales)[rec], j);
@@ -189,13 +193,16 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
     }
   }
 
+  // FP8: one binary32 scale for the matrix, applied to each finished sum
+  const float mscale = (FMT == FMT_F8) ? *reinterpret_cast<const float*>(scales) : 1.0f;
+
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int SK = blockDim.x >> 6;
   const int rs = lane / LPR;
   const int li = lane % LPR;
   const int row0 = ((int)blockIdx.x - block0) * RB;
-  const u32 row_bytes = (FMT == FMT_S8) ? (u32)K : (u32)K / 2;
+  const u32 row_bytes = (FMT == FMT_S8 || FMT == FMT_F8) ? (u32)K : (u32)K / 2;
 
   int kc[CPL];
 #pragma unroll
@@ -220,7 +227,11 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
       const u32 k0 = (u32)kc[c] * CPC;
-      if constexpr (FMT == FMT_A4) {
+      if constexpr (FMT == FMT_F8) {  // the matrix scale is applied to the row sum
+        (void)k0;
+        sr[p][c].s = u32x2{0, 0};
+        sr[p][c].z = u32x2{0, 0};
+      } else if constexpr (FMT == FMT_A4) {
         const u32 o = srow + (k0 / SUPERBLOCK) * 8u;
         sr[p][c].s = *reinterpret_cast<const u32x2*>(scales + o);
         sr[p][c].z = *reinterpret_cast<const u32x2*>(zeros + o);
@@ -265,7 +276,7 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 #pragma unroll
       for (int v = 0; v < XV; v++) {
         const u32x4 wv = xraw[m][c][v];
-        if constexpr (FMT == FMT_S8) {
+        if constexpr (FMT == FMT_S8 || FMT == FMT_F8) {
           xr[m][c][4 * v + 0] = as_h2(wv.x);
           xr[m][c][4 * v + 1] = as_h2(wv.y);
           xr[m][c][4 * v + 2] = as_h2(wv.z);
@@ -289,7 +300,9 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
       float sc, t = 0.0f;
-      if constexpr (FMT == FMT_A4) {
+      if constexpr (FMT == FMT_F8) {
+        sc = 1.0f;
+      } else if constexpr (FMT == FMT_A4) {
         const int j = ((kc[c] * CPC) % SUPERBLOCK) / SB_GROUP;
         sc = record_value(sr[p][c].s, j);
         t = record_value(sr[p][c].z, j);
@@ -309,7 +322,7 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
       const float v = group_sum<LPR>(acc[m]);
       if (li == 0) {
         if (SK == 1) {
-          if (m < Mrows && n < N) y[(u32)m * (u32)N + (u32)n] = v;
+          if (m < Mrows && n < N) y[(u32)m * (u32)N + (u32)n] = v * mscale;
         } else {
           part[(w * RB + p * RPW + rs) * MT + m] = v;
         }
@@ -324,7 +337,7 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
       float v = 0.0f;
       for (int ww = 0; ww < SK; ww++) v += part[(ww * RB + r) * MT + m];
       const int n = row0 + r;
-      if (n < N) y[(u32)m * (u32)N + (u32)n] = v;
+      if (n < N) y[(u32)m * (u32)N + (u32)n] = v * mscale;
     }
   }
 }
@@ -345,6 +358,7 @@ k_gemv_generic(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
   const int li = lane % LPR;
   const int nn = min(n, N - 1);
   const int chunks = (int)(RowBytes<FMT>::of(K) / 16);
+  const float mscale = (FMT == FMT_F8) ? *static_cast<const float*>(scales) : 1.0f;
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; m++) acc[m] = 0.0f;
@@ -367,7 +381,7 @@ k_gemv_generic(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
 #pragma unroll
   for (int m = 0; m < MT; m++) {
     const float v = group_sum<LPR>(acc[m]);
-    if (li == 0 && m < Mrows && n < N) y[(size_t)m * N + n] = v;
+    if (li == 0 && m < Mrows && n < N) y[(size_t)m * N + n] = v * mscale;
   }
 }
 
@@ -390,7 +404,7 @@ GemvCfg choose_gemv(int fmt, int M, int N, int K) {
   GemvCfg c{};
   // activation rows per launch: the smallest of 1, 2, 4, 8 covering M (or 8)
   c.mt = M <= 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));
-  const int chunks = (fmt == FMT_S8) ? K / 16 : K / 32;
+  const int chunks = (fmt == FMT_S8 || fmt == FMT_F8) ? K / 16 : K / 32;
   // measured on MI355X (width-4096 shapes, weights cold in HBM): one 16-byte chunk per lane and four
   // rows per lane beat wider per-lane slices, whose extra registers cost
   // occupancy
@@ -452,11 +466,11 @@ struct Launch {
 
 template <int FMT, int LPR, int CPL, int MT, int NP>
 static void launch_t(const Launch& L, hipStream_t s) {
-  const int chunks = (FMT == FMT_S8) ? L.K / 16 : L.K / 32;
+  const int chunks = (FMT == FMT_S8 || FMT == FMT_F8) ? L.K / 16 : L.K / 32;
   const int sk = chunks / (LPR * CPL);
   constexpr int rb = (64 / LPR) * NP;
   const size_t lds = (sk > 1) ? (size_t)sk * rb * MT * sizeof(float) : 0;
-  const int gsh = ilog2(L.group);
+  const int gsh = ilog2(L.group > 0 ? L.group : 1);
   // code bytes per row : scale bytes per row = 2^ssh
   //   int4 sym: (K/2)/(2K/G) = G/4; int8 sym: K/(2K/G) = G/2; asym: (K/2)/(K/32) = 16
   const int ssh = (FMT == FMT_A4) ? 4 : (FMT == FMT_S8 ? gsh - 1 : gsh - 2);
@@ -553,6 +567,7 @@ hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c
       }
       if (p[0]->fmt == FMT_S4) launch_fmt<FMT_S4>(L, c, s);
       else if (p[0]->fmt == FMT_S8) launch_fmt<FMT_S8>(L, c, s);
+      else if (p[0]->fmt == FMT_F8) launch_fmt<FMT_F8>(L, c, s);
       else launch_fmt<FMT_A4>(L, c, s);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -39,6 +39,7 @@ import torch
 
 LAYOUT_SYM = 0
 LAYOUT_ASYM_SB = 1
+LAYOUT_FP8_TENSOR = 2
 SUPERBLOCK = 256
 
 
@@ -58,6 +59,8 @@ class Fmt:
     def weight_bytes(self, N: int, K: int) -> int:
         """Packed code bytes plus scale (and zero) bytes of an N x K matrix."""
         codes = N * K * self.bits // 8
+        if self.layout == LAYOUT_FP8_TENSOR:
+            return codes + 4  # one binary32 scale
         if self.layout == LAYOUT_ASYM_SB:
             return codes + 2 * 8 * N * (K // SUPERBLOCK)
         return codes + 2 * N * (K // self.group)
@@ -66,7 +69,10 @@ class Fmt:
 INT4_G64 = Fmt("int4g64", 4, 64, LAYOUT_SYM)
 INT8_G16 = Fmt("int8g16", 8, 16, LAYOUT_SYM)
 ASYM4_G32 = Fmt("asym4g32", 4, 32, LAYOUT_ASYM_SB)
-FORMATS = {f.tag: f for f in (INT4_G64, INT8_G16, ASYM4_G32)}
+# FP8 E4M3 weights with one binary32 scale per matrix (package page "RWKV-7
+# FP8 Quantized Inference", section "Quantization Principle")
+FP8_E4M3 = Fmt("fp8e4m3", 8, 0, LAYOUT_FP8_TENSOR)
+FORMATS = {f.tag: f for f in (INT4_G64, INT8_G16, ASYM4_G32, FP8_E4M3)}
 
 MAT_NAMES = ("att.receptance", "att.key", "att.value", "att.output",
              "ffn.key", "ffn.value", "head")
@@ -220,6 +226,8 @@ def gen_matrix(wkey: str, layer: int, mat: int, N: int, K: int, fmt: Fmt,
     """Seeded packed weights for one matrix.  Returns ``Packed`` (and the
     unpacked int8 codes when ``keep_codes``)."""
     dev = torch.device(device)
+    if fmt.layout == LAYOUT_FP8_TENSOR:
+        return gen_fp8_matrix(wkey, layer, mat, N, K, fmt, dev, keep_codes)
     gc = generator(seed_for(wkey, layer, mat, "codes", fmt.tag, 0), dev)
     codes = gen_codes(N, K, fmt, gc, dev)
     gs = generator(seed_for(wkey, layer, mat, "scales", fmt.tag, 0), dev)
@@ -240,6 +248,32 @@ def gen_matrix(wkey: str, layer: int, mat: int, N: int, K: int, fmt: Fmt,
         return p, codes
     del codes
     return p
+
+
+def gen_fp8_matrix(wkey: str, layer: int, mat: int, N: int, K: int, fmt: Fmt, dev,
+                   keep_codes: bool = False):
+    """FP8 weights by the page's per-tensor recipe: real-valued weights (normal,
+    with a log-normal magnitude per row), scale = max|W| / 448, codes =
+    float8_e4m3fn(clamp(W / scale, -448, 448)).  The weights are drawn on the
+    CPU in row blocks (seeded per block), so the bytes do not depend on the
+    device; the cast is torch's."""
+    codes = torch.empty((N, K), dtype=torch.uint8)
+    mags = []
+    rows_per = max(1, (1 << 24) // K)
+    blocks = []
+    for b, r0 in enumerate(range(0, N, rows_per)):
+        g = torch.Generator().manual_seed(seed_for(wkey, layer, mat, f"weights{b}", fmt.tag, 0))
+        r1 = min(N, r0 + rows_per)
+        W = torch.randn((r1 - r0, K), generator=g)
+        W *= torch.exp(0.5 * torch.randn((r1 - r0, 1), generator=g))
+        blocks.append((r0, r1, W))
+        mags.append(W.abs().max())
+    scale = (torch.stack(mags).max() / 448.0).reshape(1).to(torch.float32)
+    for r0, r1, W in blocks:
+        codes[r0:r1] = (W / scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    del blocks
+    p = Packed(codes.to(dev), scale.to(dev), None, N, K, fmt)
+    return (p, codes) if keep_codes else p
 
 
 def massive_channels(cfg: Config, layer: int, mat: int, K: int) -> Tuple[List[int], float]:
@@ -280,7 +314,9 @@ def rows_of(p: Packed, rows) -> Packed:
     """A Packed holding only the listed rows (used to hand row samples to a
     checker); rows are independent, so the sub-matrix is a valid problem."""
     idx = torch.as_tensor(rows, dtype=torch.long, device=p.qweight.device)
+    scales = p.scales if p.fmt.layout == LAYOUT_FP8_TENSOR else \
+        p.scales.index_select(0, idx).contiguous()  # FP8: one scale for the matrix
     return Packed(p.qweight.index_select(0, idx).contiguous(),
-                  p.scales.index_select(0, idx).contiguous(),
+                  scales,
                   None if p.zeros is None else p.zeros.index_select(0, idx).contiguous(),
                   len(rows), p.K, p.fmt)

@@ -7,7 +7,7 @@
  * material; rows are [out][in], as the FFN key (16384x4096) and FFN value
  * (4096x16384) of a width-4096 RWKV-7 model are listed on the package page
  * "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization Details").
- * Three storage formats are supported:
+ * Four storage formats are supported:
  *
  *   RQ_LAYOUT_SYM, bits = 4, group in {32, 64, 128}
  *       The 4-bit symmetric format with one scale per group of consecutive
@@ -32,6 +32,15 @@
  *       6j..6j+5).  zeros: records of the same shape holding m and the
  *       sub-mins mn_j.  With j = (k mod 256)/32:
  *       w = (d * sc_j) * q - (m * mn_j).
+ *   RQ_LAYOUT_FP8_TENSOR, bits = 8, group = 0
+ *       FP8 E4M3 weights with one binary32 scale for the whole matrix, the
+ *       format of the package page "RWKV-7 FP8 Quantized Inference" (sections
+ *       "Core Approach: Full FP8, No Residuals" and "Quantization Principle";
+ *       the scale is fp32 per section "Quantization Metadata Format"), used
+ *       here as weight-only quantization (binary16 activations).  qweight:
+ *       uint8 [N][K], each byte an OCP E4M3 value (bias 7, 3 fraction bits,
+ *       subnormals, no infinities, S.1111.111 = NaN, largest finite 448).
+ *       scales: one float (binary32).  zeros: NULL.  w = fp8 * scale.
  *
  * Every dequantized weight is the binary32 value nearest (ties to even) the
  * exact value of its formula; for these formats that value is the same however
@@ -70,7 +79,7 @@ typedef enum {
                                split-K workspace could not be obtained           */
 } rq_status;
 
-typedef enum { RQ_LAYOUT_SYM = 0, RQ_LAYOUT_ASYM_SB = 1 } rq_layout;
+typedef enum { RQ_LAYOUT_SYM = 0, RQ_LAYOUT_ASYM_SB = 1, RQ_LAYOUT_FP8_TENSOR = 2 } rq_layout;
 
 typedef enum {
     RQ_OUT_F32 = 0,     /* binary32 weights [N][K]                               */
@@ -100,10 +109,12 @@ typedef struct {
  * Defines the dequantization of the formats above (the model card's accuracy
  * paragraph reports that the serving kernel reproduces the offline dequant bit
  * for bit; this call is that offline dequant).
- *   out: RQ_OUT_F32 -> float [N][K]; RQ_OUT_CODES_I8 -> int8 [N][K].
- *   zeros: NULL for RQ_LAYOUT_SYM, required for RQ_LAYOUT_ASYM_SB.
- * Shape rules: N >= 1, K >= group, K % group == 0, K*bits/8 % 16 == 0, and for
- * the asymmetric layout K % 256 == 0.
+ *   out: RQ_OUT_F32 -> float [N][K]; RQ_OUT_CODES_I8 -> int8 [N][K] (not for
+ *   RQ_LAYOUT_FP8_TENSOR, whose codes are not integers: RQ_ERR_UNSUPPORTED).
+ *   zeros: NULL for RQ_LAYOUT_SYM and RQ_LAYOUT_FP8_TENSOR, required for
+ *   RQ_LAYOUT_ASYM_SB.
+ * Shape rules: N >= 1, K >= 1, K % group == 0 (group > 0), K*bits/8 % 16 == 0,
+ * and for the asymmetric layout K % 256 == 0.
  */
 rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
                      void* out, int N, int K, int bits, int group, int layout,

@@ -46,7 +46,7 @@ def test_exports_every_declared_function(L):
 def test_status_values_match_header():
     for n in ["RQ_OK", "RQ_ERR_NULL", "RQ_ERR_SHAPE", "RQ_ERR_UNSUPPORTED", "RQ_ERR_ALIGN",
               "RQ_ERR_LAUNCH", "RQ_ERR_ALIAS", "RQ_ERR_DEVICE", "RQ_LAYOUT_SYM",
-              "RQ_LAYOUT_ASYM_SB", "RQ_OUT_F32", "RQ_OUT_CODES_I8"]:
+              "RQ_LAYOUT_ASYM_SB", "RQ_LAYOUT_FP8_TENSOR", "RQ_OUT_F32", "RQ_OUT_CODES_I8"]:
         assert getattr(rq, n) == header_enum(n), n
     assert rq.RQ_MAX_M == int(re.search(r"#define RQ_MAX_M (\d+)", open(HEADER).read()).group(1))
 
@@ -86,7 +86,12 @@ CASES = [
     ("int4 group 48", dict(group=48), rq.RQ_ERR_UNSUPPORTED),
     ("int4 group 16", dict(group=16), rq.RQ_ERR_UNSUPPORTED),
     ("int8 group 128", dict(bits=8, group=128), rq.RQ_ERR_UNSUPPORTED),
-    ("unknown layout", dict(layout=2), rq.RQ_ERR_UNSUPPORTED),
+    ("unknown layout", dict(layout=3), rq.RQ_ERR_UNSUPPORTED),
+    ("fp8 with a group", dict(layout=2, bits=8, group=64), rq.RQ_ERR_UNSUPPORTED),
+    ("fp8 4-bit", dict(layout=2, bits=4, group=0), rq.RQ_ERR_UNSUPPORTED),
+    ("fp8 with zeros", dict(layout=2, bits=8, group=0, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
+    ("fp8 row not whole 16 bytes", dict(layout=2, bits=8, group=0, K=264), rq.RQ_ERR_SHAPE),
+    ("sym group 0", dict(group=0), rq.RQ_ERR_UNSUPPORTED),
     ("asym group 64", dict(layout=1, group=64, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
     ("asym 8-bit", dict(layout=1, group=32, bits=8, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
     ("K not a multiple of group", dict(K=96), rq.RQ_ERR_SHAPE),
@@ -123,6 +128,7 @@ def test_product_rejects(L, fn, what, kw, status):
 DQ_ONLY = [
     ("null out", dict(out=None), rq.RQ_ERR_NULL),
     ("unknown output kind", dict(kind=2), rq.RQ_ERR_UNSUPPORTED),
+    ("fp8 codes output", dict(layout=2, bits=8, group=0, kind=1), rq.RQ_ERR_UNSUPPORTED),
     ("misaligned out", dict(out=A + (3 << 30) + 8), rq.RQ_ERR_ALIGN),
     ("out overlaps codes", dict(out=A + 16), rq.RQ_ERR_ALIAS),
 ]
