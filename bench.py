@@ -76,6 +76,7 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers of the step the CPU oracle times")
     ap.add_argument("--layers", type=int, default=None, help="(testing) fewer layers")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 W8A16 step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 64 MiB with rq_probe_copy (the reference kernel "
                          "for scaling the memory-traffic counters)")
@@ -237,6 +238,64 @@ def main():
                         "pct_of_hbm_peak": round(100 * step_bytes(M) / sec / 1e9 / HBM_PEAK_GBS,
                                                  2)}
 
+    # ---- FP8 E4M3 per-tensor weights (W8A16), M = 1 --------------------------
+    # The page's FP8 model shape: width 4096, 32 layers.  Eight distinct weight
+    # sets are cycled over the 32 layers: 1.07 GB between reuses of a set,
+    # four times the 256 MB MALL, so every byte still comes from HBM.
+    fp8 = None
+    if not args.no_fp8:
+        log("FP8 step")
+        f8 = S.FP8_E4M3
+        f8_layers, f8_sets = 32, 8
+        lay = [(mi, N, K) for (l, mi, N, K) in cfg.matrices(with_head=False) if l == 0]
+        W8s = {(s8, mi): S.gen_matrix("rwkv7-7.2b-fp8", s8, mi, N, K, f8, device=dev)
+               for s8 in range(f8_sets) for (mi, N, K) in lay}
+        mats8 = [(l, mi, N, K) for l in range(f8_layers) for (mi, N, K) in lay]
+        W8 = [W8s[(l % f8_sets, mi)] for (l, mi, N, K) in mats8]
+        X8 = [S.gen_x(cfg, l, mi, 1, K, device=dev) for (l, mi, N, K) in mats8]
+        Y8 = [torch.empty((1, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats8]
+        calls8 = ST.step_calls(mats8, W8, X8, Y8, "layer")
+        for _ in range(args.warmup):
+            for c in calls8:
+                c()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            for c in calls8:
+                c()
+        torch.cuda.synchronize()
+        sec8 = (time.perf_counter() - t) / args.steps
+        b8 = sum(f8.weight_bytes(N, K) + 2 * K + 4 * N for (_, _, N, K) in mats8)
+        shapes8 = {}
+        for (mi, N, K) in lay[3:]:  # output projection, FFN key, FFN value
+            cs = [ST.step_calls([m], [W8[i]], [X8[i]], [Y8[i]], "matrix")[0]
+                  for i, m in enumerate(mats8) if m[1] == mi]
+            for c in cs[:4]:
+                c()
+            best = 1e9
+            for _ in range(3):
+                a = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                a.record(torch.cuda.current_stream())
+                for c in cs:
+                    c()
+                e.record(torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                best = min(best, a.elapsed_time(e) * 1e-3 / len(cs))
+            mb = f8.weight_bytes(N, K) + 2 * K + 4 * N
+            shapes8[f"{N}x{K}"] = {"us_per_launch": round(best * 1e6, 3),
+                                   "GBps": round(mb / best / 1e9, 1)}
+        fp8 = {"workload": "RWKV-7 7.2B-shaped FP8 E4M3 per-tensor W8A16 decode weight "
+                           "stream: 32 layers x (4 x 4096x4096, 16384x4096, 4096x16384), "
+                           "8 distinct weight sets cycled (1.07 GB between reuses)",
+               "entry": "rq_gemv / rq_gemv_batched (vector units)", "M": 1,
+               "launch_calls": len(calls8), "bytes_per_step": b8,
+               "ms_per_step": round(sec8 * 1e3, 4), "GBps": round(b8 / sec8 / 1e9, 2),
+               "pct_of_hbm_peak": round(100 * b8 / sec8 / 1e9 / HBM_PEAK_GBS, 2),
+               "per_shape": shapes8}
+        del W8s, W8, X8, Y8, calls8
+        torch.cuda.empty_cache()
+
     # ---- CPU oracle on a bounded sample of the same step --------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -282,6 +341,7 @@ def main():
                    "bytes_per_step": step_bytes(1)},
         "m32": mfma["32"],
         "mfma_m": mfma,
+        "fp8_w8a16_m1": fp8,
         "per_shape_m1": per_kernel,
         "roofline": {"bound": "hbm", "kernel": f"int4 g64 GEMV {dom_name}, M=1",
                      "achieved": dom_v["GBps"], "peak": HBM_PEAK_GBS,
