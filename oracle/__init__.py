@@ -9,7 +9,9 @@ This module is argument marshalling over ``librq_oracle.so`` (built from
 C++ file, whose header states the formats, the readings of the pages and the
 passages they follow.  Arrays are numpy arrays in host memory:
 
-* ``qweight``: uint8 ``[N][K/2]`` (4-bit) or int8/uint8 ``[N][K]`` (8-bit);
+* ``qweight``: uint8 ``[N][K/2]`` (4-bit), int8/uint8 ``[N][K]`` (8-bit), or
+  for 5- and 6-bit codes the flat ``N*K*bits/8`` bytes of the two planes (the
+  ``[N][K/2]`` low nibbles, then the ``[N][K*(bits-4)/8]`` high bits);
 * ``scales``: float16 ``[N][K/group]`` (symmetric), uint8 ``[N][K/256][8]``
   superblock records (asymmetric) or one float32 (FP8, the matrix scale);
   ``zeros``: ``None`` or uint8 records;
@@ -140,7 +142,10 @@ def unpack_codes(qweight, N, K, bits, layout):
 def pack_codes(codes, bits, layout):
     c = np.ascontiguousarray(codes, dtype=np.int8)
     N, K = c.shape
-    out = np.empty((N, K if bits == 8 else K // 2), dtype=np.uint8)
+    if bits in (5, 6):
+        out = np.empty(N * K * bits // 8, dtype=np.uint8)
+    else:
+        out = np.empty((N, K if bits == 8 else K // 2), dtype=np.uint8)
     rc = lib().rqo_pack_codes(_ptr(c, _i8p), N, K, bits, layout, _ptr(out, _u8p))
     if rc:
         raise ValueError("rqo_pack_codes: bad argument or code out of range")

@@ -20,6 +20,8 @@
  *   - 4-bit asymmetric codes in superblocks of 32-wide groups, each group
  *     with its own scale and shift: the projection format of the COMPRESSION
  *     preset (same article and section).
+ *   - 5- and 6-bit codes: the same presets keep the FFN in 6 bits (REDUCTION)
+ *     and the FFN key and the head in 5 bits (COMPRESSION) (same section).
  *   - 8-bit floating-point codes, FP8 E4M3 ("float8_e4m3fn"), one binary32
  *     scale for the whole matrix: w = fp8 * scale (package page "RWKV-7 FP8
  *     Quantized Inference", sections "Core Approach: Full FP8, No Residuals"
@@ -42,6 +44,12 @@
  *     a 48-bit little-endian field (bytes 2-7, sc_j at bits 6j..6j+5).  The
  *     zero record has the same shape with the superblock min m and sub-mins
  *     mn_j.  The weight is w = (d*sc_j)*q - (m*mn_j);
+ *   - 5- and 6-bit codes use the asymmetric superblock layout above (the
+ *     layout the pages attach to their sub-8-bit codes), unsigned
+ *     0..2^bits-1.  qweight holds two planes: the low 4 bits of every code
+ *     exactly as the 4-bit layout stores them ([N][K/2]), then the high
+ *     bits, [N][K*(bits-4)/8] bytes, in the order given at hi_bit_position
+ *     below (the pages give only the widths; this order is ours);
  *   - dequantized weights are binary32, correctly rounded from the exact
  *     value; the model card's accuracy paragraph reports that its kernel
  *     reproduces the offline dequantization bit for bit, so the dequantized
@@ -116,11 +124,53 @@ double rqo_fp8_to_double(uint8_t b) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* High bits of 5- and 6-bit codes.  A row's high plane is a run of 32-code  */
+/* chunks (chunk c holds codes 32c..32c+31) of 4 bytes (5-bit) or 8 bytes    */
+/* (6-bit), read as little-endian 32-bit words.  In a chunk, code 8i + j     */
+/* (i = 0..3, j = 0..7) has                                                  */
+/*   base = (j >= 4 ? 16 : 0) + (j even ? 4 : 8),   g = (j mod 4) / 2;       */
+/*   5-bit: bit 4 of the code in word 0 at bit base + (g == 0 ? i - 4 : i + 4); */
+/*   6-bit: bits 4 and 5 in word i/2 at bits base + s and base + 1 + s, with */
+/*          s = -4, -2, 4, 6 for (i mod 2, g) = (0,0), (0,1), (1,0), (1,1).  */
+/* Returns the bit position of code bit 4 + b; *word gets the word index.    */
+/* ------------------------------------------------------------------------ */
+static int hi_bit_position(int bits, int c, int b, int* word) {
+    int i = c / 8, j = c % 8, g = (j % 4) / 2;
+    int base = (j >= 4 ? 16 : 0) + (j % 2 == 0 ? 4 : 8);
+    if (bits == 5) {
+        *word = 0;
+        return base + (g == 0 ? i - 4 : i + 4);
+    }
+    static const int s6[2][2] = {{-4, -2}, {4, 6}};
+    *word = i / 2;
+    return base + b + s6[i % 2][g];
+}
+
+/* Byte offset of row n's high plane within qweight. */
+static size_t hi_plane_row(int N, int K, int bits, int n) {
+    return (size_t)N * (K / 2) + (size_t)n * ((size_t)K * (bits - 4) / 8);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Code decode: the integer code q[n][k].                                    */
 /* ------------------------------------------------------------------------ */
 int rqo_code_at(const uint8_t* qweight, int N, int K, int bits, int layout,
                 int n, int k) {
-    (void)N;
+    if (bits == 5 || bits == 6) {
+        /* low 4 bits as in the 4-bit layout, high bits from the second plane */
+        int q = rqo_code_at(qweight, N, K, 4, LAYOUT_ASYM_SB, n, k);
+        const uint8_t* chunk = qweight + hi_plane_row(N, K, bits, n) +
+                               (size_t)(k / 32) * 4 * (bits - 4);
+        for (int b = 0; b < bits - 4; b++) {
+            int word;
+            int pos = hi_bit_position(bits, k % 32, b, &word);
+            const uint8_t* w = chunk + 4 * word;
+            uint32_t v = (uint32_t)w[0] | ((uint32_t)w[1] << 8) |
+                         ((uint32_t)w[2] << 16) | ((uint32_t)w[3] << 24);
+            q |= (int)((v >> pos) & 1u) << (4 + b);
+        }
+        return q;
+    }
     if (bits == 8) {
         /* one int8 two's-complement code per byte */
         return (int)(int8_t)qweight[(size_t)n * K + k];
@@ -137,7 +187,8 @@ int rqo_code_at(const uint8_t* qweight, int N, int K, int bits, int layout,
 
 static int valid_format(int bits, int group, int layout) {
     if (layout == LAYOUT_SYM) return (bits == 4 || bits == 8) && group > 0;
-    if (layout == LAYOUT_ASYM_SB) return bits == 4 && group == SB_GROUP;
+    if (layout == LAYOUT_ASYM_SB)
+        return (bits == 4 || bits == 5 || bits == 6) && group == SB_GROUP;
     if (layout == LAYOUT_FP8_TENSOR) return bits == 8 && group == 0;
     return 0;
 }
@@ -153,9 +204,10 @@ static int valid_shape(int N, int K, int bits, int group, int layout) {
 int rqo_unpack_codes(const uint8_t* qweight, int N, int K, int bits, int layout,
                      int8_t* codes) {
     if (!qweight || !codes) return BAD_ARG;
-    if (N < 1 || K < 1 || !(bits == 4 || bits == 8)) return BAD_ARG;
+    if (N < 1 || K < 1 || !(bits == 4 || bits == 5 || bits == 6 || bits == 8)) return BAD_ARG;
     if (bits == 4 && K % 2 != 0) return BAD_ARG;
-    if (layout == LAYOUT_ASYM_SB && bits != 4) return BAD_ARG;
+    if ((bits == 5 || bits == 6) && (layout != LAYOUT_ASYM_SB || K % 32 != 0)) return BAD_ARG;
+    if (layout == LAYOUT_ASYM_SB && bits == 8) return BAD_ARG;
     if (layout == LAYOUT_FP8_TENSOR) return BAD_ARG; /* codes are not integers */
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++)
@@ -167,10 +219,32 @@ int rqo_unpack_codes(const uint8_t* qweight, int N, int K, int bits, int layout,
 int rqo_pack_codes(const int8_t* codes, int N, int K, int bits, int layout,
                    uint8_t* qweight) {
     if (!qweight || !codes) return BAD_ARG;
-    if (N < 1 || K < 1 || !(bits == 4 || bits == 8)) return BAD_ARG;
+    if (N < 1 || K < 1 || !(bits == 4 || bits == 5 || bits == 6 || bits == 8)) return BAD_ARG;
     if (bits == 4 && K % 2 != 0) return BAD_ARG;
-    if (layout == LAYOUT_ASYM_SB && bits != 4) return BAD_ARG;
+    if ((bits == 5 || bits == 6) && (layout != LAYOUT_ASYM_SB || K % 32 != 0)) return BAD_ARG;
+    if (layout == LAYOUT_ASYM_SB && bits == 8) return BAD_ARG;
     if (layout == LAYOUT_FP8_TENSOR) return BAD_ARG; /* codes are not integers */
+    if (bits == 5 || bits == 6) {
+        /* low nibbles as in the 4-bit layout, then the high plane */
+        memset(qweight, 0, (size_t)N * K * bits / 8);
+        for (int n = 0; n < N; n++) {
+            for (int k = 0; k < K; k++) {
+                int c = codes[(size_t)n * K + k];
+                if (c < 0 || c >= (1 << bits)) return BAD_ARG;
+                qweight[(size_t)n * (K / 2) + k / 2] |=
+                    (uint8_t)((c & 0x0F) << (4 * (k % 2)));
+                uint8_t* chunk = qweight + hi_plane_row(N, K, bits, n) +
+                                 (size_t)(k / 32) * 4 * (bits - 4);
+                for (int b = 0; b < bits - 4; b++) {
+                    int word;
+                    int pos = hi_bit_position(bits, k % 32, b, &word);
+                    if ((c >> (4 + b)) & 1)
+                        chunk[4 * word + pos / 8] |= (uint8_t)(1u << (pos % 8));
+                }
+            }
+        }
+        return OK;
+    }
     if (bits == 8) {
         for (size_t i = 0; i < (size_t)N * K; i++) qweight[i] = (uint8_t)codes[i];
         return OK;

@@ -96,6 +96,21 @@ MUTANTS = {
     "fp8_scale_ignored": (
         "*s = (double)((const float*)scales)[0];",
         "*s = 1.0;"),
+    "hi5_shift": (
+        "return base + (g == 0 ? i - 4 : i + 4);",
+        "return base + (g == 0 ? i - 4 : i + 3);"),
+    "hi_plane_offset": (
+        "return (size_t)N * (K / 2) + (size_t)n * ((size_t)K * (bits - 4) / 8);",
+        "return (size_t)n * ((size_t)K * (bits - 4) / 8);"),
+    "hi6_bit_order": (
+        "return base + b + s6[i % 2][g];",
+        "return base + (1 - b) + s6[i % 2][g];"),
+    "hi6_word": (
+        "*word = i / 2;",
+        "*word = i % 2;"),
+    "hi_bits_shift": (
+        "q |= (int)((v >> pos) & 1u) << (4 + b);",
+        "q |= (int)((v >> pos) & 1u) << (3 + b);"),
     "check_zero_bound_lenient": (
         "ok = (yi == 0.0);",
         "ok = (fabs(yi) < 1e-20);"),

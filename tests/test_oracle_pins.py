@@ -498,3 +498,100 @@ def test_fp8_rejects_groups_and_integer_views():
         O.dequant(q, s, None, 2, 32, 4, 0, FP8)
     with pytest.raises(ValueError):
         O.unpack_codes(q, 2, 32, 8, FP8)
+
+
+# ------------------------------------------------------- 5- and 6-bit codes ---
+def test_hi_bit_literals(lit):
+    K = 256
+    for c in lit["asym_hi_bits"]:
+        bits = c["bits"]
+        codes = np.zeros((1, K), dtype=np.int8)
+        codes[0, c["k"]] = c["value"]
+        q = O.pack_codes(codes, bits, ASYM)
+        assert q.size == K * bits // 8
+        want = np.zeros_like(q)
+        if c["nibble"] is not None:
+            want[c["nibble"][0]] = hx(c["nibble"][1])
+        want[K // 2 + c["plane"][0]] = hx(c["plane"][1])
+        assert np.array_equal(q, want), c
+        assert O.code_at(q, 1, K, bits, ASYM, 0, c["k"]) == c["value"], c
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_hi_bits_fill_the_plane_once(bits):
+    """Each high bit of each of the 32 codes of a chunk has a bit of its own,
+    and together they fill the chunk's 4 (5-bit) or 8 (6-bit) bytes."""
+    K = 32 * 8
+    seen = set()
+    for k in range(32):
+        for b in range(bits - 4):
+            codes = np.zeros((1, K), dtype=np.int8)
+            codes[0, 64 + k] = 1 << (4 + b)  # chunk 2
+            q = O.pack_codes(codes, bits, ASYM)
+            plane = np.unpackbits(q[K // 2:], bitorder="little")
+            on = np.flatnonzero(plane)
+            assert on.size == 1
+            seen.add(int(on[0]))
+    nb = 32 * (bits - 4)
+    assert seen == set(range(2 * nb, 3 * nb))
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_hi_bits_round_trip_every_value(bits):
+    rng = np.random.default_rng(bits)
+    N, K = 5, 512
+    codes = rng.integers(0, 1 << bits, size=(N, K)).astype(np.int8)
+    codes[0, :32] = np.arange(32) % (1 << bits)
+    codes[1, :64] = np.arange(64) % (1 << bits)
+    q = O.pack_codes(codes, bits, ASYM)
+    assert np.array_equal(O.unpack_codes(q, N, K, bits, ASYM), codes)
+    with pytest.raises(ValueError):
+        bad = codes.copy()
+        bad[2, 7] = 1 << bits
+        O.pack_codes(bad, bits, ASYM)
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_dequant_hi_bits_exact_rational(bits):
+    """w = RN32((d*sc_j)*q - m*mn_j) with q up to 2^bits - 1, against Python's
+    exact rationals."""
+    rng = np.random.default_rng(40 + bits)
+    N, K = 3, 512
+    codes = rng.integers(0, 1 << bits, size=(N, K)).astype(np.int8)
+    q = O.pack_codes(codes, bits, ASYM)
+    B = K // 256
+    d = rng.uniform(1e-4, 2e-3, size=(N, B)).astype(np.float16)
+    m = rng.uniform(1e-4, 2e-3, size=(N, B)).astype(np.float16)
+    sc = rng.integers(0, 64, size=(N, B, 8))
+    mn = rng.integers(0, 64, size=(N, B, 8))
+    srec = np.stack([[O.pack_record(half_bits(d[n, b]), sc[n, b]) for b in range(B)]
+                     for n in range(N)])
+    zrec = np.stack([[O.pack_record(half_bits(m[n, b]), mn[n, b]) for b in range(B)]
+                     for n in range(N)])
+    w = O.dequant(q, srec, zrec, N, K, bits, 32, ASYM)
+    for n in range(N):
+        for k in range(0, K, 7):
+            b, j = k // 256, (k % 256) // 32
+            exact = (Fraction(float(d[n, b])) * int(sc[n, b, j]) * int(codes[n, k])
+                     - Fraction(float(m[n, b])) * int(mn[n, b, j]))
+            # the exact value is a binary64 here; numpy rounds it once to binary32
+            assert Fraction(float(exact)) == exact
+            assert w[n, k] == np.float32(float(exact)), (n, k)
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_gemv_hi_bits_integer_exact(bits):
+    """Power-of-two records and small integer x make every product and sum
+    exact: the oracle equals an int64 matmul of the codes."""
+    rng = np.random.default_rng(60 + bits)
+    N, M, K = 7, 2, 256
+    codes = rng.integers(0, 1 << bits, size=(N, K)).astype(np.int8)
+    q = O.pack_codes(codes, bits, ASYM)
+    one = O.pack_record(half_bits(1.0), np.ones(8, np.uint8))
+    zero = O.pack_record(half_bits(0.0), np.zeros(8, np.uint8))
+    srec = np.stack([[one]] * N)
+    zrec = np.stack([[zero]] * N)
+    x = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    y, _ = O.gemv_ref(q, srec, zrec, x, N, K, bits, 32, ASYM)
+    ref = x.astype(np.int64) @ codes.astype(np.int64).T
+    assert np.array_equal(y, ref.astype(np.float64))
