@@ -41,6 +41,8 @@ const Tuning& tuning() {
 namespace {
 
 using rq::FMT_A4;
+using rq::FMT_A5;
+using rq::FMT_A6;
 using rq::FMT_F8;
 using rq::FMT_S4;
 using rq::FMT_S8;
@@ -52,6 +54,8 @@ int format_of(int layout, int bits, int group) {
   if (layout == RQ_LAYOUT_SYM && bits == 8 && (group == 16 || group == 32 || group == 64))
     return FMT_S8;
   if (layout == RQ_LAYOUT_ASYM_SB && bits == 4 && group == 32) return FMT_A4;
+  if (layout == RQ_LAYOUT_ASYM_SB && bits == 5 && group == 32) return FMT_A5;
+  if (layout == RQ_LAYOUT_ASYM_SB && bits == 6 && group == 32) return FMT_A6;
   if (layout == RQ_LAYOUT_FP8_TENSOR && bits == 8 && group == 0) return FMT_F8;
   return -1;
 }

@@ -17,7 +17,12 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 
 // Format ids of the kernels (a function of layout and bits).
-enum Fmt { FMT_S4 = 0, FMT_S8 = 1, FMT_A4 = 2, FMT_F8 = 3 };
+enum Fmt { FMT_S4 = 0, FMT_S8 = 1, FMT_A4 = 2, FMT_F8 = 3, FMT_A5 = 4, FMT_A6 = 5 };
+
+// Asymmetric superblock layouts: 4-, 5- and 6-bit unsigned codes.
+constexpr bool is_asym(int fmt) { return fmt == FMT_A4 || fmt == FMT_A5 || fmt == FMT_A6; }
+// Bits of a code above its low nibble (they live in the high-bit plane).
+constexpr int hi_bits(int fmt) { return fmt == FMT_A5 ? 1 : (fmt == FMT_A6 ? 2 : 0); }
 
 constexpr int SUPERBLOCK = 256;  // k per asymmetric superblock
 constexpr int SB_GROUP = 32;     // k per asymmetric group
@@ -71,6 +76,53 @@ __device__ __forceinline__ void unpack4(u32 d, h2 q[4]) {
   const _Float16 b1 = SIGNED ? (_Float16)-72.0f : (_Float16)-64.0f;
   const h2 bias0 = {b0, b0};
   const h2 bias1 = {b1, b1};
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  q[0] = as_h2(t0) + bias0;
+  q[1] = __builtin_elementwise_fma(as_h2(t1), sixteenth, bias1);
+  q[2] = as_h2(t2) + bias0;
+  q[3] = __builtin_elementwise_fma(as_h2(t3), sixteenth, bias1);
+}
+
+// 5- and 6-bit codes.  The low nibbles are stored as 4-bit codes; the high
+// bits of each 32-code chunk (one 16-byte chunk of nibbles) are one dword
+// (5-bit) or two (6-bit) of the high-bit plane, in an order chosen so that a
+// rotation puts the bits of nibble dword i (codes 8i..8i+7) next to the
+// nibbles where unpack4 places them: for the pairs (q0,q4) (q1,q5) at bits
+// 4 and 20 (8 and 24) of hlo, for (q2,q6) (q3,q7) likewise in hhi.  In the
+// stored plane, code 8i + j has base = (j >= 4 ? 16 : 0) + (j even ? 4 : 8)
+// and g = (j mod 4) / 2; 5-bit: bit base + (g == 0 ? i - 4 : i + 4) of the
+// chunk's dword; 6-bit: bits base + s and base + 1 + s of dword i / 2, with
+// s = -4, -2, 4, 6 for (i mod 2, g) = (0,0), (0,1), (1,0), (1,1).
+__device__ __forceinline__ u32 rotr(u32 x, int s) { return __builtin_amdgcn_alignbit(x, x, s); }
+
+template <int HB>
+__device__ __forceinline__ void hi_words(const u32* w, int i, u32* hlo, u32* hhi) {
+  if constexpr (HB == 1) {
+    *hlo = rotr(w[0], (i + 28) & 31);  // shift i - 4
+    *hhi = rotr(w[0], i + 4);
+  } else {
+    const u32 p = w[i >> 1];
+    *hlo = rotr(p, (i & 1) ? 4 : 28);  // -4 or 4
+    *hhi = rotr(p, (i & 1) ? 6 : 30);  // -2 or 6
+  }
+}
+
+// One dword of nibbles of unsigned 5-/6-bit codes with their high bits in
+// hlo/hhi (hi_words).  Pairs as unpack4: (q0,q4) (q1,q5) (q2,q6) (q3,q7).  The
+// high bits join the nibble inside the binary16 mantissa: 1024 + q, or
+// 1024 + 16 q for the nibbles held in bits 4-7, both exact for q < 64.
+template <int HB>
+__device__ __forceinline__ void unpack4h(u32 d, u32 hlo, u32 hhi, h2 q[4]) {
+  const u32 lo = 0x000F000Fu, hi = 0x00F000F0u, key = 0x64006400u;
+  const u32 m0 = HB == 1 ? 0x00100010u : 0x00300030u;
+  const u32 m1 = HB == 1 ? 0x01000100u : 0x03000300u;
+  const u32 d2 = d >> 8;
+  const u32 t0 = ((d & lo) | key) | (hlo & m0);
+  const u32 t1 = ((d & hi) | key) | (hlo & m1);
+  const u32 t2 = ((d2 & lo) | key) | (hhi & m0);
+  const u32 t3 = ((d2 & hi) | key) | (hhi & m1);
+  const h2 bias0 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const h2 bias1 = {(_Float16)-64.0f, (_Float16)-64.0f};
   const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   q[0] = as_h2(t0) + bias0;
   q[1] = __builtin_elementwise_fma(as_h2(t1), sixteenth, bias1);

@@ -53,6 +53,24 @@ k_dequant(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
         const int nib = (int)((d >> (4 * i)) & 0xF);
         q[i] = (FMT == FMT_S4) ? ((nib ^ 8) - 8) : nib;
       }
+      if constexpr (hi_bits(FMT) > 0) {
+        // this octet is nibble dword i of its 32-code chunk; the chunk's high
+        // bits are 1 (5-bit) or 2 (6-bit) dwords of the plane after the nibbles
+        constexpr int HB = hi_bits(FMT);
+        const int ci = (k0 % 32) / 8;
+        const u32* hp = reinterpret_cast<const u32*>(
+            qw + (size_t)N * (K / 2) + (size_t)n * (K / 8 * HB) + (size_t)(k0 / 32) * 4 * HB);
+        const u32 w = hp[HB == 1 ? 0 : ci / 2];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const int g = (j % 4) / 2;
+          const int base = (j >= 4 ? 16 : 0) + (j % 2 == 0 ? 4 : 8);
+          int pos;
+          if (HB == 1) pos = base + (g == 0 ? ci - 4 : ci + 4);
+          else pos = base + ((ci % 2 == 0) ? (g == 0 ? -4 : -2) : (g == 0 ? 4 : 6));
+          q[j] |= (int)((w >> pos) & (HB == 1 ? 1u : 3u)) << 4;
+        }
+      }
     }
     if (CODES) {
       u32x2 v;
@@ -64,7 +82,7 @@ k_dequant(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
       continue;
     }
     float w[8];
-    if (FMT == FMT_A4) {
+    if (is_asym(FMT)) {
       const size_t rec = (size_t)n * (K / SUPERBLOCK) + k0 / SUPERBLOCK;
       const int j = (k0 % SUPERBLOCK) / SB_GROUP;
       const u32x2 sr = reinterpret_cast<const u32x2*>(scales)[rec];
@@ -104,6 +122,10 @@ hipError_t launch_dequant(const void* qweight, const void* scales, const void* z
     if (codes) RQ_DQ(FMT_S8, true); else RQ_DQ(FMT_S8, false);
   } else if (fmt == FMT_F8) {
     RQ_DQ(FMT_F8, false);  // codes output is rejected by the caller
+  } else if (fmt == FMT_A5) {
+    if (codes) RQ_DQ(FMT_A5, true); else RQ_DQ(FMT_A5, false);
+  } else if (fmt == FMT_A6) {
+    if (codes) RQ_DQ(FMT_A6, true); else RQ_DQ(FMT_A6, false);
   } else {
     if (codes) RQ_DQ(FMT_A4, true); else RQ_DQ(FMT_A4, false);
   }

@@ -667,7 +667,8 @@ size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
 }
 
 bool gemm_supports(int fmt, int M, int K, int group) {
-  if (fmt == FMT_F8) return false;  // FP8 weights run on the vector-unit kernel
+  // FP8 and 5-/6-bit codes run on the vector-unit kernel
+  if (fmt == FMT_F8 || fmt == FMT_A5 || fmt == FMT_A6) return false;
   const int mt = (M + 15) / 16;
   for (int p = 0; p < kNumPlans; p++)
     if (plan_ok(fmt, mt, group, K, p)) return true;

@@ -51,7 +51,7 @@ __device__ __forceinline__ void load_x_chunk(const _Float16* __restrict__ xrow, 
     } else {
       pair_x4(w.x, w.y, w.z, w.w, &dst[4 * v]);
     }
-    if (FMT == FMT_A4) {
+    if (is_asym(FMT)) {
       s += half_lo(w.x) + half_hi(w.x) + half_lo(w.y) + half_hi(w.y) +
            half_lo(w.z) + half_hi(w.z) + half_lo(w.w) + half_hi(w.w);
     }
@@ -59,9 +59,11 @@ __device__ __forceinline__ void load_x_chunk(const _Float16* __restrict__ xrow, 
   *xsum = s;
 }
 
-// sum_k q[k] * x[k] over one 16-byte chunk of codes, binary32.
+// sum_k q[k] * x[k] over one 16-byte chunk of codes, binary32.  hw: the
+// chunk's high-bit words (5- and 6-bit codes only).
 template <int FMT>
-__device__ __forceinline__ float chunk_dot(const u32x4 code, const h2* xp) {
+__device__ __forceinline__ float chunk_dot(const u32x4 code, const h2* xp,
+                                           const u32* hw = nullptr) {
   float a = 0.0f;
   const u32 d[4] = {code.x, code.y, code.z, code.w};
   if (FMT == FMT_S8 || FMT == FMT_F8) {
@@ -77,7 +79,13 @@ __device__ __forceinline__ float chunk_dot(const u32x4 code, const h2* xp) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       h2 q[4];
-      unpack4<FMT == FMT_S4>(d[i], q);
+      if constexpr (hi_bits(FMT) > 0) {
+        u32 hlo, hhi;
+        hi_words<hi_bits(FMT)>(hw, i, &hlo, &hhi);
+        unpack4h<hi_bits(FMT)>(d[i], hlo, hhi, q);
+      } else {
+        unpack4<FMT == FMT_S4>(d[i], q);
+      }
 #pragma unroll
       for (int j = 0; j < 4; j++) a = __builtin_amdgcn_fdot2(q[j], xp[4 * i + j], a, false);
     }
@@ -85,9 +93,18 @@ __device__ __forceinline__ float chunk_dot(const u32x4 code, const h2* xp) {
   return a;
 }
 
+// Byte offset of the high-bit words of chunk kc of row n (5- and 6-bit codes):
+// the plane follows the N x K/2 nibbles; a row holds K*HB/8 bytes, a chunk 4*HB.
+template <int FMT>
+__device__ __forceinline__ u32 hi_offset(int N, int K, u32 n, int kc) {
+  constexpr int HB = hi_bits(FMT);
+  return (u32)N * (u32)(K / 2) + n * (u32)(K / 8 * HB) + (u32)kc * (4u * HB);
+}
+
 template <int FMT, int CPL>
 struct PassData {
   u32x4 code[CPL];
+  u32 hw[CPL][2];  // high-bit words (5- and 6-bit codes)
   float s[CPL];   // scale (sym) or d*sc_j (asym)
   float t[CPL];   // m*mn_j (asym)
 };
@@ -96,19 +113,27 @@ template <int FMT, int CPL>
 __device__ __forceinline__ void load_pass(PassData<FMT, CPL>& pd,
                                           const uint8_t* __restrict__ qw,
                                           const void* __restrict__ scales,
-                                          const void* __restrict__ zeros, int n, int K,
-                                          int group, const int* kc) {
+                                          const void* __restrict__ zeros, int n, int N,
+                                          int K, int group, const int* kc) {
   constexpr int CPC = Chunk<FMT>::codes;
   const uint8_t* row = qw + (size_t)n * RowBytes<FMT>::of(K);
 #pragma unroll
   for (int c = 0; c < CPL; c++) pd.code[c] = load_stream16(row + (size_t)kc[c] * 16);
+  if constexpr (hi_bits(FMT) > 0) {
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      const uint8_t* hp = qw + hi_offset<FMT>(N, K, (u32)n, kc[c]);
+      pd.hw[c][0] = *reinterpret_cast<const u32*>(hp);
+      pd.hw[c][1] = hi_bits(FMT) == 2 ? reinterpret_cast<const u32*>(hp)[1] : 0u;
+    }
+  }
 #pragma unroll
   for (int c = 0; c < CPL; c++) {
     const int k0 = kc[c] * CPC;
     if (FMT == FMT_F8) {  // one scale for the matrix, applied to the row sum
       pd.s[c] = 1.0f;
       pd.t[c] = 0.0f;
-    } else if (FMT == FMT_A4) {
+    } else if (is_asym(FMT)) {
       const size_t rec = (size_t)n * (K / SUPERBLOCK) + k0 / SUPERBLOCK;
       const int j = (k0 % SUPERBLOCK) / SB_GROUP;
       pd.s[c] = record_value(reinterpret_cast<const u32x2*>(scales)[rec], j);
@@ -208,16 +233,36 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 #pragma unroll
   for (int c = 0; c < CPL; c++) kc[c] = w * (LPR * CPL) + c * LPR + li;
 
-  u32 roff[NP];  // code offset of each visited row
+  u32 rowi[NP], roff[NP];  // each visited row and its code offset
 #pragma unroll
-  for (int p = 0; p < NP; p++) roff[p] = (u32)min(row0 + p * RPW + rs, N - 1) * row_bytes;
+  for (int p = 0; p < NP; p++) {
+    rowi[p] = (u32)min(row0 + p * RPW + rs, N - 1);
+    roff[p] = rowi[p] * row_bytes;
+  }
 
-  // 1. codes of every row this lane visits
+  // 1. codes of every row this lane visits (5-/6-bit: and their high bits)
   u32x4 code[NP][CPL];
 #pragma unroll
   for (int p = 0; p < NP; p++)
 #pragma unroll
     for (int c = 0; c < CPL; c++) code[p][c] = load_stream16(qw + (roff[p] + kc[c] * 16u));
+  u32 hw[NP][CPL][2];
+  if constexpr (hi_bits(FMT) > 0) {
+#pragma unroll
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        const uint8_t* hp = qw + hi_offset<FMT>(N, K, rowi[p], kc[c]);
+        if constexpr (hi_bits(FMT) == 1) {
+          hw[p][c][0] = load_stream4(hp);
+          hw[p][c][1] = 0u;
+        } else {
+          const u32x2 v = load_stream8(hp);
+          hw[p][c][0] = v.x;
+          hw[p][c][1] = v.y;
+        }
+      }
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep the code loads ahead of everything else
   // 2. their scale material
   ScaleRaw<FMT> sr[NP][CPL];
@@ -231,7 +276,7 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
         (void)k0;
         sr[p][c].s = u32x2{0, 0};
         sr[p][c].z = u32x2{0, 0};
-      } else if constexpr (FMT == FMT_A4) {
+      } else if constexpr (is_asym(FMT)) {
         const u32 o = srow + (k0 / SUPERBLOCK) * 8u;
         sr[p][c].s = *reinterpret_cast<const u32x2*>(scales + o);
         sr[p][c].z = *reinterpret_cast<const u32x2*>(zeros + o);
@@ -284,7 +329,7 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
         } else {
           pair_x4(wv.x, wv.y, wv.z, wv.w, &xr[m][c][4 * v]);
         }
-        if constexpr (FMT == FMT_A4)
+        if constexpr (is_asym(FMT))
           sum += half_lo(wv.x) + half_hi(wv.x) + half_lo(wv.y) + half_hi(wv.y) +
                  half_lo(wv.z) + half_hi(wv.z) + half_lo(wv.w) + half_hi(wv.w);
       }
@@ -302,7 +347,7 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
       float sc, t = 0.0f;
       if constexpr (FMT == FMT_F8) {
         sc = 1.0f;
-      } else if constexpr (FMT == FMT_A4) {
+      } else if constexpr (is_asym(FMT)) {
         const int j = ((kc[c] * CPC) % SUPERBLOCK) / SB_GROUP;
         sc = record_value(sr[p][c].s, j);
         t = record_value(sr[p][c].z, j);
@@ -311,9 +356,9 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
       }
 #pragma unroll
       for (int m = 0; m < MT; m++) {
-        const float d = chunk_dot<FMT>(code[p][c], xr[m][c]);
+        const float d = chunk_dot<FMT>(code[p][c], xr[m][c], hw[p][c]);
         acc[m] = __builtin_fmaf(d, sc, acc[m]);
-        if (FMT == FMT_A4) acc[m] = __builtin_fmaf(-t, xs[m][c], acc[m]);
+        if (is_asym(FMT)) acc[m] = __builtin_fmaf(-t, xs[m][c], acc[m]);
       }
     }
     const int n = row0 + p * RPW + rs;
@@ -365,16 +410,16 @@ k_gemv_generic(const uint8_t* __restrict__ qw, const void* __restrict__ scales,
   for (int c = li; c < chunks; c += LPR) {
     int kc[1] = {c};
     PassData<FMT, 1> pd;
-    load_pass<FMT, 1>(pd, qw, scales, zeros, nn, K, group, kc);
+    load_pass<FMT, 1>(pd, qw, scales, zeros, nn, N, K, group, kc);
 #pragma unroll
     for (int m = 0; m < MT; m++) {
       if (m < Mrows) {
         h2 xp[XP];
         float xs;
         load_x_chunk<FMT>(x + (size_t)m * K, c * CPC, xp, &xs);
-        const float d = chunk_dot<FMT>(pd.code[0], xp);
+        const float d = chunk_dot<FMT>(pd.code[0], xp, pd.hw[0]);
         acc[m] = __builtin_fmaf(d, pd.s[0], acc[m]);
-        if (FMT == FMT_A4) acc[m] = __builtin_fmaf(-pd.t[0], xs, acc[m]);
+        if (is_asym(FMT)) acc[m] = __builtin_fmaf(-pd.t[0], xs, acc[m]);
       }
     }
   }
@@ -473,7 +518,7 @@ static void launch_t(const Launch& L, hipStream_t s) {
   const int gsh = ilog2(L.group > 0 ? L.group : 1);
   // code bytes per row : scale bytes per row = 2^ssh
   //   int4 sym: (K/2)/(2K/G) = G/4; int8 sym: K/(2K/G) = G/2; asym: (K/2)/(K/32) = 16
-  const int ssh = (FMT == FMT_A4) ? 4 : (FMT == FMT_S8 ? gsh - 1 : gsh - 2);
+  const int ssh = is_asym(FMT) ? 4 : (FMT == FMT_S8 ? gsh - 1 : gsh - 2);
   auto fill = [&](GemvEntry* e, int* blocks) {
     int b = 0;
     for (int i = 0; i < L.count; i++) {
@@ -568,6 +613,8 @@ hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c
       if (p[0]->fmt == FMT_S4) launch_fmt<FMT_S4>(L, c, s);
       else if (p[0]->fmt == FMT_S8) launch_fmt<FMT_S8>(L, c, s);
       else if (p[0]->fmt == FMT_F8) launch_fmt<FMT_F8>(L, c, s);
+      else if (p[0]->fmt == FMT_A5) launch_fmt<FMT_A5>(L, c, s);
+      else if (p[0]->fmt == FMT_A6) launch_fmt<FMT_A6>(L, c, s);
       else launch_fmt<FMT_A4>(L, c, s);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

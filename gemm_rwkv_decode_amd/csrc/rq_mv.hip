@@ -314,7 +314,8 @@ static int mv_ck(int fmt, int group) {
 
 bool mv_supports(int fmt, int M, int K, int group) {
   if (M < 1 || M > 4) return false;
-  if (fmt == FMT_F8) return false;  // FP8 weights run on the vector-unit kernel
+  // FP8 and 5-/6-bit codes run on the vector-unit kernel
+  if (fmt == FMT_F8 || fmt == FMT_A5 || fmt == FMT_A6) return false;
   const int ck = mv_ck(fmt, group);
   if (K % ck != 0 || K / ck < MV_WAVES) return false;
   const int me = M <= 1 ? 1 : (M <= 2 ? 2 : 4);

@@ -53,7 +53,7 @@ class Fmt:
     def code_range(self) -> Tuple[int, int]:
         """Inclusive range of the codes the generators emit."""
         if self.layout == LAYOUT_ASYM_SB:
-            return 0, 15
+            return 0, (1 << self.bits) - 1
         return (-7, 7) if self.bits == 4 else (-127, 127)
 
     def weight_bytes(self, N: int, K: int) -> int:
@@ -72,7 +72,12 @@ ASYM4_G32 = Fmt("asym4g32", 4, 32, LAYOUT_ASYM_SB)
 # FP8 E4M3 weights with one binary32 scale per matrix (package page "RWKV-7
 # FP8 Quantized Inference", section "Quantization Principle")
 FP8_E4M3 = Fmt("fp8e4m3", 8, 0, LAYOUT_FP8_TENSOR)
-FORMATS = {f.tag: f for f in (INT4_G64, INT8_G16, ASYM4_G32, FP8_E4M3)}
+# 5- and 6-bit codes in the asymmetric superblock layout (news article
+# "rwkv-quant: ...", section "Two presets and six sizes": FFN key and head in
+# 5 bits, FFN in 6 bits)
+ASYM5_G32 = Fmt("asym5g32", 5, 32, LAYOUT_ASYM_SB)
+ASYM6_G32 = Fmt("asym6g32", 6, 32, LAYOUT_ASYM_SB)
+FORMATS = {f.tag: f for f in (INT4_G64, INT8_G16, ASYM4_G32, FP8_E4M3, ASYM5_G32, ASYM6_G32)}
 
 MAT_NAMES = ("att.receptance", "att.key", "att.value", "att.output",
              "ffn.key", "ffn.value", "head")
@@ -165,6 +170,40 @@ def pack_nibbles(codes: torch.Tensor) -> torch.Tensor:
     return (lo | (hi << 4)).to(torch.uint8).contiguous()
 
 
+# high-bit placement of 5-/6-bit codes: shift of a (nibble dword i, g) group
+_HI5 = lambda i, g: i - 4 if g == 0 else i + 4  # noqa: E731
+_HI6 = ((-4, -2), (4, 6))
+
+
+def pack_hi_planes(codes: torch.Tensor, bits: int) -> torch.Tensor:
+    """Unsigned codes [N][K] (0..2^bits-1, bits 5 or 6) -> flat uint8: the low
+    nibbles as the 4-bit layout stores them ([N][K/2]), then the high-bit
+    plane: per row, per 32-code chunk, 1 (5-bit) or 2 (6-bit) little-endian
+    dwords; code 8i+j of a chunk with base = (j >= 4 ? 16 : 0) + (j even ? 4 :
+    8) and g = (j mod 4) / 2 has bit 4 at bit base + (g == 0 ? i-4 : i+4) of
+    the chunk's dword (5-bit), or bits 4 and 5 at base + s and base + 1 + s of
+    dword i/2, s = -4, -2, 4, 6 for (i mod 2, g) = (0,0), (0,1), (1,0), (1,1)
+    (6-bit)."""
+    N, K = codes.shape
+    hb = bits - 4
+    c = codes.to(torch.int64)
+    nib = pack_nibbles(c & 0xF)
+    hi = (c >> 4).reshape(N, K // 32, 4, 8)
+    words = torch.zeros((N, K // 32, hb), dtype=torch.int64, device=codes.device)
+    for i in range(4):
+        for j in range(8):
+            g = (j % 4) // 2
+            base = (16 if j >= 4 else 0) + (4 if j % 2 == 0 else 8)
+            for b in range(hb):
+                if hb == 1:
+                    w, pos = 0, base + _HI5(i, g)
+                else:
+                    w, pos = i // 2, base + b + _HI6[i % 2][g]
+                words[:, :, w] |= ((hi[:, :, i, j] >> b) & 1) << pos
+    plane = torch.stack([(words >> (8 * t)) & 0xFF for t in range(4)], dim=-1)
+    return torch.cat([nib.reshape(-1), plane.to(torch.uint8).reshape(-1)]).contiguous()
+
+
 def pack_records(base: torch.Tensor, sub: torch.Tensor) -> torch.Tensor:
     """base float16 [N][B], sub uint8 [N][B][8] (0..63) -> uint8 [N][B][8].
 
@@ -214,6 +253,8 @@ def encode(codes: torch.Tensor, fmt: Fmt, scales=None, d=None, sc=None, m=None,
     N, K = codes.shape
     if fmt.bits == 8:
         qw = codes.to(torch.int8).contiguous()
+    elif fmt.bits in (5, 6):
+        qw = pack_hi_planes(codes, fmt.bits)
     else:
         qw = pack_nibbles(codes)
     if fmt.layout == LAYOUT_SYM:
@@ -316,7 +357,14 @@ def rows_of(p: Packed, rows) -> Packed:
     idx = torch.as_tensor(rows, dtype=torch.long, device=p.qweight.device)
     scales = p.scales if p.fmt.layout == LAYOUT_FP8_TENSOR else \
         p.scales.index_select(0, idx).contiguous()  # FP8: one scale for the matrix
-    return Packed(p.qweight.index_select(0, idx).contiguous(),
+    if p.fmt.bits in (5, 6):  # two planes: nibbles [N][K/2], high bits [N][K*(bits-4)/8]
+        half = p.N * p.K // 2
+        nib = p.qweight[:half].reshape(p.N, p.K // 2).index_select(0, idx)
+        hi = p.qweight[half:].reshape(p.N, -1).index_select(0, idx)
+        qw = torch.cat([nib.reshape(-1), hi.reshape(-1)]).contiguous()
+    else:
+        qw = p.qweight.index_select(0, idx).contiguous()
+    return Packed(qw,
                   scales,
                   None if p.zeros is None else p.zeros.index_select(0, idx).contiguous(),
                   len(rows), p.K, p.fmt)

@@ -7,7 +7,7 @@
  * material; rows are [out][in], as the FFN key (16384x4096) and FFN value
  * (4096x16384) of a width-4096 RWKV-7 model are listed on the package page
  * "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization Details").
- * Four storage formats are supported:
+ * Five storage formats are supported:
  *
  *   RQ_LAYOUT_SYM, bits = 4, group in {32, 64, 128}
  *       The 4-bit symmetric format with one scale per group of consecutive
@@ -32,6 +32,19 @@
  *       6j..6j+5).  zeros: records of the same shape holding m and the
  *       sub-mins mn_j.  With j = (k mod 256)/32:
  *       w = (d * sc_j) * q - (m * mn_j).
+ *   RQ_LAYOUT_ASYM_SB, bits = 5 or 6, group = 32
+ *       The same superblock layout with 5- or 6-bit unsigned codes (0..31,
+ *       0..63): the FFN key and head in 5 bits (COMPRESSION) and the FFN in
+ *       6 bits (REDUCTION), same article and section; the pages give the
+ *       widths only, the storage below is ours.  qweight holds two planes: the
+ *       low 4 bits of every code exactly as the 4-bit layout stores them
+ *       ([N][K/2]), then the high bits, [N][K*(bits-4)/8] bytes: per row, per
+ *       32-code chunk, 1 (5-bit) or 2 (6-bit) little-endian dwords.  Code
+ *       8i + j of a chunk (i = 0..3, j = 0..7), with base = (j >= 4 ? 16 : 0)
+ *       + (j even ? 4 : 8) and g = (j mod 4)/2, keeps bit 4 at bit
+ *       base + (g == 0 ? i - 4 : i + 4) of the dword (5-bit), or bits 4 and 5
+ *       at bits base + s and base + 1 + s of dword i/2 with s = -4, -2, 4, 6
+ *       for (i mod 2, g) = (0,0), (0,1), (1,0), (1,1) (6-bit).
  *   RQ_LAYOUT_FP8_TENSOR, bits = 8, group = 0
  *       FP8 E4M3 weights with one binary32 scale for the whole matrix, the
  *       format of the package page "RWKV-7 FP8 Quantized Inference" (sections
