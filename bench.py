@@ -76,7 +76,8 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers of the step the CPU oracle times")
     ap.add_argument("--layers", type=int, default=None, help="(testing) fewer layers")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 W8A16 step")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 W8A16 step and the 5-/6-bit shapes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 64 MiB with rq_probe_copy (the reference kernel "
                          "for scaling the memory-traffic counters)")
@@ -296,6 +297,36 @@ def main():
         del W8s, W8, X8, Y8, calls8
         torch.cuda.empty_cache()
 
+    # ---- 5- and 6-bit asymmetric codes, M = 1: launch time per shape --------
+    # Twelve distinct matrices per shape (over 500 MB between reuses).
+    hib = None
+    if not args.no_fp8:
+        log("5-/6-bit shapes")
+        hib = {}
+        for f in (S.ASYM5_G32, S.ASYM6_G32):
+            for (N, K) in ((16384, 4096), (4096, 16384)):
+                Wh = [S.gen_matrix("rwkv7-13.3b-hib", r, 4, N, K, f, device=dev) for r in range(12)]
+                xh = S.gen_x(cfg, 0, 4, 1, K, device=dev)
+                yh = torch.empty((1, N), dtype=torch.float32, device=dev)
+                cs = [ST.step_calls([(0, 4, N, K)], [w], [xh], [yh], "matrix")[0] for w in Wh]
+                for c in cs:
+                    c()
+                best = 1e9
+                for _ in range(3):
+                    a = torch.cuda.Event(enable_timing=True)
+                    e = torch.cuda.Event(enable_timing=True)
+                    a.record(torch.cuda.current_stream())
+                    for c in cs * 2:
+                        c()
+                    e.record(torch.cuda.current_stream())
+                    torch.cuda.synchronize()
+                    best = min(best, a.elapsed_time(e) * 1e-3 / (2 * len(cs)))
+                mb = f.weight_bytes(N, K) + 2 * K + 4 * N
+                hib[f"{f.tag} {N}x{K}"] = {"us_per_launch": round(best * 1e6, 3),
+                                           "bytes": mb, "GBps": round(mb / best / 1e9, 1)}
+                del Wh, cs
+        torch.cuda.empty_cache()
+
     # ---- CPU oracle on a bounded sample of the same step --------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -342,6 +373,7 @@ def main():
         "m32": mfma["32"],
         "mfma_m": mfma,
         "fp8_w8a16_m1": fp8,
+        "asym_5_6_bit_m1": hib,
         "per_shape_m1": per_kernel,
         "roofline": {"bound": "hbm", "kernel": f"int4 g64 GEMV {dom_name}, M=1",
                      "achieved": dom_v["GBps"], "peak": HBM_PEAK_GBS,
