@@ -70,8 +70,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--m32-steps", type=int, default=20)
-    ap.add_argument("--graph", action="store_true",
-                    help="replay each step as a captured graph instead of direct launches")
+    ap.add_argument("--stream", dest="graph", action="store_false",
+                    help="direct launches on one stream instead of replaying each step as "
+                         "a captured HIP graph (the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers of the step the CPU oracle times")
@@ -290,6 +291,7 @@ def main():
                            "stream: 32 layers x (4 x 4096x4096, 16384x4096, 4096x16384), "
                            "8 distinct weight sets cycled (1.07 GB between reuses)",
                "entry": "rq_gemv / rq_gemv_batched (vector units)", "M": 1,
+               "launch_mode": "stream",
                "launch_calls": len(calls8), "bytes_per_step": b8,
                "ms_per_step": round(sec8 * 1e3, 4), "GBps": round(b8 / sec8 / 1e9, 2),
                "pct_of_hbm_peak": round(100 * b8 / sec8 / 1e9 / HBM_PEAK_GBS, 2),
