@@ -47,14 +47,20 @@
 
 namespace rq {
 
+// One byte per code (int8, FP8); FP8 has no per-group scale material (one
+// binary32 scale for the matrix, applied to the finished sums), and its
+// groups are nominal 64-wide units of work.
+constexpr bool mm_byte(int fmt) { return fmt == FMT_S8 || fmt == FMT_F8; }
+constexpr int MM_F8_GROUP = 64;
+
 template <int FMT>
 struct MfmaT {
-  static constexpr int KS = (FMT == FMT_S8) ? 16 : 32;  // k per MFMA
+  static constexpr int KS = mm_byte(FMT) ? 16 : 32;  // k per MFMA
 };
 
 template <int FMT>
 __device__ __forceinline__ f4 mfma_step(const u32* a, const u32* b, f4 c) {
-  if constexpr (FMT == FMT_S8) {
+  if constexpr (mm_byte(FMT)) {
     const h4 av = __builtin_bit_cast(h4, u32x2{a[0], a[1]});
     const h4 bv = __builtin_bit_cast(h4, u32x2{b[0], b[1]});
     return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
@@ -96,8 +102,9 @@ constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd) {
 constexpr int mm_cslot(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
   const int round = mm_round(fmt, mt, wk, g, rd);
   const int rows = 16 * nt * wr;
-  const int codes = rows * (fmt == FMT_S8 ? round : round / 2);
-  const int scales = fmt == FMT_A4 ? 2 * rows * (round / SUPERBLOCK) * 8 : rows * (round / g) * 2;
+  const int codes = rows * (mm_byte(fmt) ? round : round / 2);
+  const int scales = fmt == FMT_F8 ? 0
+                     : fmt == FMT_A4 ? 2 * rows * (round / SUPERBLOCK) * 8 : rows * (round / g) * 2;
   return codes + scales;
 }
 // copy instructions per round: x row segments; code pieces and scale dwords
@@ -109,8 +116,9 @@ constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd) {
 constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
   const int round = mm_round(fmt, mt, wk, g, rd);
   const int rows = 16 * nt * wr;
-  const int cc = (rows * (fmt == FMT_S8 ? round : round / 2) / 16 + 63) / 64;
-  const int sd = fmt == FMT_A4 ? rows * (round / SUPERBLOCK) * 2 : rows * (round / g) / 2;
+  const int cc = (rows * (mm_byte(fmt) ? round : round / 2) / 16 + 63) / 64;
+  const int sd = fmt == FMT_F8 ? 0
+                 : fmt == FMT_A4 ? rows * (round / SUPERBLOCK) * 2 : rows * (round / g) / 2;
   return cc + (fmt == FMT_A4 ? 2 : 1) * ((sd + 63) / 64);
 }
 // Rounds copied ahead.  Code slots to keep MM_CODE_AHEAD bytes in flight
@@ -151,10 +159,10 @@ struct Mm {
   static constexpr int ROWS = TR * WR;              // rows per workgroup
   static constexpr int XSTR = ROUND + 8;            // halves per LDS row of x
   static constexpr int GPC = KC / G;                // groups per chunk
-  static constexpr int DPG = (FMT == FMT_S8) ? G / 16 : G / 32;  // dwords per lane per group
+  static constexpr int DPG = mm_byte(FMT) ? G / 16 : G / 32;  // dwords per lane per group
   static constexpr int BPL = DPG * 4;               // code bytes per lane per group
-  static constexpr int GB = (FMT == FMT_S8) ? G : G / 2;  // code bytes per group of a row
-  static constexpr int RS = (FMT == FMT_S8) ? ROUND : ROUND / 2;  // code bytes per row and round
+  static constexpr int GB = mm_byte(FMT) ? G : G / 2;  // code bytes per group of a row
+  static constexpr int RS = mm_byte(FMT) ? ROUND : ROUND / 2;  // code bytes per row and round
   static constexpr int PR = RS / 16;                // 16-byte code pieces per row and round
   // piece swizzle: row n's piece p sits at n*PR + (p ^ (n & SWZ)); 16 rows of
   // a fragment read then start in 16 (PR >= 16) or 8 different bank groups
@@ -162,7 +170,7 @@ struct Mm {
   static constexpr int NSB = ROUND / SUPERBLOCK;    // superblocks per round (asym)
   // scale dwords per row and round: sym, the round's binary16 scales; asym,
   // per kind (scale records, zero records) two dwords per superblock
-  static constexpr int SRD = (FMT == FMT_A4) ? 2 * NSB : ROUND / G / 2;
+  static constexpr int SRD = (FMT == FMT_F8) ? 0 : (FMT == FMT_A4) ? 2 * NSB : ROUND / G / 2;
   // LDS: x ring (DX+1 slots), then code ring (DC+1 slots)
   static constexpr int XSLOT = mm_xslot(FMT, MT, G, WK, RD);
   static constexpr int CSLOT = mm_cslot(FMT, MT, G, WR, WK, NT, RD);
@@ -253,12 +261,14 @@ __device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, in
     const int pos = (c - S::XN) * 64 + lane;  // piece position in the slot
     const int n = pos / S::PR, sp = pos % S::PR;
     const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
-    const u32 row_bytes = (S::FMT == FMT_S8) ? (u32)K : (u32)K / 2;
+    const u32 row_bytes = mm_byte(S::FMT) ? (u32)K : (u32)K / 2;
     return (u32)row * row_bytes + (u32)(sp ^ (n & S::SWZ)) * 16u;
   } else {
-    const int j = (c - S::XN - S::CN) % S::SNK;
+    // scale copies (none for FP8: SNK is 0 and no copy index reaches here)
+    const int j = (c - S::XN - S::CN) % (S::SNK > 0 ? S::SNK : 1);
     const int q = j * 64 + lane;
-    const int n = q / S::SRD, dw = q % S::SRD;
+    constexpr int SRD1 = S::SRD > 0 ? S::SRD : 1;
+    const int n = q / SRD1, dw = q % SRD1;
     const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
     if constexpr (S::FMT == FMT_A4)
       return ((u32)row * (u32)(K / SUPERBLOCK) * 2u + (u32)dw) * 4u;
@@ -274,7 +284,7 @@ __device__ __forceinline__ const char* copy_src(int c, int k0, const _Float16* x
                                                 const void* zeros) {
   if (c < S::XN) return reinterpret_cast<const char*>(x) + (size_t)k0 * 2;
   if (c < S::XN + S::CN)
-    return reinterpret_cast<const char*>(qw) + (size_t)(S::FMT == FMT_S8 ? k0 : k0 / 2);
+    return reinterpret_cast<const char*>(qw) + (size_t)(mm_byte(S::FMT) ? k0 : k0 / 2);
   if constexpr (S::FMT == FMT_A4) {
     const bool zr = (c - S::XN - S::CN) >= S::SNK;
     return reinterpret_cast<const char*>(zr ? zeros : scales) + (size_t)(k0 / SUPERBLOCK) * 8;
@@ -292,7 +302,8 @@ __device__ __forceinline__ int copy_dst(int c) {
   }
   if (c < S::XN + S::CN) return S::C_OFF + (c - S::XN) * 1024;
   const int i = c - S::XN - S::CN;
-  return ((S::FMT == FMT_A4 && i >= S::SNK) ? S::Z_OFF : S::S_OFF) + (i % S::SNK) * 256;
+  return ((S::FMT == FMT_A4 && i >= S::SNK) ? S::Z_OFF : S::S_OFF) +
+         (i % (S::SNK > 0 ? S::SNK : 1)) * 256;
 }
 template <class S>
 constexpr int copy_lanes(int c) {
@@ -301,7 +312,7 @@ constexpr int copy_lanes(int c) {
     const int left = S::CPIECES - (c - S::XN) * 64;
     return left < 64 ? left : 64;
   }
-  const int left = S::SDK - ((c - S::XN - S::CN) % S::SNK) * 64;
+  const int left = S::SDK - ((c - S::XN - S::CN) % (S::SNK > 0 ? S::SNK : 1)) * 64;
   return left < 64 ? left : 64;
 }
 
@@ -348,7 +359,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
       for (int mt = 0; mt < MT; mt++) {
         const _Float16* src =
             xb + (mt * 16 + col) * S::XSTR + kx + g * G + h * QPL + s * (KS / 4);
-        if constexpr (FMT == FMT_S8) {
+        if constexpr (mm_byte(FMT)) {
           const u32x2 v = *reinterpret_cast<const u32x2*>(src);
           a[s][mt][0] = v.x; a[s][mt][1] = v.y;
         } else {
@@ -362,9 +373,10 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
       for (int nt = 0; nt < NT; nt++) {
         u32 b[4];
         const u32 d = code[nt][s];
-        if constexpr (FMT == FMT_S8) {
+        if constexpr (mm_byte(FMT)) {
           h2 q[2];
-          unpack8(d, q);
+          if constexpr (FMT == FMT_F8) unpack_fp8(d, q);
+          else unpack8(d, q);
           b[0] = as_u32(q[0]); b[1] = as_u32(q[1]);
         } else {
           h2 q[4];
@@ -373,8 +385,11 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
           b[2] = as_u32(q[2]); b[3] = as_u32(q[3]);
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-          P[nt][mt] = mfma_step<FMT>(a[s][mt], b, s == 0 ? f4{0, 0, 0, 0} : P[nt][mt]);
+        for (int mt = 0; mt < MT; mt++) {
+          // FP8: no group scale, so the products accumulate straight into acc
+          const f4 c0 = (FMT == FMT_F8) ? acc[nt][mt] : f4{0, 0, 0, 0};
+          P[nt][mt] = mfma_step<FMT>(a[s][mt], b, s == 0 ? c0 : P[nt][mt]);
+        }
       }
     }
     // asymmetric: the group sums of x, in the layout of P, from one more MFMA
@@ -388,7 +403,11 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
     }
     // group epilogue in binary32
 #pragma unroll
-    for (int nt = 0; nt < NT; nt++) {
+    for (int nt = 0; nt < NT && FMT == FMT_F8; nt++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[nt][mt] = P[nt][mt];
+#pragma unroll
+    for (int nt = 0; nt < NT && FMT != FMT_F8; nt++) {
       const int n = wr * S::TR + nt * 16 + col;
       float sc, t = 0.0f;
       if constexpr (FMT == FMT_A4) {
@@ -517,6 +536,8 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
   const int k_begin = split * kr;
   // y itself, or this K-range's slice of the partial-sum workspace
   float* __restrict__ y = e.out + (size_t)split * M * N;
+  // FP8: the matrix scale multiplies every finished sum (or partial sum)
+  const float mscale = (S::FMT == FMT_F8) ? *static_cast<const float*>(scales) : 1.0f;
   const int nrounds = kr / S::ROUND;
   const int row0 = ((int)blockIdx.x - e.block_begin) * S::ROWS;
 
@@ -539,7 +560,7 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) acc[nt][mt] = f4{0, 0, 0, 0};
     const int kx = wk * S::KC;  // chunk within the round
-    const int cb0 = (S::FMT == FMT_S8) ? kx : kx / 2;
+    const int cb0 = mm_byte(S::FMT) ? kx : kx / 2;
     const int j0 = kx / S::G;
     for (int r = 0; r < nrounds; r++) {
       __builtin_amdgcn_s_barrier();  // round r is in LDS
@@ -580,7 +601,7 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int m = mt * 16 + 4 * h + i;
-          if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i];
+          if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i] * mscale;
         }
     }
     return;
@@ -643,7 +664,7 @@ static bool plan_fits(int fmt, int mt, int g, const Plan& q) {
   const int round = q.wk * kc;
   const int dx = mm_xdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
   const int dc = mm_cdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
-  const int rs = fmt == FMT_S8 ? round : round / 2;
+  const int rs = mm_byte(fmt) ? round : round / 2;
   const int red = q.wk > 1 ? q.wr * q.wk * 64 * q.nt * mt * 4 * 4 : 0;
   if (kc % g != 0 || kc / g > 8) return false;
   if (q.nt * mt > (64 * (q.wr * q.wk + MM_XP + MM_CP) > 512 ? 4 : 8)) return false;
@@ -667,8 +688,9 @@ size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
 }
 
 bool gemm_supports(int fmt, int M, int K, int group) {
-  // FP8 and 5-/6-bit codes run on the vector-unit kernel
-  if (fmt == FMT_F8 || fmt == FMT_A5 || fmt == FMT_A6) return false;
+  // 5-/6-bit codes run on the vector-unit kernel
+  if (fmt == FMT_A5 || fmt == FMT_A6) return false;
+  if (fmt == FMT_F8) group = MM_F8_GROUP;
   const int mt = (M + 15) / 16;
   for (int p = 0; p < kNumPlans; p++)
     if (plan_ok(fmt, mt, group, K, p)) return true;
@@ -676,6 +698,7 @@ bool gemm_supports(int fmt, int M, int K, int group) {
 }
 
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
+  if (fmt == FMT_F8) group = MM_F8_GROUP;
   GemmCfg c{};
   c.mt = (M + 15) / 16;
   c.splits = 1;
@@ -778,7 +801,9 @@ template <int FMT, int MT>
 static void launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
                          hipStream_t s) {
   const int g = p[0]->group;
-  if constexpr (FMT == FMT_S8) {
+  if constexpr (FMT == FMT_F8) {
+    return launch_plan<FMT, MT, MM_F8_GROUP>(p, n, c, ws, s);
+  } else if constexpr (FMT == FMT_S8) {
     if (g == 16) return launch_plan<FMT, MT, 16>(p, n, c, ws, s);
     if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
     return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
@@ -810,6 +835,7 @@ hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c
     const Problem* const* q = p + first;
     if (q[0]->fmt == FMT_S4) launch_fmt<FMT_S4>(q, n, c, ws, s);
     else if (q[0]->fmt == FMT_S8) launch_fmt<FMT_S8>(q, n, c, ws, s);
+    else if (q[0]->fmt == FMT_F8) launch_fmt<FMT_F8>(q, n, c, ws, s);
     else launch_fmt<FMT_A4>(q, n, c, ws, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -136,3 +136,41 @@ def test_full_width_shapes(N, K):
     yr, b = T.oracle_y(sub, x)
     got = y if rows is None else y[:, rows]
     T.assert_close(got, yr, b, f"fp8 {N}x{K} M=1")
+
+
+@pytest.fixture
+def tune(monkeypatch):
+    def set_(**kv):
+        for k, v in kv.items():
+            monkeypatch.setenv(k, str(v))
+        rq.tuning_reload()
+    yield set_
+    monkeypatch.undo()
+    rq.tuning_reload()
+
+
+@pytest.mark.parametrize("plan", [str(i) for i in range(1, 16)])
+def test_matrix_core_plans(tune, plan):
+    """FP8 on every workgroup arrangement of the matrix-core kernel (the
+    products accumulate straight into the tile; the matrix scale multiplies
+    the stored sums), ragged N."""
+    tune(RQ_GEMM_PLAN=plan)
+    p = T.to_dev(S.gen_matrix("f8plan", 2, 0, 130, 2048, F))
+    for M in (16, 48):
+        x = x_for(M, 2048, seed=M + int(plan))
+        y = torch.full((M, 130), float("nan"), device="cuda")
+        T.run("gemm", p, x, y)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"fp8 plan={plan} M={M}")
+
+
+@pytest.mark.parametrize("splits", ["2", "4"])
+def test_matrix_core_split_k(tune, splits):
+    """K split over workgroups: each partial is scaled, the reduce adds them."""
+    tune(RQ_GEMM_SPLITS=splits)
+    p = T.to_dev(S.gen_matrix("f8split", 0, 0, 256, 8192, F))
+    x = x_for(64, 8192, seed=5)
+    y = torch.full((64, 256), float("nan"), device="cuda")
+    T.run("gemm", p, x, y)
+    yr, b = T.oracle_y(p, x)
+    T.assert_close(y, yr, b, f"fp8 splits={splits}")
