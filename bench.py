@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="(testing) fewer layers")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 W8A16 step and the 5-/6-bit shapes")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the fp16 dense and tensor-parallel shard measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 64 MiB with rq_probe_copy (the reference kernel "
                          "for scaling the memory-traffic counters)")
@@ -350,8 +352,72 @@ def main():
                 del Wh, cs
         torch.cuda.empty_cache()
 
+    # ---- context: the same products in fp16 dense (torch F.linear), and one
+    # GPU's share of an 8-way tensor-parallel split -------------------------
+    def launch_time(calls, reps=3):
+        """Best average seconds per call over back-to-back runs of `calls`."""
+        for c in calls[:4]:
+            c()
+        best = 1e9
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            a.record(torch.cuda.current_stream())
+            for c in calls:
+                c()
+            e.record(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(e) * 1e-3 / len(calls))
+        return best
+
+    dense = None
+    if not args.no_context:
+        log("fp16 dense comparison")
+        dense = {}
+        for (N, K) in ((4096, 4096), (16384, 4096), (4096, 16384)):
+            reps = max(2, (1 << 30) // (2 * N * K))  # >= 1 GB of fp16 weights between reuses
+            Wd = [torch.randn((N, K), device=dev).half() for _ in range(reps)]
+            Wq = [S.gen_matrix("rwkv7-13.3b-dense", r, 4, N, K, fmt, device=dev)
+                  for r in range(reps)]
+            for M in (1, 32):
+                xd = S.gen_x(cfg, 0, 4, M, K, device=dev)
+                yd = torch.empty((M, N), dtype=torch.float16, device=dev)
+                yq = torch.empty((M, N), dtype=torch.float32, device=dev)
+                tf = launch_time([(lambda w=w: torch.matmul(xd, w.t(), out=yd)) for w in Wd])
+                entry = "rq_gemv" if M == 1 else "rq_gemm_smallm"
+                tq = launch_time([rq.prepare(entry, w.qweight, w.scales, None, xd, yq, M, N, K,
+                                             4, 64, 0) for w in Wq])
+                dense[f"{N}x{K} M={M}"] = {
+                    "fp16_us": round(tf * 1e6, 3), "int4g64_us": round(tq * 1e6, 3),
+                    "int4g64_entry": entry, "speedup": round(tf / tq, 3),
+                    "fp16_GBps": round((2 * N * K + 2 * M * K + 2 * M * N) / tf / 1e9, 1)}
+            del Wd, Wq
+            torch.cuda.empty_cache()
+
+    tp8 = None
+    if not args.no_context:
+        log("tensor-parallel shard shapes")
+        tp8 = {}
+        # column shards (receptance/key/value/output rows, FFN key rows) and row
+        # shards (output and FFN value along K) of an 8-way split, M = 1
+        for (N, K, what) in ((512, 4096, "column shard of a 4096x4096 projection"),
+                             (2048, 4096, "column shard of the FFN key"),
+                             (4096, 512, "row shard of the output projection"),
+                             (4096, 2048, "row shard of the FFN value")):
+            reps = max(2, (600 << 20) // fmt.weight_bytes(N, K))
+            Wt = [S.gen_matrix("rwkv7-13.3b-tp8", r, 0, N, K, fmt, device=dev) for r in range(reps)]
+            xt = S.gen_x(cfg, 0, 0, 1, K, device=dev)
+            yt = torch.empty((1, N), dtype=torch.float32, device=dev)
+            t = launch_time([rq.prepare("rq_gemv", w.qweight, w.scales, None, xt, yt, 1, N, K,
+                                        4, 64, 0) for w in Wt])
+            mb = fmt.weight_bytes(N, K) + 2 * K + 4 * N
+            tp8[f"{N}x{K}"] = {"what": what, "us_per_launch": round(t * 1e6, 3),
+                               "GBps": round(mb / t / 1e9, 1)}
+            del Wt
+        torch.cuda.empty_cache()
+
     # ---- CPU oracle on a bounded sample of the same step --------------------
-    cpu = None
+    cpu = cpu_threads = None
     if not args.no_cpu_baseline:
         import oracle
         sample = [i for i, m in enumerate(mats) if m[0] < args.cpu_layers]
@@ -368,6 +434,15 @@ def main():
                "sample": f"first {args.cpu_layers} layers ({len(sample)} matrices, "
                          f"{sb / 1e6:.1f} MB) of the same M=1 step, single thread, "
                          f"{dt:.1f} s"}
+        # the same sample over disjoint row ranges on P threads (the oracle
+        # unchanged; P capped at this GPU's share of host cores)
+        P = max(1, min(16, os.cpu_count() or 1))
+        t = time.perf_counter()
+        for q, s, x, (_, _, N, K) in host:
+            oracle.gemv_ref(q, s, None, x, N, K, 4, 64, 0, threads=P)
+        dtp = time.perf_counter() - t
+        cpu_threads = {"value": round(sb / dtp / 1e9, 4), "unit": "GB/s", "cores": P,
+                       "kind": "oracle", "seconds": round(dtp, 2)}
 
     out = {
         "metric": METRIC,
@@ -405,6 +480,9 @@ def main():
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, "
                                      "scaled by a 64 MiB copy)"},
         "cpu_baseline": cpu,
+        "cpu_oracle_threads": cpu_threads,
+        "vs_fp16_dense": dense,
+        "tp8_shard_shapes_m1": tp8,
     }
     print(json.dumps(out), flush=True)
 
