@@ -282,17 +282,18 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
   const hipStream_t s = static_cast<hipStream_t>(stream);
   for (int i = 0; i < count; i++) {
     if (done[i]) continue;
-    int n = 0, rows = 0;
+    int n = 0, rows = 0, blocks48 = 0;
     for (int j = i; j < count; j++) {
       if (!done[j] && pb[j].K == pb[i].K) {
         order[n++] = &pb[j];
         rows += pb[j].N;
+        blocks48 += (pb[j].N + 47) / 48;
         done[j] = true;
       }
     }
     hipError_t e;
     if (M >= rq::MFMA_MIN_M && rq::gemm_supports(fmt, M, pb[i].K, group)) {
-      rq::GemmCfg c = rq::choose_gemm(fmt, M, rows, pb[i].K, group);
+      rq::GemmCfg c = rq::choose_gemm(fmt, M, rows, pb[i].K, group, blocks48);
       c.splits = 1;
       e = rq::launch_gemm_many(order, n, c, nullptr, s);
     } else if (rq::use_mv(fmt, M, pb[i].K, group))

@@ -99,13 +99,17 @@ constexpr int mm_round(int fmt, int mt, int wk, int g, int rd) {
 constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd) {
   return (16 * mt) * (mm_round(fmt, mt, wk, g, rd) + 8) * 2;
 }
+// Scale material is copied in whole 64-lane copies of 4-byte elements; each
+// kind's region is padded to whole copies (the lanes past the last row copy
+// the last row again into the padding), so no copy needs a lane predicate.
 constexpr int mm_cslot(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
   const int round = mm_round(fmt, mt, wk, g, rd);
   const int rows = 16 * nt * wr;
   const int codes = rows * (mm_byte(fmt) ? round : round / 2);
-  const int scales = fmt == FMT_F8 ? 0
-                     : fmt == FMT_A4 ? 2 * rows * (round / SUPERBLOCK) * 8 : rows * (round / g) * 2;
-  return codes + scales;
+  if (fmt == FMT_F8) return codes;
+  const int srd = fmt == FMT_A4 ? 2 * (round / SUPERBLOCK) : round / g / 2;  // dwords per row
+  const int region = (rows * srd + 63) / 64 * 256;
+  return codes + (fmt == FMT_A4 ? 2 : 1) * region;
 }
 // copy instructions per round: x row segments; code pieces and scale dwords
 constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd) {
@@ -177,7 +181,7 @@ struct Mm {
   static constexpr int CRING = (DX + 1) * XSLOT;    // byte offset of the code ring
   static constexpr int C_OFF = 0;                   // within a code slot
   static constexpr int S_OFF = ROWS * RS;
-  static constexpr int Z_OFF = S_OFF + ROWS * SRD * 4;  // asym zero records
+  static constexpr int Z_OFF = S_OFF + ((ROWS * SRD + 63) / 64) * 256;  // asym zero records
   // copies of one round
   static constexpr int SEG = ROUND * 2 < 1024 ? ROUND * 2 : 1024;  // x bytes per copy
   static constexpr int SEG_LANES = SEG / 16;
@@ -207,6 +211,7 @@ struct Mm {
   static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
                           CN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
                 "copy counts");
+  static_assert(CPIECES % 64 == 0, "code rows are whole copies");
   static_assert(!FITS || ((DX - 1) * XPP <= 63 && (DC - 1) * CPP <= 63),
                 "wait counts fit the counter");
 };
@@ -248,7 +253,8 @@ __device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
 // pieces (row n's 16-byte piece p stored at position n*PR + (p ^ (n & SWZ)), so
 // that the 16 rows a fragment read touches spread over the banks), then scale
 // dwords (row n's dword d at n*SRD + d; asym: scale records, then zero
-// records).  copy_off gives this lane's byte offset from the copy's base,
+// records; the lanes past the last row repeat it into the region's padding).
+// copy_off gives this lane's byte offset from the copy's base,
 // which does not change from round to round; copy_src/copy_dst the uniform
 // parts.
 template <class S>
@@ -304,16 +310,6 @@ __device__ __forceinline__ int copy_dst(int c) {
   const int i = c - S::XN - S::CN;
   return ((S::FMT == FMT_A4 && i >= S::SNK) ? S::Z_OFF : S::S_OFF) +
          (i % (S::SNK > 0 ? S::SNK : 1)) * 256;
-}
-template <class S>
-constexpr int copy_lanes(int c) {
-  if (c < S::XN) return S::SEG_LANES;
-  if (c < S::XN + S::CN) {
-    const int left = S::CPIECES - (c - S::XN) * 64;
-    return left < 64 ? left : 64;
-  }
-  const int left = S::SDK - ((c - S::XN - S::CN) % (S::SNK > 0 ? S::SNK : 1)) * 64;
-  return left < 64 ? left : 64;
 }
 
 // Multiply one chunk into acc from the LDS x slot `xsl` and code slot `sl`:
@@ -470,16 +466,17 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
       const char* src = copy_src<S>(c, k0, x, qw, scales, zeros) + off[i];
       char* dst = slot + copy_dst<S>(c);
       if constexpr (XW) {
+        // every x copy of a round has the same lane count
         if (S::SEG_LANES == 64 || lane < S::SEG_LANES) lds_copy16(src, dst);
       } else {
-        constexpr int dummy = 0;
-        (void)dummy;
+        // Code and scale copies are whole-wave instructions with no lane
+        // predicate: the code rows are whole copies, the scale regions are
+        // padded to whole copies.  (Predicated copies of different lane counts
+        // in one unrolled sequence were once merged by the compiler into a
+        // block that issued some of them under another copy's lane mask.)
         const int cc = S::XN + (i < S::CN + S::SN ? i : S::CN + S::SN - 1);
-        const int lanes = copy_lanes<S>(cc);
-        if (lane < lanes) {
-          if (cc >= S::XN + S::CN) lds_copy4(src, dst);
-          else lds_copy16(src, dst);
-        }
+        if (cc >= S::XN + S::CN) lds_copy4(src, dst);
+        else lds_copy16(src, dst);
       }
     }
   };
@@ -651,6 +648,10 @@ static constexpr Plan kPlans[] = {
     {1, 8, 2, 1},  // 12: 32 rows, 8 K-slices
     {1, 4, 2, 1},  // 13: 32 rows, 4 K-slices
     {4, 2, 2, 1},  // 14: 128 rows, 2 K-slices
+    // three row groups: 48-row workgroups (12288 rows -> 256 workgroups)
+    {3, 2, 1, 1},  // 15: 48 rows, 2 K-slices
+    {3, 2, 1, 2},  // 16: as 15, half rounds
+    {3, 4, 1, 1},  // 17: 48 rows, 4 K-slices
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -697,7 +698,7 @@ bool gemm_supports(int fmt, int M, int K, int group) {
   return false;
 }
 
-GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
+GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48) {
   if (fmt == FMT_F8) group = MM_F8_GROUP;
   GemmCfg c{};
   c.mt = (M + 15) / 16;
@@ -708,16 +709,16 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
   // workgroups cut the x staging per row (every workgroup stages all of x,
   // M*K*2 bytes, from L2).  Measured on MI355X for the RWKV-7 shapes, int4
   // g64, weights cold in HBM.
-  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14};
-  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14};
-  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14};
+  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
   // Few rows and long rows (K >= 16384) or a full M-tile stack (M > 48): the
   // x staging of 16-row workgroups dominates, so 64-row workgroups with K
   // split four ways (a second, small kernel adds the partial sums) -- at
   // 4096x16384: 16.2 -> 15.0 us (M=16), 23.0 -> 18.8 us (M=32),
   // 45.8 -> 25.0 us (M=64).
-  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14};
-  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14};
+  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
   const bool split_k = N < 8192 && (K >= 16384 || c.mt >= 4);
   const int* order = split_k ? (c.mt == 1 ? split_n_m16 : split_n)
                              : (N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n));
@@ -725,6 +726,16 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group) {
   if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
       plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
     c.plan = tu.gemm_plan - 1;
+  // 48-row workgroups where they make one wave of 224..256 row blocks (64-row
+  // ones leave a quarter of the CUs idle): one 12288x4096 product,
+  // 14.1 -> 11.2 us (M=16), 18.3 -> 12.1 us (M=32), 30.1 -> 20.3 us (M=64).
+  // Blocks are counted per problem: three 4096-row problems need 258, and
+  // the two past one wave nearly double the launch.
+  const int b48 = blocks48 > 0 ? blocks48 : (N + 47) / 48;
+  if (c.plan < 0 && !split_k && b48 >= 224 && b48 <= 256) {
+    const int p48 = c.mt <= 2 ? 17 : 15;
+    if (plan_ok(fmt, c.mt, group, K, p48)) c.plan = p48;
+  }
   for (int i = 0; i < kNumPlans && c.plan < 0; i++)
     if (plan_ok(fmt, c.mt, group, K, order[i])) c.plan = order[i];
   // Splits divide K into whole rounds and the partial sums stay under 64 MiB.
@@ -793,7 +804,10 @@ static void launch_plan(const Problem* const* p, int n, const GemmCfg& c, float*
     case 11: return launch_s<Mm<FMT, MT, 2, 2, 4, G, 1>>(p, n, c, ws, s);
     case 12: return launch_s<Mm<FMT, MT, 2, 1, 8, G, 1>>(p, n, c, ws, s);
     case 13: return launch_s<Mm<FMT, MT, 2, 1, 4, G, 1>>(p, n, c, ws, s);
-    default: return launch_s<Mm<FMT, MT, 2, 4, 2, G, 1>>(p, n, c, ws, s);
+    case 14: return launch_s<Mm<FMT, MT, 2, 4, 2, G, 1>>(p, n, c, ws, s);
+    case 15: return launch_s<Mm<FMT, MT, 1, 3, 2, G, 1>>(p, n, c, ws, s);
+    case 16: return launch_s<Mm<FMT, MT, 1, 3, 2, G, 2>>(p, n, c, ws, s);
+    default: return launch_s<Mm<FMT, MT, 1, 3, 4, G, 1>>(p, n, c, ws, s);
   }
 }
 

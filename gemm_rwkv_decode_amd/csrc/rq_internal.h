@@ -63,7 +63,9 @@ constexpr int MFMA_MIN_M = 16;
 
 // The matrix-core kernel needs K to be a whole number of its rounds.
 bool gemm_supports(int fmt, int M, int K, int group);
-GemmCfg choose_gemm(int fmt, int M, int N, int K, int group);
+// N: rows of all problems of the launch; blocks48: their 48-row blocks, each
+// problem rounded up (0: one problem of N rows)
+GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48 = 0);
 // ws: float workspace of at least splits*M*N entries (unused when
 // splits == 1).
 hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s);

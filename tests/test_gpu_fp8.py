@@ -149,7 +149,7 @@ def tune(monkeypatch):
     rq.tuning_reload()
 
 
-@pytest.mark.parametrize("plan", [str(i) for i in range(1, 16)])
+@pytest.mark.parametrize("plan", [str(i) for i in range(1, 19)])
 def test_matrix_core_plans(tune, plan):
     """FP8 on every workgroup arrangement of the matrix-core kernel (the
     products accumulate straight into the tile; the matrix scale multiplies
