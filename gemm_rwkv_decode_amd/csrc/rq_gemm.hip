@@ -102,14 +102,19 @@ constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd) {
 // Scale material is copied in whole 64-lane copies of 4-byte elements; each
 // kind's region is padded to whole copies (the lanes past the last row copy
 // the last row again into the padding), so no copy needs a lane predicate.
+// 5-/6-bit codes add the rows' high-bit plane for the round (round/8 bytes
+// per high bit and row), in 16-byte pieces, padded to whole copies too.
+constexpr int mm_hi_copies(int fmt, int round, int rows) {
+  return (rows * (round / 8 * hi_bits(fmt)) / 16 + 63) / 64;
+}
 constexpr int mm_cslot(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
   const int round = mm_round(fmt, mt, wk, g, rd);
   const int rows = 16 * nt * wr;
-  const int codes = rows * (mm_byte(fmt) ? round : round / 2);
+  const int codes = rows * (mm_byte(fmt) ? round : round / 2) + mm_hi_copies(fmt, round, rows) * 1024;
   if (fmt == FMT_F8) return codes;
-  const int srd = fmt == FMT_A4 ? 2 * (round / SUPERBLOCK) : round / g / 2;  // dwords per row
+  const int srd = is_asym(fmt) ? 2 * (round / SUPERBLOCK) : round / g / 2;  // dwords per row
   const int region = (rows * srd + 63) / 64 * 256;
-  return codes + (fmt == FMT_A4 ? 2 : 1) * region;
+  return codes + (is_asym(fmt) ? 2 : 1) * region;
 }
 // copy instructions per round: x row segments; code pieces and scale dwords
 constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd) {
@@ -122,8 +127,8 @@ constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd)
   const int rows = 16 * nt * wr;
   const int cc = (rows * (mm_byte(fmt) ? round : round / 2) / 16 + 63) / 64;
   const int sd = fmt == FMT_F8 ? 0
-                 : fmt == FMT_A4 ? rows * (round / SUPERBLOCK) * 2 : rows * (round / g) / 2;
-  return cc + (fmt == FMT_A4 ? 2 : 1) * ((sd + 63) / 64);
+                 : is_asym(fmt) ? rows * (round / SUPERBLOCK) * 2 : rows * (round / g) / 2;
+  return cc + mm_hi_copies(fmt, round, rows) + (is_asym(fmt) ? 2 : 1) * ((sd + 63) / 64);
 }
 // Rounds copied ahead.  Code slots to keep MM_CODE_AHEAD bytes in flight
 // come first (at least 2 rounds), then as many x rounds as fit (at most
@@ -174,13 +179,19 @@ struct Mm {
   static constexpr int NSB = ROUND / SUPERBLOCK;    // superblocks per round (asym)
   // scale dwords per row and round: sym, the round's binary16 scales; asym,
   // per kind (scale records, zero records) two dwords per superblock
-  static constexpr int SRD = (FMT == FMT_F8) ? 0 : (FMT == FMT_A4) ? 2 * NSB : ROUND / G / 2;
+  static constexpr int SRD = (FMT == FMT_F8) ? 0 : is_asym(FMT) ? 2 * NSB : ROUND / G / 2;
+  // 5-/6-bit codes: the high-bit plane of the round, HRS bytes per row
+  static constexpr int HB = hi_bits(FMT);
+  static constexpr int HRS = ROUND / 8 * HB;
+  static constexpr int HPR = HRS / 16;              // 16-byte pieces per row and round
   // LDS: x ring (DX+1 slots), then code ring (DC+1 slots)
   static constexpr int XSLOT = mm_xslot(FMT, MT, G, WK, RD);
   static constexpr int CSLOT = mm_cslot(FMT, MT, G, WR, WK, NT, RD);
   static constexpr int CRING = (DX + 1) * XSLOT;    // byte offset of the code ring
   static constexpr int C_OFF = 0;                   // within a code slot
-  static constexpr int S_OFF = ROWS * RS;
+  static constexpr int HN = mm_hi_copies(FMT, ROUND, ROWS);  // high-bit copies
+  static constexpr int H_OFF = ROWS * RS;           // high-bit plane (rows of HRS bytes)
+  static constexpr int S_OFF = H_OFF + HN * 1024;
   static constexpr int Z_OFF = S_OFF + ((ROWS * SRD + 63) / 64) * 256;  // asym zero records
   // copies of one round
   static constexpr int SEG = ROUND * 2 < 1024 ? ROUND * 2 : 1024;  // x bytes per copy
@@ -191,17 +202,18 @@ struct Mm {
   static constexpr int CN = (CPIECES + 63) / 64;
   static constexpr int SDK = ROWS * SRD;            // scale dwords per kind
   static constexpr int SNK = (SDK + 63) / 64;
-  static constexpr int SN = (FMT == FMT_A4 ? 2 : 1) * SNK;
-  static constexpr int COPIES = XN + CN + SN;
+  static constexpr int SN = (is_asym(FMT) ? 2 : 1) * SNK;
+  static constexpr int CHN = CN + HN;                // code and high-bit copies
+  static constexpr int COPIES = XN + CHN + SN;
   static constexpr int XPP = (XN + MM_XP - 1) / MM_XP;         // per x-copying wave
-  static constexpr int CPP = (CN + SN + MM_CP - 1) / MM_CP;    // per code-copying wave
+  static constexpr int CPP = (CHN + SN + MM_CP - 1) / MM_CP;   // per code-copying wave
   static constexpr int RED = (WK > 1) ? W * 64 * NT * MT * 4 : 0;  // floats
   static constexpr int LDS_BYTES = CRING + (DC + 1) * CSLOT;
   // structural conditions (the host's plan_fits checks the same)
   static constexpr bool VALID =
       GPC >= 1 && GPC <= 8 && KC % G == 0 &&
-      (FMT != FMT_A4 || (SUPERBLOCK % KC == 0 && ROUND % SUPERBLOCK == 0)) &&
-      (FMT == FMT_A4 || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
+      (!is_asym(FMT) || (SUPERBLOCK % KC == 0 && ROUND % SUPERBLOCK == 0)) &&
+      (is_asym(FMT) || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
       SEG_LANES <= 64 && ROUND * 2 % SEG == 0;
   // accumulator tiles per wave the register file holds without spilling:
   // 12 waves per workgroup leave 168 registers a lane
@@ -209,7 +221,7 @@ struct Mm {
   static constexpr bool FITS = VALID && REGS && DX >= 1 && DC >= 1 &&
                                LDS_BYTES <= LDS_LIMIT && RED * 4 <= LDS_LIMIT;
   static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
-                          CN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
+                          CHN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
                 "copy counts");
   static_assert(CPIECES % 64 == 0, "code rows are whole copies");
   static_assert(!FITS || ((DX - 1) * XPP <= 63 && (DC - 1) * CPP <= 63),
@@ -251,9 +263,10 @@ __device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
 // Copy c of a round, c in [0, COPIES): x row segments first (rows >= M
 // repeat row M-1; they only feed outputs that are never stored), then code
 // pieces (row n's 16-byte piece p stored at position n*PR + (p ^ (n & SWZ)), so
-// that the 16 rows a fragment read touches spread over the banks), then scale
+// that the 16 rows a fragment read touches spread over the banks), then, for
+// 5-/6-bit codes, high-bit pieces (row n's piece p at n*HPR + p), then scale
 // dwords (row n's dword d at n*SRD + d; asym: scale records, then zero
-// records; the lanes past the last row repeat it into the region's padding).
+// records).  The lanes past the last row repeat it into the region's padding.
 // copy_off gives this lane's byte offset from the copy's base,
 // which does not change from round to round; copy_src/copy_dst the uniform
 // parts.
@@ -269,14 +282,21 @@ __device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, in
     const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
     const u32 row_bytes = mm_byte(S::FMT) ? (u32)K : (u32)K / 2;
     return (u32)row * row_bytes + (u32)(sp ^ (n & S::SWZ)) * 16u;
+  } else if (c < S::XN + S::CHN) {
+    // high-bit pieces: the round's HRS bytes of a row, K/8*HB bytes apart
+    constexpr int HPR1 = S::HPR > 0 ? S::HPR : 1;
+    const int pos = (c - S::XN - S::CN) * 64 + lane;
+    const int n = pos / HPR1, hp = pos % HPR1;
+    const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
+    return (u32)row * (u32)(K / 8 * S::HB) + (u32)hp * 16u;
   } else {
     // scale copies (none for FP8: SNK is 0 and no copy index reaches here)
-    const int j = (c - S::XN - S::CN) % (S::SNK > 0 ? S::SNK : 1);
+    const int j = (c - S::XN - S::CHN) % (S::SNK > 0 ? S::SNK : 1);
     const int q = j * 64 + lane;
     constexpr int SRD1 = S::SRD > 0 ? S::SRD : 1;
     const int n = q / SRD1, dw = q % SRD1;
     const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
-    if constexpr (S::FMT == FMT_A4)
+    if constexpr (is_asym(S::FMT))
       return ((u32)row * (u32)(K / SUPERBLOCK) * 2u + (u32)dw) * 4u;
     else  // K / G is even (host check): a row's scales start on a dword
       return ((u32)row * (u32)(K / S::G) / 2u + (u32)dw) * 4u;
@@ -287,19 +307,21 @@ __device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, in
 template <class S>
 __device__ __forceinline__ const char* copy_src(int c, int k0, const _Float16* x,
                                                 const uint8_t* qw, const void* scales,
-                                                const void* zeros) {
+                                                const void* zeros, int N, int K) {
   if (c < S::XN) return reinterpret_cast<const char*>(x) + (size_t)k0 * 2;
   if (c < S::XN + S::CN)
     return reinterpret_cast<const char*>(qw) + (size_t)(mm_byte(S::FMT) ? k0 : k0 / 2);
-  if constexpr (S::FMT == FMT_A4) {
-    const bool zr = (c - S::XN - S::CN) >= S::SNK;
+  if (c < S::XN + S::CHN)  // the high-bit plane follows every row's nibbles
+    return reinterpret_cast<const char*>(qw) + (size_t)N * (K / 2) + (size_t)(k0 / 8) * S::HB;
+  if constexpr (is_asym(S::FMT)) {
+    const bool zr = (c - S::XN - S::CHN) >= S::SNK;
     return reinterpret_cast<const char*>(zr ? zeros : scales) + (size_t)(k0 / SUPERBLOCK) * 8;
   } else {
     return reinterpret_cast<const char*>(scales) + (size_t)(k0 / S::G) * 2;
   }
 }
 
-// Destination offset of copy c within its slot, and its active lanes.
+// Destination offset of copy c within its slot.
 template <class S>
 __device__ __forceinline__ int copy_dst(int c) {
   if (c < S::XN) {
@@ -307,8 +329,9 @@ __device__ __forceinline__ int copy_dst(int c) {
     return (m * S::XSTR + seg * (S::SEG / 2)) * 2;
   }
   if (c < S::XN + S::CN) return S::C_OFF + (c - S::XN) * 1024;
-  const int i = c - S::XN - S::CN;
-  return ((S::FMT == FMT_A4 && i >= S::SNK) ? S::Z_OFF : S::S_OFF) +
+  if (c < S::XN + S::CHN) return S::H_OFF + (c - S::XN - S::CN) * 1024;
+  const int i = c - S::XN - S::CHN;
+  return ((is_asym(S::FMT) && i >= S::SNK) ? S::Z_OFF : S::S_OFF) +
          (i % (S::SNK > 0 ? S::SNK : 1)) * 256;
 }
 
@@ -346,6 +369,18 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
         code[nt][0] = *reinterpret_cast<const u32*>(src);
       }
     }
+    // 5-/6-bit codes: the high-bit dwords of the row's 32-code chunk
+    u32 hw[NT][2];
+    if constexpr (S::HB > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        const int n = wr * S::TR + nt * 16 + col;
+        const u32* hp = reinterpret_cast<const u32*>(sl + S::H_OFF + n * S::HRS +
+                                                     (cb0 / 16 + g) * 4 * S::HB);
+        hw[nt][0] = hp[0];
+        hw[nt][1] = S::HB == 2 ? hp[1] : 0u;
+      }
+    }
     f4 P[NT][MT];
     // A fragments of every K-step of the group and every M-tile
     u32 a[DPG][MT][4];
@@ -374,6 +409,18 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
           if constexpr (FMT == FMT_F8) unpack_fp8(d, q);
           else unpack8(d, q);
           b[0] = as_u32(q[0]); b[1] = as_u32(q[1]);
+        } else if constexpr (S::HB > 0) {
+          // this lane's nibble dword is dword h of the group's 32-code chunk
+          u32 hlo, hhi;
+          hi_words<S::HB>(hw[nt], h, &hlo, &hhi);
+          h2 q[4];
+          unpack4h<S::HB>(d, hlo, hhi, q);
+          // pairs (q0,q4) (q1,q5) (q2,q6) (q3,q7) -> k order (q0,q1) .. (q6,q7)
+          const u32 p0 = as_u32(q[0]), p1 = as_u32(q[1]), p2 = as_u32(q[2]), p3 = as_u32(q[3]);
+          b[0] = __builtin_amdgcn_perm(p1, p0, 0x05040100u);
+          b[1] = __builtin_amdgcn_perm(p3, p2, 0x05040100u);
+          b[2] = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
+          b[3] = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
         } else {
           h2 q[4];
           unpack4n<FMT == FMT_S4>(d, q);
@@ -391,7 +438,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
     // asymmetric: the group sums of x, in the layout of P, from one more MFMA
     // against codes that are all 1 (a group is one K-step)
     f4 xg[MT];
-    if constexpr (FMT == FMT_A4) {
+    if constexpr (is_asym(FMT)) {
       const u32 one2 = 0x3C003C00u;  // binary16 (1, 1)
       const u32 ones[4] = {one2, one2, one2, one2};
 #pragma unroll
@@ -406,7 +453,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
     for (int nt = 0; nt < NT && FMT != FMT_F8; nt++) {
       const int n = wr * S::TR + nt * 16 + col;
       float sc, t = 0.0f;
-      if constexpr (FMT == FMT_A4) {
+      if constexpr (is_asym(FMT)) {
         const int kin = (kb % S::ROUND) + g * G;  // k within the round
         const int sb = kin / SUPERBLOCK, j = (kin % SUPERBLOCK) / SB_GROUP;
         const u32* sr = reinterpret_cast<const u32*>(sl + S::S_OFF) + n * S::SRD + 2 * sb;
@@ -423,7 +470,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           float v = __builtin_fmaf(sc, P[nt][mt][i], acc[nt][mt][i]);
-          if constexpr (FMT == FMT_A4) v = __builtin_fmaf(-t, xg[mt][i], v);
+          if constexpr (is_asym(FMT)) v = __builtin_fmaf(-t, xg[mt][i], v);
           acc[nt][mt][i] = v;
         }
       }
@@ -451,7 +498,7 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
   static_assert(MM_CP == 1, "the code wave's copies are compile-time");
   // copy index of position i (uniform)
   auto cidx = [&](int i) {
-    return XW ? min(i * MM_XP + p, S::XN - 1) : S::XN + min(i, S::CN + S::SN - 1);
+    return XW ? min(i * MM_XP + p, S::XN - 1) : S::XN + min(i, S::CHN + S::SN - 1);
   };
   u32 off[NC];
 #pragma unroll
@@ -463,19 +510,19 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
 #pragma unroll
     for (int i = 0; i < NC; i++) {
       const int c = cidx(i);
-      const char* src = copy_src<S>(c, k0, x, qw, scales, zeros) + off[i];
+      const char* src = copy_src<S>(c, k0, x, qw, scales, zeros, N, K) + off[i];
       char* dst = slot + copy_dst<S>(c);
       if constexpr (XW) {
         // every x copy of a round has the same lane count
         if (S::SEG_LANES == 64 || lane < S::SEG_LANES) lds_copy16(src, dst);
       } else {
-        // Code and scale copies are whole-wave instructions with no lane
-        // predicate: the code rows are whole copies, the scale regions are
-        // padded to whole copies.  (Predicated copies of different lane counts
-        // in one unrolled sequence were once merged by the compiler into a
-        // block that issued some of them under another copy's lane mask.)
-        const int cc = S::XN + (i < S::CN + S::SN ? i : S::CN + S::SN - 1);
-        if (cc >= S::XN + S::CN) lds_copy4(src, dst);
+        // Code, high-bit and scale copies are whole-wave instructions with no
+        // lane predicate: the code rows are whole copies, the other regions
+        // are padded to whole copies.  (Predicated copies of different lane
+        // counts in one unrolled sequence were once merged by the compiler
+        // into a block that issued some of them under another copy's mask.)
+        const int cc = S::XN + (i < S::CHN + S::SN ? i : S::CHN + S::SN - 1);
+        if (cc >= S::XN + S::CHN) lds_copy4(src, dst);
         else lds_copy16(src, dst);
       }
     }
@@ -669,8 +716,8 @@ static bool plan_fits(int fmt, int mt, int g, const Plan& q) {
   const int red = q.wk > 1 ? q.wr * q.wk * 64 * q.nt * mt * 4 * 4 : 0;
   if (kc % g != 0 || kc / g > 8) return false;
   if (q.nt * mt > (64 * (q.wr * q.wk + MM_XP + MM_CP) > 512 ? 4 : 8)) return false;
-  if (fmt == FMT_A4 && (SUPERBLOCK % kc != 0 || round % SUPERBLOCK != 0)) return false;
-  if (fmt != FMT_A4 && (round / g) % 2 != 0) return false;
+  if (is_asym(fmt) && (SUPERBLOCK % kc != 0 || round % SUPERBLOCK != 0)) return false;
+  if (!is_asym(fmt) && (round / g) % 2 != 0) return false;
   if (rs / 16 < 8 || ((rs / 16) & (rs / 16 - 1)) != 0) return false;
   const int bytes = (dx + 1) * mm_xslot(fmt, mt, g, q.wk, q.rd) +
                     (dc + 1) * mm_cslot(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
@@ -689,8 +736,6 @@ size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
 }
 
 bool gemm_supports(int fmt, int M, int K, int group) {
-  // 5-/6-bit codes run on the vector-unit kernel
-  if (fmt == FMT_A5 || fmt == FMT_A6) return false;
   if (fmt == FMT_F8) group = MM_F8_GROUP;
   const int mt = (M + 15) / 16;
   for (int p = 0; p < kNumPlans; p++)
@@ -821,7 +866,7 @@ static void launch_group(const Problem* const* p, int n, const GemmCfg& c, float
     if (g == 16) return launch_plan<FMT, MT, 16>(p, n, c, ws, s);
     if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
     return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
-  } else if constexpr (FMT == FMT_A4) {
+  } else if constexpr (is_asym(FMT)) {
     return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
   } else {
     if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
@@ -850,6 +895,8 @@ hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c
     if (q[0]->fmt == FMT_S4) launch_fmt<FMT_S4>(q, n, c, ws, s);
     else if (q[0]->fmt == FMT_S8) launch_fmt<FMT_S8>(q, n, c, ws, s);
     else if (q[0]->fmt == FMT_F8) launch_fmt<FMT_F8>(q, n, c, ws, s);
+    else if (q[0]->fmt == FMT_A5) launch_fmt<FMT_A5>(q, n, c, ws, s);
+    else if (q[0]->fmt == FMT_A6) launch_fmt<FMT_A6>(q, n, c, ws, s);
     else launch_fmt<FMT_A4>(q, n, c, ws, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

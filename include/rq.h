@@ -170,8 +170,8 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
 /*
  * rq_gemm_smallm -- the same product and contract as rq_gemv, computed on the
  * matrix cores (fp16 MFMA on exact integer or FP8 codes, fp32 per-group
- * scaling; FP8 sums are scaled once by the matrix scale).  5- and 6-bit codes
- * are computed as rq_gemv computes them.
+ * scaling; FP8 sums are scaled once by the matrix scale).  Every layout and
+ * code width, 5- and 6-bit codes included.
  * Tuned for 16 <= M <= 64 (batched decode); smaller M is padded to 16.
  * For some shapes the K dimension is split across workgroups; the partial sums
  * then pass through a workspace the library allocates once per (device,

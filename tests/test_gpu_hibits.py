@@ -107,3 +107,59 @@ def test_ffn_key_width_4096(f):
     rows = sorted(set(torch.randperm(N, generator=g)[:64].tolist()) | {0, N - 1})
     yr, b = T.oracle_y(S.rows_of(p, rows), x)
     T.assert_close(y[:, rows], yr, b, f"{f.tag} 16384x4096 M=1")
+
+
+@pytest.fixture
+def tune(monkeypatch):
+    def set_(**kv):
+        for k, v in kv.items():
+            monkeypatch.setenv(k, str(v))
+        rq.tuning_reload()
+    yield set_
+    monkeypatch.undo()
+    rq.tuning_reload()
+
+
+@pytest.mark.parametrize("plan", [str(i) for i in range(1, 19)])
+@pytest.mark.parametrize("f", FMTS, ids=lambda f: f.tag)
+def test_matrix_core_plans(tune, plan, f):
+    """Every workgroup arrangement of the matrix-core kernel (high-bit plane
+    copied with the codes each round), ragged N, 1..4 M-tiles."""
+    tune(RQ_GEMM_PLAN=plan)
+    p = T.to_dev(S.gen_matrix("hbmm", 2, 0, 130, 4096, f))
+    for M in (16, 20, 33, 64):
+        what = f"plan={plan} {f.tag} M={M}"
+        T.say(what)
+        x = x_for(M, 4096, seed=M + 3)
+        y = torch.full((M, p.N), float("nan"), device="cuda")
+        T.run("gemm", p, x, y)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, what)
+
+
+@pytest.mark.parametrize("splits", ["2", "4", "8"])
+@pytest.mark.parametrize("f", FMTS, ids=lambda f: f.tag)
+def test_matrix_core_split_k(tune, splits, f):
+    tune(RQ_GEMM_SPLITS=splits)
+    p = T.to_dev(S.gen_matrix("hbsk", 3, 0, 256, 8192, f))
+    for M in (16, 64):
+        what = f"splits={splits} {f.tag} M={M}"
+        T.say(what)
+        x = x_for(M, 8192, seed=M + 5)
+        y = torch.full((M, p.N), float("nan"), device="cuda")
+        T.run("gemm", p, x, y)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, what)
+
+
+@pytest.mark.parametrize("f", FMTS, ids=lambda f: f.tag)
+def test_ffn_shapes_m32_matrix_cores(f):
+    """The width-4096 FFN shapes at M = 32 on the matrix cores, every row."""
+    for (N, K) in ((16384, 4096), (4096, 16384)):
+        p = T.to_dev(S.gen_matrix("hbffn32", 0, 4, N, K, f))
+        x = x_for(32, K, seed=N + K)
+        y = torch.full((32, N), float("nan"), device="cuda")
+        T.say(f"{f.tag} {N}x{K} M=32")
+        T.run("gemm", p, x, y)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"{f.tag} {N}x{K} M=32")
