@@ -180,6 +180,49 @@ __device__ __forceinline__ void pair_x4(u32 w0, u32 w1, u32 w2, u32 w3, h2 p[4])
   p[3] = as_h2(__builtin_amdgcn_perm(w3, w1, 0x07060302u));
 }
 
+// 64-byte spans of a row in the MFMA B layout.  The four lane quarters of a
+// row (l/16 = h) each need G/4 consecutive codes of every group, which for
+// groups under 64 bytes is less than one 16-byte load.  So a row is read in
+// 64-byte spans, one 16-byte piece per quarter -- quarter h takes piece
+// span_piece<SG>(h) -- and the pieces are exchanged across the quarters once
+// they have arrived: v_permlane16_swap exchanges a register of lane rows 1
+// and 3 with one of rows 0 and 2, v_permlane32_swap one of rows 2, 3 with
+// one of rows 0, 1.  SG is the number of groups in a span (64 / group bytes).
+template <int SG>
+__device__ __forceinline__ int span_piece(int h) {
+  return SG == 2 ? ((h & 1) << 1 | (h >> 1)) : h;
+}
+__device__ __forceinline__ void lane_swap16(u32& x, u32& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+__device__ __forceinline__ void lane_swap32(u32& x, u32& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+// A span's four dwords v[0..3] as loaded -> v[j*DPG + s] = dword s of this
+// quarter's share of group j of the span (DPG = 4 / SG dwords).
+//  SG = 1: the quarter's piece is its share already.
+//  SG = 2: quarters 0..3 hold pieces 0, 2, 1, 3 (group 0 = pieces 0-1, group 1
+//          = pieces 2-3); one exchange between quarters 0<->1 and 2<->3 gives
+//          quarter h dwords 2h, 2h+1 of each group.
+//  SG = 4: quarter u holds group u; a 4x4 transpose across the quarters gives
+//          quarter h dword h of each group.
+template <int SG>
+__device__ __forceinline__ void span_fix(u32* v) {
+  if constexpr (SG == 2) {
+    lane_swap16(v[0], v[2]);
+    lane_swap16(v[1], v[3]);
+  } else if constexpr (SG == 4) {
+    lane_swap16(v[0], v[1]);
+    lane_swap16(v[2], v[3]);
+    lane_swap32(v[0], v[2]);
+    lane_swap32(v[1], v[3]);
+  }
+}
+
 // Exact binary16 -> binary32 of the low / high half of a dword.
 __device__ __forceinline__ float half_lo(u32 v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));

@@ -16,9 +16,11 @@
 // D = [16 m][16 n], lane l holding D[4*(l/16) + i][l%16].  Lane l supplies row
 // l%16 of A and column l%16 of B; its lane group h = l/16 supplies one
 // quarter of the K-step.  For 4-bit codes a lane takes, per group of G, the
-// G/4 consecutive codes of its row in quarter h (one 4-, 8- or 16-byte load),
-// which unpack4 delivers pairwise as (q0,q4) (q1,q5) ...; the matching x is
-// stored in LDS already permuted the same way (pair_x4).
+// G/4 consecutive codes of its row in quarter h, which unpack4 delivers
+// pairwise as (q0,q4) (q1,q5) ...; the matching x is stored in LDS already
+// permuted the same way (pair_x4).  The codes are read in 64-byte spans of a
+// row, one 16-byte piece per quarter, and exchanged across the quarters
+// (span_fix) once they have arrived.
 //
 // Work split: a workgroup of 8 waves owns 16 rows; wave w owns the w-th
 // eighth of K, in chunks of CG groups.  It first copies its x range into its
@@ -85,6 +87,11 @@ template <int FMT, int G>
 struct MvChunk {
   static constexpr int CG = mv_cg<FMT>();
   static constexpr int DPG = (FMT == FMT_S8) ? G / 16 : G / 32;  // dwords per lane per group
+  static constexpr int GB = (FMT == FMT_S8) ? G : G / 2;          // code bytes per group, row
+  static constexpr int SG = 64 / GB;                              // groups per 64-byte span
+  static constexpr int NSP = CG / SG;                             // spans per chunk
+  // codes as loaded: one 16-byte piece per span (span_fix puts them in MFMA
+  // order once they have arrived)
   u32 code[CG * DPG];
   u32 sc[CG / 2];   // sym: the chunk's binary16 scales of this lane's row
   u32x2 srec, zrec; // asym: the superblock's records
@@ -96,10 +103,10 @@ __device__ __forceinline__ void mv_load(MvChunk<FMT, G>& r, const uint8_t* __res
                                         const void* __restrict__ zeros, u32 row, int K,
                                         int kb, int h) {
   using R = MvChunk<FMT, G>;
-  constexpr int BPL = R::DPG * 4;                  // code bytes per lane per group
-  constexpr int GB = (FMT == FMT_S8) ? G : G / 2;  // code bytes per group of a row
   const u32 row_bytes = (FMT == FMT_S8) ? (u32)K : (u32)K / 2;
-  const uint8_t* p = qw + (row * row_bytes + (u32)((FMT == FMT_S8) ? kb : kb / 2) + h * BPL);
+  // 64-byte spans of the row, 16 bytes per lane quarter (span_piece)
+  const uint8_t* p = qw + (row * row_bytes + (u32)((FMT == FMT_S8) ? kb : kb / 2) +
+                           (u32)(span_piece<R::SG>(h) * 16));
   // scale material first: waiting for it does not wait for the codes
   if constexpr (FMT == FMT_A4) {
     const u32 rec = row * (u32)(K / SUPERBLOCK) + (u32)(kb / SUPERBLOCK);
@@ -112,27 +119,22 @@ __device__ __forceinline__ void mv_load(MvChunk<FMT, G>& r, const uint8_t* __res
     r.sc[0] = v.x; r.sc[1] = v.y; r.sc[2] = v.z; r.sc[3] = v.w;
   }
 #pragma unroll
-  for (int g = 0; g < R::CG; g++) {
-    if constexpr (BPL == 16) {
-      const u32x4 v = load_stream16(p + g * GB);
-      r.code[4 * g + 0] = v.x; r.code[4 * g + 1] = v.y;
-      r.code[4 * g + 2] = v.z; r.code[4 * g + 3] = v.w;
-    } else if constexpr (BPL == 8) {
-      const u32x2 v = load_stream8(p + g * GB);
-      r.code[2 * g + 0] = v.x; r.code[2 * g + 1] = v.y;
-    } else {
-      r.code[g] = load_stream4(p + g * GB);
-    }
+  for (int sp = 0; sp < R::NSP; sp++) {
+    const u32x4 v = load_stream16(p + sp * 64);
+    r.code[4 * sp + 0] = v.x; r.code[4 * sp + 1] = v.y;
+    r.code[4 * sp + 2] = v.z; r.code[4 * sp + 3] = v.w;
   }
 }
 
 // Multiply one chunk: x of the chunk at column kx of this wave's LDS rows.
 template <int FMT, int G, int ME>
-__device__ __forceinline__ void mv_chunk(const MvChunk<FMT, G>& r, const _Float16* xw,
+__device__ __forceinline__ void mv_chunk(MvChunk<FMT, G>& r, const _Float16* xw,
                                          int xstr, int kx, int mrow, int h, f4& acc) {
   using R = MvChunk<FMT, G>;
   constexpr int KS = MvMfma<FMT>::KS;
   constexpr int QPL = G / 4;  // k per lane group per group
+#pragma unroll
+  for (int sp = 0; sp < R::NSP; sp++) span_fix<R::SG>(&r.code[4 * sp]);
 #pragma unroll
   for (int g = 0; g < R::CG; g++) {
     u32 a[R::DPG][4];
