@@ -240,56 +240,8 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
     roff[p] = rowi[p] * row_bytes;
   }
 
-  // 1. codes of every row this lane visits (5-/6-bit: and their high bits)
-  u32x4 code[NP][CPL];
-#pragma unroll
-  for (int p = 0; p < NP; p++)
-#pragma unroll
-    for (int c = 0; c < CPL; c++) code[p][c] = load_stream16(qw + (roff[p] + kc[c] * 16u));
-  u32 hw[NP][CPL][2];
-  if constexpr (hi_bits(FMT) > 0) {
-#pragma unroll
-    for (int p = 0; p < NP; p++)
-#pragma unroll
-      for (int c = 0; c < CPL; c++) {
-        const uint8_t* hp = qw + hi_offset<FMT>(N, K, rowi[p], kc[c]);
-        if constexpr (hi_bits(FMT) == 1) {
-          hw[p][c][0] = load_stream4(hp);
-          hw[p][c][1] = 0u;
-        } else {
-          const u32x2 v = load_stream8(hp);
-          hw[p][c][0] = v.x;
-          hw[p][c][1] = v.y;
-        }
-      }
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep the code loads ahead of everything else
-  // 2. their scale material
-  ScaleRaw<FMT> sr[NP][CPL];
-#pragma unroll
-  for (int p = 0; p < NP; p++) {
-    const u32 srow = roff[p] >> ssh;
-#pragma unroll
-    for (int c = 0; c < CPL; c++) {
-      const u32 k0 = (u32)kc[c] * CPC;
-      if constexpr (FMT == FMT_F8) {  // the matrix scale is applied to the row sum
-        (void)k0;
-        sr[p][c].s = u32x2{0, 0};
-        sr[p][c].z = u32x2{0, 0};
-      } else if constexpr (is_asym(FMT)) {
-        const u32 o = srow + (k0 / SUPERBLOCK) * 8u;
-        sr[p][c].s = *reinterpret_cast<const u32x2*>(scales + o);
-        sr[p][c].z = *reinterpret_cast<const u32x2*>(zeros + o);
-      } else {
-        sr[p][c].s.x = *reinterpret_cast<const uint16_t*>(scales + srow + ((k0 >> gsh) << 1));
-        sr[p][c].s.y = 0;
-        sr[p][c].z = u32x2{0, 0};
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // 3. the activations of this lane's chunks: all raw loads first, then the
-  //    pairing (a wait inside the load loop would also wait for the codes)
+  // 1. the activations of this lane's chunks (from L2), issued first: loads of
+  //    one wave complete in order, so the pairing below waits for x alone
   constexpr int XV = CPC / 8;  // 16-byte pieces of x per chunk
   u32x4 xraw[MT][CPL][XV];
 #pragma unroll
@@ -310,6 +262,50 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
       for (int c = 0; c < CPL; c++)
 #pragma unroll
         for (int v = 0; v < XV; v++) xraw[m][c][v] = u32x4{0, 0, 0, 0};
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. row by row: the codes this lane takes of the row (5-/6-bit: and their
+  //    high bits), then the row's scale material; row p's products below
+  //    wait for these loads and the ones before them only
+  u32x4 code[NP][CPL];
+  u32 hw[NP][CPL][2];
+  ScaleRaw<FMT> sr[NP][CPL];
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+#pragma unroll
+    for (int c = 0; c < CPL; c++) code[p][c] = load_stream16(qw + (roff[p] + kc[c] * 16u));
+    if constexpr (hi_bits(FMT) > 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        const uint8_t* hp = qw + hi_offset<FMT>(N, K, rowi[p], kc[c]);
+        if constexpr (hi_bits(FMT) == 1) {
+          hw[p][c][0] = load_stream4(hp);
+          hw[p][c][1] = 0u;
+        } else {
+          const u32x2 v = load_stream8(hp);
+          hw[p][c][0] = v.x;
+          hw[p][c][1] = v.y;
+        }
+      }
+    }
+    const u32 srow = roff[p] >> ssh;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      const u32 k0 = (u32)kc[c] * CPC;
+      if constexpr (FMT == FMT_F8) {  // the matrix scale is applied to the row sum
+        (void)k0;
+        sr[p][c].s = u32x2{0, 0};
+        sr[p][c].z = u32x2{0, 0};
+      } else if constexpr (is_asym(FMT)) {
+        const u32 o = srow + (k0 / SUPERBLOCK) * 8u;
+        sr[p][c].s = *reinterpret_cast<const u32x2*>(scales + o);
+        sr[p][c].z = *reinterpret_cast<const u32x2*>(zeros + o);
+      } else {
+        sr[p][c].s.x = *reinterpret_cast<const uint16_t*>(scales + srow + ((k0 >> gsh) << 1));
+        sr[p][c].s.y = 0;
+        sr[p][c].z = u32x2{0, 0};
+      }
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   h2 xr[MT][CPL][XP];
   float xs[MT][CPL];
