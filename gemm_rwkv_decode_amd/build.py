@@ -14,7 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["rq_api.hip", "rq_dequant.hip", "rq_gemv.hip", "rq_gemm.hip", "rq_mv.hip",
+SOURCES = ["rq_gemm_s4.hip", "rq_gemm_s8.hip", "rq_gemm_a4.hip", "rq_gemm_a5.hip",
+           "rq_gemm_a6.hip", "rq_gemm_f8.hip",  # the slowest first
+           "rq_api.hip", "rq_dequant.hip", "rq_gemv.hip", "rq_gemm.hip", "rq_mv.hip",
            "rq_probe.hip"]
 
 FLAGS = [

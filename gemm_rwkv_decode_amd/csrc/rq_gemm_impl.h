@@ -1,0 +1,783 @@
+// rq_gemm_impl.h -- the matrix-core kernel k_mm and its launch templates,
+// shared by rq_gemm.hip (plan choice, dispatch, split-K reduce) and the
+// per-format translation units rq_gemm_<format>.hip that instantiate it (so
+// the instances compile in parallel).
+//
+// Numerics.  The codes are small integers, exact in binary16, and x is
+// binary16 already, so one fp16 MFMA per K-step forms the exact products
+// q*x and sums them in binary32.  Each MFMA covers K-steps that lie inside
+// one quantization group; at the end of a group the binary32 group sum P is
+// scaled in binary32: acc += s * P (and, asymmetric, acc -= t * sum_k x).
+// (Rounding x or the dequantized weight to a 16-bit type before the product
+// would cost up to 2^-9 of a term -- far above the 1e-3 per-output budget on
+// activations with massive channels; exact codes avoid that.)
+//
+// Layout of one MFMA (v_mfma_f32_16x16x32_f16 for 4-bit codes,
+// v_mfma_f32_16x16x16_f16 for 8-bit codes): A = x tile [16 m][KS k],
+// B = W^T tile [KS k][16 n], D = [16 m][16 n] with lane l holding
+// D[4*(l/16) + i][l%16].  Lane l supplies row l%16 of A and column l%16 of B;
+// its lane group h = l/16 supplies one quarter of the K-step.  Which k a
+// (lane group, element) slot carries is free as long as A and B agree, so a
+// lane takes the G/4 consecutive codes of its row that fall in its quarter of
+// the group (one 4-, 8- or 16-byte load per group) and the matching x.
+//
+// Work split (MI355X: 256 CUs, 64 B/clk per CU from L2, ~160 B/clk of LDS
+// reads).  A workgroup owns WR*NT*16 rows and the whole K range (or one
+// K-range when K is split across workgroups).  Its W = WR*WK waves form WR
+// row groups of NT 16-row tiles times WK K-slices.  K advances in rounds of
+// WK*KC k: in a round, K-slice w multiplies the w-th KC-wide chunk.  The
+// round's x tile [M][WK*KC] is staged once per workgroup into LDS (double
+// buffered, one barrier per round) with coalesced 16-byte loads; every wave
+// reads its MFMA fragments from there.  Codes and scales are prefetched D
+// rounds ahead into registers.  At the end the WK K-slices of a row group
+// are added in a fixed order through LDS, so no other workgroup and no
+// second kernel is involved.  Every workgroup of a launch on a small-N
+// matrix reads all of x, so staging x (M*K*2 bytes per workgroup at up to
+// 64 B/clk) bounds those launches; splitting K over workgroups shortens it at
+// the price of a partial-sum workspace and a reduce kernel, used only where
+// that wins.
+//
+// Split-K reduction.  When the K dimension is split, every K-range writes its
+// partial tile to a workspace with plain stores and a second, small kernel
+// adds the partials in K-range order into y.  Results are deterministic; no
+// workgroup waits for another and no device-wide fence is needed (a fence per
+// workgroup costs tens of microseconds: it writes the L2 back).
+#pragma once
+
+#include "rq_common.h"
+#include "rq_internal.h"
+
+#include <type_traits>
+
+namespace rq {
+
+// One byte per code (int8, FP8); FP8 has no per-group scale material (one
+// binary32 scale for the matrix, applied to the finished sums), and its
+// groups are nominal 64-wide units of work.
+constexpr bool mm_byte(int fmt) { return fmt == FMT_S8 || fmt == FMT_F8; }
+constexpr int MM_F8_GROUP = 64;
+
+template <int FMT>
+struct MfmaT {
+  static constexpr int KS = mm_byte(FMT) ? 16 : 32;  // k per MFMA
+};
+
+template <int FMT>
+__device__ __forceinline__ f4 mfma_step(const u32* a, const u32* b, f4 c) {
+  if constexpr (mm_byte(FMT)) {
+    const h4 av = __builtin_bit_cast(h4, u32x2{a[0], a[1]});
+    const h4 bv = __builtin_bit_cast(h4, u32x2{b[0], b[1]});
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
+  } else {
+    const h8 av = __builtin_bit_cast(h8, u32x4{a[0], a[1], a[2], a[3]});
+    const h8 bv = __builtin_bit_cast(h8, u32x4{b[0], b[1], b[2], b[3]});
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
+  }
+}
+
+// Rounds are sized so one x round of the M-tile is about 32 KB (rd = 1) or
+// 16 KB (rd = 2): k per round 1024 / MT rounded down to a power of two, / rd.
+constexpr int mm_round_target(int mt) { return mt == 1 ? 1024 : (mt == 2 ? 512 : 256); }
+
+// k per wave chunk: whole groups, at least one MFMA K-step, at most 8 groups.
+constexpr int mm_kc(int fmt, int mt, int wk, int g, int rd) {
+  const int want = mm_round_target(mt) / rd / wk;
+  const int lo = g > 32 ? g : 32;
+  const int kc = want > lo ? want : lo;
+  return kc < 8 * g ? kc : 8 * g;
+}
+
+constexpr int LDS_LIMIT = 160 * 1024;
+constexpr int MM_XP = 3;           // waves copying x
+constexpr int MM_CP = 1;           // waves copying codes and scale material
+constexpr int MM_MAX_XDEPTH = 6;   // x rounds copied ahead (x comes from L2)
+constexpr int MM_MAX_CDEPTH = 13;  // code rounds copied ahead (codes come from HBM)
+constexpr int MM_CODE_AHEAD = 32 * 1024;  // code bytes to keep in flight, at least
+
+// Bytes of one x round slot ([MP][ROUND+8] halves) and of one code round
+// slot (the workgroup's code rows [ROWS][ROUND*bits/8], then its scale
+// material).
+constexpr int mm_round(int fmt, int mt, int wk, int g, int rd) {
+  return wk * mm_kc(fmt, mt, wk, g, rd);
+}
+constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd) {
+  return (16 * mt) * (mm_round(fmt, mt, wk, g, rd) + 8) * 2;
+}
+// Scale material is copied in whole 64-lane copies of 4-byte elements; each
+// kind's region is padded to whole copies (the lanes past the last row copy
+// the last row again into the padding), so no copy needs a lane predicate.
+// 5-/6-bit codes add the rows' high-bit plane for the round (round/8 bytes
+// per high bit and row), in 16-byte pieces, padded to whole copies too.
+constexpr int mm_hi_copies(int fmt, int round, int rows) {
+  return (rows * (round / 8 * hi_bits(fmt)) / 16 + 63) / 64;
+}
+constexpr int mm_cslot(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int round = mm_round(fmt, mt, wk, g, rd);
+  const int rows = 16 * nt * wr;
+  const int codes = rows * (mm_byte(fmt) ? round : round / 2) + mm_hi_copies(fmt, round, rows) * 1024;
+  if (fmt == FMT_F8) return codes;
+  const int srd = is_asym(fmt) ? 2 * (round / SUPERBLOCK) : round / g / 2;  // dwords per row
+  const int region = (rows * srd + 63) / 64 * 256;
+  return codes + (is_asym(fmt) ? 2 : 1) * region;
+}
+// copy instructions per round: x row segments; code pieces and scale dwords
+constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd) {
+  const int round = mm_round(fmt, mt, wk, g, rd);
+  const int seg = round * 2 < 1024 ? round * 2 : 1024;
+  return (16 * mt) * (round * 2 / seg);
+}
+constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int round = mm_round(fmt, mt, wk, g, rd);
+  const int rows = 16 * nt * wr;
+  const int cc = (rows * (mm_byte(fmt) ? round : round / 2) / 16 + 63) / 64;
+  const int sd = fmt == FMT_F8 ? 0
+                 : is_asym(fmt) ? rows * (round / SUPERBLOCK) * 2 : rows * (round / g) / 2;
+  return cc + mm_hi_copies(fmt, round, rows) + (is_asym(fmt) ? 2 : 1) * ((sd + 63) / 64);
+}
+// Rounds copied ahead.  Code slots to keep MM_CODE_AHEAD bytes in flight
+// come first (at least 2 rounds), then as many x rounds as fit (at most
+// MM_MAX_XDEPTH), then the rest of the LDS goes to more code rounds; each
+// copying wave's pending copies must fit its counter (63).
+constexpr int mm_xdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int xs = mm_xslot(fmt, mt, g, wk, rd), cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
+  const int xpp = (mm_xcopies(fmt, mt, g, wk, rd) + MM_XP - 1) / MM_XP;
+  int dcmin = (MM_CODE_AHEAD + cs - 1) / cs;
+  dcmin = dcmin < 2 ? 2 : (dcmin > MM_MAX_CDEPTH ? MM_MAX_CDEPTH : dcmin);
+  int d = MM_MAX_XDEPTH;
+  while (d > 0 && ((d + 1) * xs + (dcmin + 1) * cs > LDS_LIMIT || (d - 1) * xpp > 63)) d--;
+  return d;
+}
+constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+  const int left = LDS_LIMIT - (mm_xdepth(fmt, mt, g, wr, wk, nt, rd) + 1) *
+                                   mm_xslot(fmt, mt, g, wk, rd);
+  const int cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
+  const int cpp = (mm_ccopies(fmt, mt, g, wr, wk, nt, rd) + MM_CP - 1) / MM_CP;
+  int d = MM_MAX_CDEPTH;
+  while (d > 0 && ((d + 1) * cs > left || (d - 1) * cpp > 63)) d--;
+  return d;
+}
+
+// Compile-time shape of one kernel instance.
+template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_>
+struct Mm {
+  static constexpr int FMT = FMT_, MT = MT_, NT = NT_, WR = WR_, WK = WK_, G = G_, RD = RD_;
+  static constexpr int W = WR * WK;                 // multiplying waves
+  static constexpr int THREADS = 64 * (W + MM_XP + MM_CP);
+  static constexpr int KC = mm_kc(FMT, MT, WK, G, RD);  // k per wave chunk
+  static constexpr int ROUND = WK * KC;             // k per round
+  static constexpr int DX = mm_xdepth(FMT, MT, G, WR, WK, NT, RD);  // x rounds ahead
+  static constexpr int DC = mm_cdepth(FMT, MT, G, WR, WK, NT, RD);  // code rounds ahead
+  static constexpr int MP = 16 * MT;                // padded activation rows
+  static constexpr int TR = 16 * NT;                // rows per wave
+  static constexpr int ROWS = TR * WR;              // rows per workgroup
+  static constexpr int XSTR = ROUND + 8;            // halves per LDS row of x
+  static constexpr int GPC = KC / G;                // groups per chunk
+  static constexpr int DPG = mm_byte(FMT) ? G / 16 : G / 32;  // dwords per lane per group
+  static constexpr int BPL = DPG * 4;               // code bytes per lane per group
+  static constexpr int GB = mm_byte(FMT) ? G : G / 2;  // code bytes per group of a row
+  static constexpr int RS = mm_byte(FMT) ? ROUND : ROUND / 2;  // code bytes per row and round
+  static constexpr int PR = RS / 16;                // 16-byte code pieces per row and round
+  // piece swizzle: row n's piece p sits at n*PR + (p ^ (n & SWZ)); 16 rows of
+  // a fragment read then start in 16 (PR >= 16) or 8 different bank groups
+  static constexpr int SWZ = PR >= 16 ? 15 : 7;
+  static constexpr int NSB = ROUND / SUPERBLOCK;    // superblocks per round (asym)
+  // scale dwords per row and round: sym, the round's binary16 scales; asym,
+  // per kind (scale records, zero records) two dwords per superblock
+  static constexpr int SRD = (FMT == FMT_F8) ? 0 : is_asym(FMT) ? 2 * NSB : ROUND / G / 2;
+  // 5-/6-bit codes: the high-bit plane of the round, HRS bytes per row
+  static constexpr int HB = hi_bits(FMT);
+  static constexpr int HRS = ROUND / 8 * HB;
+  static constexpr int HPR = HRS / 16;              // 16-byte pieces per row and round
+  // LDS: x ring (DX+1 slots), then code ring (DC+1 slots)
+  static constexpr int XSLOT = mm_xslot(FMT, MT, G, WK, RD);
+  static constexpr int CSLOT = mm_cslot(FMT, MT, G, WR, WK, NT, RD);
+  static constexpr int CRING = (DX + 1) * XSLOT;    // byte offset of the code ring
+  static constexpr int C_OFF = 0;                   // within a code slot
+  static constexpr int HN = mm_hi_copies(FMT, ROUND, ROWS);  // high-bit copies
+  static constexpr int H_OFF = ROWS * RS;           // high-bit plane (rows of HRS bytes)
+  static constexpr int S_OFF = H_OFF + HN * 1024;
+  static constexpr int Z_OFF = S_OFF + ((ROWS * SRD + 63) / 64) * 256;  // asym zero records
+  // copies of one round
+  static constexpr int SEG = ROUND * 2 < 1024 ? ROUND * 2 : 1024;  // x bytes per copy
+  static constexpr int SEG_LANES = SEG / 16;
+  static constexpr int SEGS_PER_ROW = ROUND * 2 / SEG;
+  static constexpr int XN = MP * SEGS_PER_ROW;
+  static constexpr int CPIECES = ROWS * PR;
+  static constexpr int CN = (CPIECES + 63) / 64;
+  static constexpr int SDK = ROWS * SRD;            // scale dwords per kind
+  static constexpr int SNK = (SDK + 63) / 64;
+  static constexpr int SN = (is_asym(FMT) ? 2 : 1) * SNK;
+  static constexpr int CHN = CN + HN;                // code and high-bit copies
+  static constexpr int COPIES = XN + CHN + SN;
+  static constexpr int XPP = (XN + MM_XP - 1) / MM_XP;         // per x-copying wave
+  static constexpr int CPP = (CHN + SN + MM_CP - 1) / MM_CP;   // per code-copying wave
+  static constexpr int RED = (WK > 1) ? W * 64 * NT * MT * 4 : 0;  // floats
+  static constexpr int LDS_BYTES = CRING + (DC + 1) * CSLOT;
+  // structural conditions (the host's plan_fits checks the same)
+  static constexpr bool VALID =
+      GPC >= 1 && GPC <= 8 && KC % G == 0 &&
+      (!is_asym(FMT) || (SUPERBLOCK % KC == 0 && ROUND % SUPERBLOCK == 0)) &&
+      (is_asym(FMT) || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
+      SEG_LANES <= 64 && ROUND * 2 % SEG == 0;
+  // accumulator tiles per wave the register file holds without spilling:
+  // 12 waves per workgroup leave 168 registers a lane
+  static constexpr bool REGS = NT * MT <= (THREADS > 512 ? 4 : 8);
+  static constexpr bool FITS = VALID && REGS && DX >= 1 && DC >= 1 &&
+                               LDS_BYTES <= LDS_LIMIT && RED * 4 <= LDS_LIMIT;
+  static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
+                          CHN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
+                "copy counts");
+  static_assert(CPIECES % 64 == 0, "code rows are whole copies");
+  static_assert(!FITS || ((DX - 1) * XPP <= 63 && (DC - 1) * CPP <= 63),
+                "wait counts fit the counter");
+};
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean "do not wait").
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most k*STEP vector loads of this wave are pending, k in
+// [0, KMAX] (a switch: the counter takes an immediate).
+template <int STEP, int KMAX>
+__device__ __forceinline__ void wait_vm_rounds(int k) {
+  if constexpr (KMAX > 0) {
+    if (k >= KMAX) {
+      wait_vm<KMAX * STEP>();
+      return;
+    }
+    wait_vm_rounds<STEP, KMAX - 1>(k);
+  } else {
+    wait_vm<0>();
+  }
+}
+
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                   0);
+}
+__device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0,
+                                   0);
+}
+
+// Copy c of a round, c in [0, COPIES): x row segments first (rows >= M
+// repeat row M-1; they only feed outputs that are never stored), then code
+// pieces (row n's 16-byte piece p stored at position n*PR + (p ^ (n & SWZ)), so
+// that the 16 rows a fragment read touches spread over the banks), then, for
+// 5-/6-bit codes, high-bit pieces (row n's piece p at n*HPR + p), then scale
+// dwords (row n's dword d at n*SRD + d; asym: scale records, then zero
+// records).  The lanes past the last row repeat it into the region's padding.
+// copy_off gives this lane's byte offset from the copy's base,
+// which does not change from round to round; copy_src/copy_dst the uniform
+// parts.
+template <class S>
+__device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, int lane) {
+  if (c < S::XN) {
+    const int m = c / S::SEGS_PER_ROW, seg = c % S::SEGS_PER_ROW;
+    const int mr = m < M ? m : M - 1;
+    return ((u32)mr * (u32)K + (u32)(seg * (S::SEG / 2) + lane * 8)) * 2u;
+  } else if (c < S::XN + S::CN) {
+    const int pos = (c - S::XN) * 64 + lane;  // piece position in the slot
+    const int n = pos / S::PR, sp = pos % S::PR;
+    const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
+    const u32 row_bytes = mm_byte(S::FMT) ? (u32)K : (u32)K / 2;
+    return (u32)row * row_bytes + (u32)(sp ^ (n & S::SWZ)) * 16u;
+  } else if (c < S::XN + S::CHN) {
+    // high-bit pieces: the round's HRS bytes of a row, K/8*HB bytes apart
+    constexpr int HPR1 = S::HPR > 0 ? S::HPR : 1;
+    const int pos = (c - S::XN - S::CN) * 64 + lane;
+    const int n = pos / HPR1, hp = pos % HPR1;
+    const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
+    return (u32)row * (u32)(K / 8 * S::HB) + (u32)hp * 16u;
+  } else {
+    // scale copies (none for FP8: SNK is 0 and no copy index reaches here)
+    const int j = (c - S::XN - S::CHN) % (S::SNK > 0 ? S::SNK : 1);
+    const int q = j * 64 + lane;
+    constexpr int SRD1 = S::SRD > 0 ? S::SRD : 1;
+    const int n = q / SRD1, dw = q % SRD1;
+    const int row = min(row0 + min(n, S::ROWS - 1), N - 1);
+    if constexpr (is_asym(S::FMT))
+      return ((u32)row * (u32)(K / SUPERBLOCK) * 2u + (u32)dw) * 4u;
+    else  // K / G is even (host check): a row's scales start on a dword
+      return ((u32)row * (u32)(K / S::G) / 2u + (u32)dw) * 4u;
+  }
+}
+
+// Source base of copy c in round t (k0: the round's first k).
+template <class S>
+__device__ __forceinline__ const char* copy_src(int c, int k0, const _Float16* x,
+                                                const uint8_t* qw, const void* scales,
+                                                const void* zeros, int N, int K) {
+  if (c < S::XN) return reinterpret_cast<const char*>(x) + (size_t)k0 * 2;
+  if (c < S::XN + S::CN)
+    return reinterpret_cast<const char*>(qw) + (size_t)(mm_byte(S::FMT) ? k0 : k0 / 2);
+  if (c < S::XN + S::CHN)  // the high-bit plane follows every row's nibbles
+    return reinterpret_cast<const char*>(qw) + (size_t)N * (K / 2) + (size_t)(k0 / 8) * S::HB;
+  if constexpr (is_asym(S::FMT)) {
+    const bool zr = (c - S::XN - S::CHN) >= S::SNK;
+    return reinterpret_cast<const char*>(zr ? zeros : scales) + (size_t)(k0 / SUPERBLOCK) * 8;
+  } else {
+    return reinterpret_cast<const char*>(scales) + (size_t)(k0 / S::G) * 2;
+  }
+}
+
+// Destination offset of copy c within its slot.
+template <class S>
+__device__ __forceinline__ int copy_dst(int c) {
+  if (c < S::XN) {
+    const int m = c / S::SEGS_PER_ROW, seg = c % S::SEGS_PER_ROW;
+    return (m * S::XSTR + seg * (S::SEG / 2)) * 2;
+  }
+  if (c < S::XN + S::CN) return S::C_OFF + (c - S::XN) * 1024;
+  if (c < S::XN + S::CHN) return S::H_OFF + (c - S::XN - S::CN) * 1024;
+  const int i = c - S::XN - S::CHN;
+  return ((is_asym(S::FMT) && i >= S::SNK) ? S::Z_OFF : S::S_OFF) +
+         (i % (S::SNK > 0 ? S::SNK : 1)) * 256;
+}
+
+// Multiply one chunk into acc from the LDS x slot `xsl` and code slot `sl`:
+// x of the chunk at column kx of the x tile, code bytes at cb0 of the rows'
+// round segments,
+// the chunk's groups j0 .. j0+GPC-1 of the round's scales.  kb is the
+// chunk's first k.
+template <class S>
+__device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
+                                         const char* __restrict__ sl, int kx, int cb0, int j0,
+                                         int kb, int wr, int h, int col,
+                                         f4 (&acc)[S::NT][S::MT]) {
+  constexpr int FMT = S::FMT, G = S::G, MT = S::MT, NT = S::NT, DPG = S::DPG;
+  constexpr int KS = MfmaT<FMT>::KS;
+  constexpr int QPL = G / 4;  // k per lane group per group
+  const _Float16* xb = reinterpret_cast<const _Float16*>(xsl);
+#pragma unroll
+  for (int g = 0; g < S::GPC; g++) {
+    // this lane's codes: row n, bytes [cb0 + g*GB + h*BPL, +BPL) of the row
+    u32 code[NT][DPG];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int n = wr * S::TR + nt * 16 + col;
+      const int byte = cb0 + g * S::GB + h * S::BPL;
+      const char* src =
+          sl + S::C_OFF + (n * S::PR + ((byte / 16) ^ (n & S::SWZ))) * 16 + byte % 16;
+      if constexpr (S::BPL == 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        code[nt][0] = v.x; code[nt][1] = v.y; code[nt][2] = v.z; code[nt][3] = v.w;
+      } else if constexpr (S::BPL == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+        code[nt][0] = v.x; code[nt][1] = v.y;
+      } else {
+        code[nt][0] = *reinterpret_cast<const u32*>(src);
+      }
+    }
+    // 5-/6-bit codes: the high-bit dwords of the row's 32-code chunk
+    u32 hw[NT][2];
+    if constexpr (S::HB > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        const int n = wr * S::TR + nt * 16 + col;
+        const u32* hp = reinterpret_cast<const u32*>(sl + S::H_OFF + n * S::HRS +
+                                                     (cb0 / 16 + g) * 4 * S::HB);
+        hw[nt][0] = hp[0];
+        hw[nt][1] = S::HB == 2 ? hp[1] : 0u;
+      }
+    }
+    f4 P[NT][MT];
+    // A fragments of every K-step of the group and every M-tile
+    u32 a[DPG][MT][4];
+#pragma unroll
+    for (int s = 0; s < DPG; s++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const _Float16* src =
+            xb + (mt * 16 + col) * S::XSTR + kx + g * G + h * QPL + s * (KS / 4);
+        if constexpr (mm_byte(FMT)) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+          a[s][mt][0] = v.x; a[s][mt][1] = v.y;
+        } else {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+          a[s][mt][0] = v.x; a[s][mt][1] = v.y; a[s][mt][2] = v.z; a[s][mt][3] = v.w;
+        }
+      }
+#pragma unroll
+    for (int s = 0; s < DPG; s++) {
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        u32 b[4];
+        const u32 d = code[nt][s];
+        if constexpr (mm_byte(FMT)) {
+          h2 q[2];
+          if constexpr (FMT == FMT_F8) unpack_fp8(d, q);
+          else unpack8(d, q);
+          b[0] = as_u32(q[0]); b[1] = as_u32(q[1]);
+        } else if constexpr (S::HB > 0) {
+          // this lane's nibble dword is dword h of the group's 32-code chunk
+          u32 hlo, hhi;
+          hi_words<S::HB>(hw[nt], h, &hlo, &hhi);
+          h2 q[4];
+          unpack4h<S::HB>(d, hlo, hhi, q);
+          // pairs (q0,q4) (q1,q5) (q2,q6) (q3,q7) -> k order (q0,q1) .. (q6,q7)
+          const u32 p0 = as_u32(q[0]), p1 = as_u32(q[1]), p2 = as_u32(q[2]), p3 = as_u32(q[3]);
+          b[0] = __builtin_amdgcn_perm(p1, p0, 0x05040100u);
+          b[1] = __builtin_amdgcn_perm(p3, p2, 0x05040100u);
+          b[2] = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
+          b[3] = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
+        } else {
+          h2 q[4];
+          unpack4n<FMT == FMT_S4>(d, q);
+          b[0] = as_u32(q[0]); b[1] = as_u32(q[1]);
+          b[2] = as_u32(q[2]); b[3] = as_u32(q[3]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          // FP8: no group scale, so the products accumulate straight into acc
+          const f4 c0 = (FMT == FMT_F8) ? acc[nt][mt] : f4{0, 0, 0, 0};
+          P[nt][mt] = mfma_step<FMT>(a[s][mt], b, s == 0 ? c0 : P[nt][mt]);
+        }
+      }
+    }
+    // asymmetric: the group sums of x, in the layout of P, from one more MFMA
+    // against codes that are all 1 (a group is one K-step)
+    f4 xg[MT];
+    if constexpr (is_asym(FMT)) {
+      const u32 one2 = 0x3C003C00u;  // binary16 (1, 1)
+      const u32 ones[4] = {one2, one2, one2, one2};
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) xg[mt] = mfma_step<FMT>(a[0][mt], ones, f4{0, 0, 0, 0});
+    }
+    // group epilogue in binary32
+#pragma unroll
+    for (int nt = 0; nt < NT && FMT == FMT_F8; nt++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[nt][mt] = P[nt][mt];
+#pragma unroll
+    for (int nt = 0; nt < NT && FMT != FMT_F8; nt++) {
+      const int n = wr * S::TR + nt * 16 + col;
+      float sc, t = 0.0f;
+      if constexpr (is_asym(FMT)) {
+        const int kin = (kb % S::ROUND) + g * G;  // k within the round
+        const int sb = kin / SUPERBLOCK, j = (kin % SUPERBLOCK) / SB_GROUP;
+        const u32* sr = reinterpret_cast<const u32*>(sl + S::S_OFF) + n * S::SRD + 2 * sb;
+        const u32* zr = reinterpret_cast<const u32*>(sl + S::Z_OFF) + n * S::SRD + 2 * sb;
+        sc = record_value(u32x2{sr[0], sr[1]}, j);
+        t = record_value(u32x2{zr[0], zr[1]}, j);
+      } else {
+        const int j = j0 + g;  // group within the round
+        const u32 pair = reinterpret_cast<const u32*>(sl + S::S_OFF)[n * S::SRD + j / 2];
+        sc = (j & 1) ? half_hi(pair) : half_lo(pair);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float v = __builtin_fmaf(sc, P[nt][mt][i], acc[nt][mt][i]);
+          if constexpr (is_asym(FMT)) v = __builtin_fmaf(-t, xg[mt][i], v);
+          acc[nt][mt][i] = v;
+        }
+      }
+    }
+    // keep the scheduler from hoisting later groups' LDS reads into this one
+    // (it would hold every group's fragments in registers at once)
+    if constexpr (MT * NT >= 4) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The copying waves.  x waves take the round's x copies p, p+XP, ...; the
+// code wave takes its code and scale copies.  Each group runs its own number
+// of rounds ahead of the multiplying waves (x: DX, codes: DC); a wave's
+// copies complete in issue order, so before the barrier of round r it waits
+// until only rounds r+1 .. r+ahead-1 may be in flight.  After the barrier
+// the slots of round r-1 are free and take round r+ahead.  (A copy index
+// past the end repeats the last copy: every wave issues the same number.)
+template <class S, bool XW>
+__device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
+                                            const uint8_t* qw, const void* scales,
+                                            const void* zeros, int M, int K, int N, int row0,
+                                            int k_begin, int nrounds, int lane) {
+  constexpr int NC = XW ? S::XPP : S::CPP;
+  constexpr int AHEAD = XW ? S::DX : S::DC;
+  static_assert(MM_CP == 1, "the code wave's copies are compile-time");
+  // copy index of position i (uniform)
+  auto cidx = [&](int i) {
+    return XW ? min(i * MM_XP + p, S::XN - 1) : S::XN + min(i, S::CHN + S::SN - 1);
+  };
+  u32 off[NC];
+#pragma unroll
+  for (int i = 0; i < NC; i++) off[i] = copy_off<S>(cidx(i), M, K, N, row0, lane);
+  auto issue = [&](int t) {
+    char* slot = XW ? lds + (t % (S::DX + 1)) * S::XSLOT
+                    : lds + S::CRING + (t % (S::DC + 1)) * S::CSLOT;
+    const int k0 = k_begin + t * S::ROUND;
+#pragma unroll
+    for (int i = 0; i < NC; i++) {
+      const int c = cidx(i);
+      const char* src = copy_src<S>(c, k0, x, qw, scales, zeros, N, K) + off[i];
+      char* dst = slot + copy_dst<S>(c);
+      if constexpr (XW) {
+        // every x copy of a round has the same lane count
+        if (S::SEG_LANES == 64 || lane < S::SEG_LANES) lds_copy16(src, dst);
+      } else {
+        // Code, high-bit and scale copies are whole-wave instructions with no
+        // lane predicate: the code rows are whole copies, the other regions
+        // are padded to whole copies.  (Predicated copies of different lane
+        // counts in one unrolled sequence were once merged by the compiler
+        // into a block that issued some of them under another copy's mask.)
+        const int cc = S::XN + (i < S::CHN + S::SN ? i : S::CHN + S::SN - 1);
+        if (cc >= S::XN + S::CHN) lds_copy4(src, dst);
+        else lds_copy16(src, dst);
+      }
+    }
+  };
+#pragma unroll 1
+  for (int t = 0; t < AHEAD; t++)
+    if (t < nrounds) issue(t);
+#pragma unroll 1
+  for (int r = 0; r < nrounds; r++) {
+    wait_vm_rounds<NC, AHEAD - 1>(min(AHEAD - 1, nrounds - 1 - r));
+    __builtin_amdgcn_s_barrier();
+    if (r + AHEAD < nrounds) issue(r + AHEAD);
+  }
+}
+
+// Problems of one launch (they share the format, M, K and the group size):
+// workgroups [block_begin, next block_begin) along x belong to entry i.
+struct MmEntry {
+  const uint8_t* qw;
+  const void* sc;
+  const void* zr;
+  const _Float16* x;
+  float* out;  // y, or the partial-sum workspace when K is split
+  int N;
+  int block_begin;
+};
+struct MmBatch {
+  MmEntry e[MM_BATCH];
+  int count;
+};
+
+template <class S>
+__global__ void __launch_bounds__(S::THREADS)
+k_mm(const MmBatch bt, int M, int K, int kr) {
+  constexpr int NT = S::NT, MT = S::MT;
+  static_assert(S::FITS, "LDS budget and prefetch depth");
+  constexpr int LDS_BYTES = S::LDS_BYTES > S::RED * 4 ? S::LDS_BYTES : S::RED * 4;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+
+  // this workgroup's problem (uniform scan of the table)
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < MM_BATCH; i++)
+    if (i < bt.count && (int)blockIdx.x >= bt.e[i].block_begin) pi = i;
+  const MmEntry& e = bt.e[pi];
+  const uint8_t* __restrict__ qw = e.qw;
+  const void* __restrict__ scales = e.sc;
+  const void* __restrict__ zeros = e.zr;
+  const _Float16* __restrict__ x = e.x;
+  const int N = e.N;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.y;
+  const int k_begin = split * kr;
+  // y itself, or this K-range's slice of the partial-sum workspace
+  float* __restrict__ y = e.out + (size_t)split * M * N;
+  // FP8: the matrix scale multiplies every finished sum (or partial sum)
+  const float mscale = (S::FMT == FMT_F8) ? *static_cast<const float*>(scales) : 1.0f;
+  const int nrounds = kr / S::ROUND;
+  const int row0 = ((int)blockIdx.x - e.block_begin) * S::ROWS;
+
+  if (wave >= S::W) {
+    if (wave < S::W + MM_XP)
+      copy_rounds<S, true>(wave - S::W, lds, x, qw, scales, zeros, M, K, N, row0, k_begin,
+                           nrounds, lane);
+    else
+      copy_rounds<S, false>(wave - S::W - MM_XP, lds, x, qw, scales, zeros, M, K, N, row0,
+                            k_begin, nrounds, lane);
+  } else {
+    // ---- multiplying wave: row group wr, K-slice wk
+    const int wk = wave % S::WK;
+    const int wr = wave / S::WK;
+    const int h = lane >> 4;
+    const int col = lane & 15;
+    f4 acc[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[nt][mt] = f4{0, 0, 0, 0};
+    const int kx = wk * S::KC;  // chunk within the round
+    const int cb0 = mm_byte(S::FMT) ? kx : kx / 2;
+    const int j0 = kx / S::G;
+    for (int r = 0; r < nrounds; r++) {
+      __builtin_amdgcn_s_barrier();  // round r is in LDS
+      mm_chunk<S>(lds + (r % (S::DX + 1)) * S::XSLOT,
+                  lds + S::CRING + (r % (S::DC + 1)) * S::CSLOT, kx, cb0, j0,
+                  k_begin + r * S::ROUND + kx, wr, h, col, acc);
+    }
+    if constexpr (S::WK > 1) {
+      __syncthreads();  // every wave is done with the slots
+      float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            red[((wave * NT + nt) * MT + mt) * 256 + i * 64 + lane] = acc[nt][mt][i];
+      __syncthreads();
+      if (wk != 0) return;
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            float v = acc[nt][mt][i];
+#pragma unroll
+            for (int q = 1; q < S::WK; q++)
+              v += red[(((wave + q) * NT + nt) * MT + mt) * 256 + i * 64 + lane];
+            acc[nt][mt][i] = v;
+          }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int n = row0 + wr * S::TR + nt * 16 + col;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = mt * 16 + 4 * h + i;
+          if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i] * mscale;
+        }
+    }
+    return;
+  }
+  // copying waves join the reduction's two barriers
+  if constexpr (S::WK > 1) {
+    __syncthreads();
+    __syncthreads();
+  }
+}
+
+// Workgroup arrangements: row groups x K-slices x 16-row tiles per wave, and
+// the round size (rd = 2: half the default round).
+struct Plan {
+  int wr, wk, nt, rd;
+};
+static constexpr Plan kPlans[] = {
+    {1, 4, 1, 1},  // 0: 16 rows, 4 K-slices
+    {1, 8, 1, 1},  // 1: 16 rows, 8 K-slices
+    {4, 1, 1, 1},  // 2: 64 rows, whole chunks per wave
+    {2, 4, 1, 1},  // 3: 32 rows, 4 K-slices
+    {2, 2, 1, 1},  // 4: 32 rows, 2 K-slices
+    {4, 2, 1, 1},  // 5: 64 rows, 2 K-slices
+    {1, 4, 1, 2},  // 6: as 0, half rounds
+    {4, 2, 1, 2},  // 7: as 5, half rounds
+    {2, 4, 1, 2},  // 8: as 3, half rounds
+    {4, 1, 1, 2},  // 9: as 2, half rounds
+    // two 16-row tiles per wave: each A fragment read from LDS feeds two MFMAs
+    {2, 2, 2, 1},  // 10: 64 rows, 2 K-slices
+    {2, 4, 2, 1},  // 11: 64 rows, 4 K-slices
+    {1, 8, 2, 1},  // 12: 32 rows, 8 K-slices
+    {1, 4, 2, 1},  // 13: 32 rows, 4 K-slices
+    {4, 2, 2, 1},  // 14: 128 rows, 2 K-slices
+    // three row groups: 48-row workgroups (12288 rows -> 256 workgroups)
+    {3, 2, 1, 1},  // 15: 48 rows, 2 K-slices
+    {3, 2, 1, 2},  // 16: as 15, half rounds
+    {3, 4, 1, 1},  // 17: 48 rows, 4 K-slices
+};
+constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
+
+// Adds the split-K partial sums into y (rq_gemm.hip).
+void launch_split_reduce(const float* ws, float* y, size_t count, int splits, hipStream_t s);
+
+// One launch over p[0..count), count <= MM_BATCH; K is split (c.splits > 1,
+// partial sums in ws) only for a single problem.
+template <class S>
+void launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
+                     hipStream_t s) {
+  if constexpr (!S::FITS) {
+    return;  // never chosen (plan_ok)
+  } else {
+  MmBatch bt{};
+  int blocks = 0;
+  for (int i = 0; i < count; i++) {
+    bt.e[i] = MmEntry{static_cast<const uint8_t*>(p[i]->qweight), p[i]->scales, p[i]->zeros,
+                      static_cast<const _Float16*>(p[i]->x), c.splits > 1 ? ws : p[i]->y,
+                      p[i]->N, blocks};
+    blocks += (p[i]->N + S::ROWS - 1) / S::ROWS;
+  }
+  bt.count = count;
+  const int M = p[0]->M, K = p[0]->K;
+  hipLaunchKernelGGL((k_mm<S>), dim3(blocks, c.splits), dim3(S::THREADS), 0, s, bt, M, K,
+                     K / c.splits);
+  if (c.splits > 1) launch_split_reduce(ws, p[0]->y, (size_t)M * p[0]->N, c.splits, s);
+  }
+}
+
+template <int FMT, int MT, int G>
+void launch_plan(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                        hipStream_t s) {
+  switch (c.plan) {
+    case 0: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 1>>(p, n, c, ws, s);
+    case 1: return launch_s<Mm<FMT, MT, 1, 1, 8, G, 1>>(p, n, c, ws, s);
+    case 2: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 1>>(p, n, c, ws, s);
+    case 3: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 1>>(p, n, c, ws, s);
+    case 4: return launch_s<Mm<FMT, MT, 1, 2, 2, G, 1>>(p, n, c, ws, s);
+    case 5: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 1>>(p, n, c, ws, s);
+    case 6: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 2>>(p, n, c, ws, s);
+    case 7: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 2>>(p, n, c, ws, s);
+    case 8: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 2>>(p, n, c, ws, s);
+    case 9: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, n, c, ws, s);
+    case 10: return launch_s<Mm<FMT, MT, 2, 2, 2, G, 1>>(p, n, c, ws, s);
+    case 11: return launch_s<Mm<FMT, MT, 2, 2, 4, G, 1>>(p, n, c, ws, s);
+    case 12: return launch_s<Mm<FMT, MT, 2, 1, 8, G, 1>>(p, n, c, ws, s);
+    case 13: return launch_s<Mm<FMT, MT, 2, 1, 4, G, 1>>(p, n, c, ws, s);
+    case 14: return launch_s<Mm<FMT, MT, 2, 4, 2, G, 1>>(p, n, c, ws, s);
+    case 15: return launch_s<Mm<FMT, MT, 1, 3, 2, G, 1>>(p, n, c, ws, s);
+    case 16: return launch_s<Mm<FMT, MT, 1, 3, 2, G, 2>>(p, n, c, ws, s);
+    default: return launch_s<Mm<FMT, MT, 1, 3, 4, G, 1>>(p, n, c, ws, s);
+  }
+}
+
+template <int FMT, int MT>
+void launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                         hipStream_t s) {
+  const int g = p[0]->group;
+  if constexpr (FMT == FMT_F8) {
+    return launch_plan<FMT, MT, MM_F8_GROUP>(p, n, c, ws, s);
+  } else if constexpr (FMT == FMT_S8) {
+    if (g == 16) return launch_plan<FMT, MT, 16>(p, n, c, ws, s);
+    if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
+  } else if constexpr (is_asym(FMT)) {
+    return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
+  } else {
+    if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
+    if (g == 64) return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 128>(p, n, c, ws, s);
+  }
+}
+
+template <int FMT>
+void launch_fmt(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                       hipStream_t s) {
+  switch (c.mt) {
+    case 1: return launch_group<FMT, 1>(p, n, c, ws, s);
+    case 2: return launch_group<FMT, 2>(p, n, c, ws, s);
+    case 3: return launch_group<FMT, 3>(p, n, c, ws, s);
+    default: return launch_group<FMT, 4>(p, n, c, ws, s);
+  }
+}
+
+// One per format, each in its own translation unit (rq_gemm_<format>.hip).
+void launch_gemm_fmt_s4(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+void launch_gemm_fmt_s8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+void launch_gemm_fmt_a4(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+void launch_gemm_fmt_a5(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+void launch_gemm_fmt_a6(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+void launch_gemm_fmt_f8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+
+}  // namespace rq
