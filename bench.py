@@ -134,12 +134,14 @@ def main():
 
     flops_per_m = sum(2 * N * K for (_, _, N, K) in mats)
 
-    def timed(kind, M, steps, warmup, graph):
+    def timed(kind, M, steps, warmup, graph, step=None):
         """Seconds per step.  Graph mode prepares the calls on a side stream,
-        captures one step there and replays it."""
+        captures one step there and replays it.  step: (mats, W, X, Y) of
+        another workload (default: this one at M)."""
+        smats, sW, sX, sY = step if step is not None else (mats, W, X[M], Y[M])
         if graph:
             s = torch.cuda.Stream()
-            calls = ST.step_calls(mats, W, X[M], Y[M], kind, stream=s)
+            calls = ST.step_calls(smats, sW, sX, sY, kind, stream=s)
             with torch.cuda.stream(s):
                 for _ in range(warmup):
                     for c in calls:
@@ -152,7 +154,7 @@ def main():
             torch.cuda.synchronize()
             run = g.replay
         else:
-            calls = ST.step_calls(mats, W, X[M], Y[M], kind)
+            calls = ST.step_calls(smats, sW, sX, sY, kind)
 
             def run():
                 for c in calls:
@@ -416,6 +418,33 @@ def main():
             del Wt
         torch.cuda.empty_cache()
 
+    # ---- context: the other workload shapes of the pages, same layer schedule
+    others = None
+    if not args.no_context:
+        others = {}
+        for wkey in ("rwkv7-1.5b", "rwkv7-2.9b"):
+            c2 = S.CONFIGS[wkey]
+            m2 = c2.matrices()
+            for f2 in c2.formats:
+                log(f"workload {wkey} {f2.tag}")
+                W2 = [S.gen_matrix(c2.key, l, mi, N, K, f2, device=dev) for (l, mi, N, K) in m2]
+                wb = sum(f2.weight_bytes(N, K) for (_, _, N, K) in m2)
+                fl = sum(2 * N * K for (_, _, N, K) in m2)
+                for M2 in c2.ms:
+                    X2 = [S.gen_x(c2, l, mi, M2, K, device=dev) for (l, mi, N, K) in m2]
+                    Y2 = [torch.empty((M2, N), dtype=torch.float32, device=dev)
+                          for (_, _, N, _) in m2]
+                    sec, ncalls = timed("layer", M2, args.m32_steps, 2, args.graph,
+                                        step=(m2, W2, X2, Y2))
+                    nb = wb + sum(2 * M2 * K + 4 * M2 * N for (_, _, N, K) in m2)
+                    others[f"{wkey} {f2.tag} M={M2}"] = {
+                        "layers": c2.layers, "width": c2.width, "launch_calls": ncalls,
+                        "ms_per_step": round(sec * 1e3, 4), "GBps": round(nb / sec / 1e9, 1),
+                        "tflops": round(M2 * fl / sec / 1e12, 2)}
+                    del X2, Y2
+                del W2
+                torch.cuda.empty_cache()
+
     # ---- CPU oracle on a bounded sample of the same step --------------------
     cpu = cpu_threads = None
     if not args.no_cpu_baseline:
@@ -483,6 +512,7 @@ def main():
         "cpu_oracle_threads": cpu_threads,
         "vs_fp16_dense": dense,
         "tp8_shard_shapes_m1": tp8,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
 
