@@ -197,6 +197,61 @@ rq_status check_product(const void* qweight, const void* scales, const void* zer
                       layout, M);
 }
 
+enum Kernel { KERN_VECTOR, KERN_DECODE_MFMA, KERN_SMALLM_MFMA };
+
+// The kernel rq_gemv and rq_gemv_batched use for M activation rows (N: rows of
+// the launch).  Measured on MI355X, weights cold in HBM, int4 g64 / int8 g16 /
+// asym4 / FP8 / 5- and 6-bit codes at widths 2048..4096 and K up to 16384:
+//  * M >= 5: the small-batch matrix-core kernel (M padded to 16) beats the
+//    vector-unit passes of eight rows by 1.35x to 11x (int4 4096x4096 M = 8:
+//    11.5 -> 5.8 us; 2560x10240 asymmetric M = 8: 65.7 -> 13.1 us).
+//  * M = 3..4: the same kernel for int4, int8 and FP8 (int8 8192x2048 M = 4:
+//    8.6 us on the decode kernel -> 7.6 us); the decode kernel for asymmetric
+//    4-bit (2560x10240: 11.7 vs 12.8 us); the vector-unit kernel for 5- and
+//    6-bit codes (16384x4096: 20.8 vs 23.0 us).
+//  * M <= 2: the vector-unit kernel, unless none of its tuned launch shapes
+//    splits the row (the generic kernel: FP8 4096x16384 at M = 2 takes
+//    52.1 us there, 18.0 us on the small-batch kernel).  Then the decode
+//    kernel for int4 and asymmetric 4-bit (2048x65536 at M = 1: 32.3 and
+//    43.2 us, against 36.4 and 58.7 us on the small-batch kernel), the
+//    small-batch kernel otherwise (int8 4096x32768 at M = 1: 37.0 against
+//    42.9 us).
+// *gc receives the vector-unit launch shape when that kernel is chosen.  The
+// common decode case (M <= 2, a tuned vector-unit shape) returns after one
+// launch-shape search, so stream-mode callers pay little host time per call.
+Kernel pick_kernel(int fmt, int M, int N, int K, int group, rq::GemvCfg* gc) {
+  const int t = rq::tuning().gemv_kernel;
+  if (t == 1 || (t == 0 && M <= 2)) {
+    *gc = rq::choose_gemv(fmt, M, N, K);
+    if (t == 1 || gc->lpr != 0) return KERN_VECTOR;
+  }
+  const bool mv = rq::mv_supports(fmt, M, K, group);
+  const bool mm = rq::gemm_supports(fmt, M, K, group);
+  Kernel k;
+  if (t == 2) {
+    k = mv ? KERN_DECODE_MFMA : KERN_VECTOR;
+  } else if (t == 3) {
+    k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
+  } else if (M >= 5) {
+    k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
+  } else if (M >= 3) {
+    if (fmt == FMT_A4 && mv) {
+      k = KERN_DECODE_MFMA;
+    } else if (fmt == FMT_A5 || fmt == FMT_A6) {
+      *gc = rq::choose_gemv(fmt, M, N, K);
+      if (gc->lpr != 0) return KERN_VECTOR;
+      k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
+    } else {
+      k = mm ? KERN_SMALLM_MFMA : (mv ? KERN_DECODE_MFMA : KERN_VECTOR);
+    }
+  } else {  // M <= 2 on the generic vector-unit kernel
+    if (mv && (fmt == FMT_S4 || fmt == FMT_A4 || !mm)) return KERN_DECODE_MFMA;
+    k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
+  }
+  if (k == KERN_VECTOR) *gc = rq::choose_gemv(fmt, M, N, K);
+  return k;
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,13 +288,17 @@ rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
   st = check_device(&dev);
   if (st != RQ_OK) return st;
   rq::Problem p{qweight, scales, zeros, x, y, M, N, K, group, fmt};
+  const rq::Problem* one = &p;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (rq::use_mv(fmt, M, K, group)) {
-    const rq::Problem* one = &p;
-    e = rq::launch_mv_many(&one, 1, s);
-  } else {
-    e = rq::launch_gemv(p, rq::choose_gemv(fmt, M, N, K), s);
+  rq::GemvCfg gc{};
+  switch (pick_kernel(fmt, M, N, K, group, &gc)) {
+    case KERN_DECODE_MFMA: e = rq::launch_mv_many(&one, 1, s); break;
+    case KERN_SMALLM_MFMA:
+      // K kept whole: this entry point never allocates
+      e = rq::launch_gemm(p, rq::choose_gemm(fmt, M, N, K, group, 0, false), nullptr, s);
+      break;
+    default: e = rq::launch_gemv(p, gc, s); break;
   }
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
@@ -292,14 +351,16 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
       }
     }
     hipError_t e;
-    if (M >= rq::MFMA_MIN_M && rq::gemm_supports(fmt, M, pb[i].K, group)) {
-      rq::GemmCfg c = rq::choose_gemm(fmt, M, rows, pb[i].K, group, blocks48);
-      c.splits = 1;
-      e = rq::launch_gemm_many(order, n, c, nullptr, s);
-    } else if (rq::use_mv(fmt, M, pb[i].K, group))
-      e = rq::launch_mv_many(order, n, s);
-    else
-      e = rq::launch_gemv_many(order, n, rq::choose_gemv(fmt, M, rows, pb[i].K), s);
+    rq::GemvCfg gc{};
+    switch (pick_kernel(fmt, M, rows, pb[i].K, group, &gc)) {
+      case KERN_SMALLM_MFMA:
+        e = rq::launch_gemm_many(
+            order, n, rq::choose_gemm(fmt, M, rows, pb[i].K, group, blocks48, false), nullptr,
+            s);
+        break;
+      case KERN_DECODE_MFMA: e = rq::launch_mv_many(order, n, s); break;
+      default: e = rq::launch_gemv_many(order, n, gc, s); break;
+    }
     if (e != hipSuccess) return RQ_ERR_LAUNCH;
   }
   return RQ_OK;

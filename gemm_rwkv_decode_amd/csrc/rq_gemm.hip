@@ -69,7 +69,7 @@ bool gemm_supports(int fmt, int M, int K, int group) {
   return false;
 }
 
-GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48) {
+GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool allow_split) {
   if (fmt == FMT_F8) group = MM_F8_GROUP;
   GemmCfg c{};
   c.mt = (M + 15) / 16;
@@ -90,7 +90,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48) {
   // 45.8 -> 25.0 us (M=64).
   static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
   static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
-  const bool split_k = N < 8192 && (K >= 16384 || c.mt >= 4);
+  const bool split_k = allow_split && N < 8192 && (K >= 16384 || c.mt >= 4);
   const int* order = split_k ? (c.mt == 1 ? split_n_m16 : split_n)
                              : (N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n));
   c.plan = -1;
@@ -118,6 +118,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48) {
   if (split_k && rows == 64 && blocks < 256) want = (256 + blocks - 1) / blocks;
   if (want > 4) want = 4;
   if (tu.gemm_splits) want = tu.gemm_splits;
+  if (!allow_split) want = 1;
   const int nr = K / round_k(fmt, c.mt, group, c.plan);
   if (want > nr) want = nr;
   if (want < 1) want = 1;

@@ -12,7 +12,10 @@ namespace rq {
 // rq_tuning_reload().
 struct Tuning {
   int gemv_lpr, gemv_cpl, gemv_npass, gemm_plan, gemm_splits;
-  int gemv_kernel;  // M <= 4: 0 automatic, 1 vector-unit kernel, 2 matrix-core kernel
+  // kernel of rq_gemv and rq_gemv_batched: 0 automatic, 1 vector-unit
+  // kernel, 2 matrix-core decode kernel (M <= 4), 3 matrix-core small-batch
+  // kernel; 2 and 3 fall back to 1 where they cannot take the shape
+  int gemv_kernel;
 };
 const Tuning& tuning();
 
@@ -48,8 +51,6 @@ hipError_t launch_gemv_many(const Problem* const* p, int count, const GemvCfg& c
 // group and M, up to MV_BATCH per launch.
 constexpr int MV_BATCH = 16;
 bool mv_supports(int fmt, int M, int K, int group);
-// whether rq_gemv / rq_gemv_batched take the matrix-core kernel
-bool use_mv(int fmt, int M, int K, int group);
 hipError_t launch_mv_many(const Problem* const* p, int count, hipStream_t s);
 
 struct GemmCfg {
@@ -58,14 +59,13 @@ struct GemmCfg {
   int splits;  // K split across workgroups
 };
 
-// Smallest M that rq_gemv_batched computes on the matrix-core kernel.
-constexpr int MFMA_MIN_M = 16;
-
 // The matrix-core kernel needs K to be a whole number of its rounds.
 bool gemm_supports(int fmt, int M, int K, int group);
 // N: rows of all problems of the launch; blocks48: their 48-row blocks, each
-// problem rounded up (0: one problem of N rows)
-GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48 = 0);
+// problem rounded up (0: one problem of N rows).  allow_split = false keeps K
+// whole (no workspace) and picks the plan for that.
+GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48 = 0,
+                    bool allow_split = true);
 // ws: float workspace of at least splits*M*N entries (unused when
 // splits == 1).
 hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s);

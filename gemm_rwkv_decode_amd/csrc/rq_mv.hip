@@ -327,17 +327,6 @@ bool mv_supports(int fmt, int M, int K, int group) {
   return mv_lds_bytes(kr, me) <= MV_LDS;
 }
 
-bool use_mv(int fmt, int M, int K, int group) {
-  // Measured on MI355X (int4 g64, width-4096 shapes, weights cold in HBM): at
-  // M = 1 and 2 the vector-unit kernel is faster (at M = 1 by 1.2x to 2x); at
-  // M = 4 this kernel is (1.0x to 4.3x: the vector-unit kernel keeps x in
-  // registers, which caps its waves per row at four activation rows).
-  const int k = tuning().gemv_kernel;
-  if (k == 1) return false;
-  if (k == 0 && M < 3) return false;
-  return mv_supports(fmt, M, K, group);
-}
-
 template <int FMT, int G, int ME>
 static hipError_t launch_mv_t(const Problem* const* p, int count, int M, hipStream_t s) {
   constexpr int B = MV_BATCH;

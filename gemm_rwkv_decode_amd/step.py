@@ -20,8 +20,12 @@ import gemm_rwkv_decode_amd as rq
 # matrix indices within a layer (the head is 6)
 RECEPTANCE, KEY, VALUE, OUTPUT, FFN_KEY, FFN_VALUE, HEAD = range(7)
 
-# smallest M routed to the matrix-core entry point
-MFMA_MIN_M = 16
+# Smallest M a step sends to rq_gemm_smallm, which may split K over
+# workgroups (through its workspace).  From M = 5 on rq_gemv and
+# rq_gemv_batched run the same matrix-core kernel but keep K whole; below it
+# rq_gemv picks the kernel for M (vector units or the decode matrix-core
+# kernel).
+MFMA_MIN_M = 5
 
 KINDS = ("layer", "matrix", "batched")
 
@@ -48,10 +52,10 @@ def step_calls(mats: Sequence[Tuple[int, int, int, int]], W: Sequence, X: Sequen
 
     kinds:
       "layer"   -- per layer: receptance, key and value in one grouped launch
-                   (rq_gemv_batched, which takes the matrix cores from M = 16
-                   on), then output, FFN key, FFN value; the head last.
-      "matrix"  -- one launch per matrix, in order (rq_gemv below M = 16,
-                   rq_gemm_smallm from M = 16 on).
+                   (rq_gemv_batched), then output, FFN key, FFN value; the
+                   head last.
+      "matrix"  -- one launch per matrix, in order (rq_gemv below M = 5,
+                   rq_gemm_smallm from M = 5 on).
       "batched" -- every product through rq_gemv_batched, up to RQ_MAX_BATCH
                    per call, ignoring the order between layers (a bound on
                    what grouping could reach, not a valid decode order).

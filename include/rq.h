@@ -139,10 +139,15 @@ rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
  * the model card reports against fp16, section "Speed").
  *   x: binary16 [M][K] row-major.  y: float [M][N] row-major, overwritten.
  * Each output is within 1e-3 * sum_k |x[m][k] * w[n][k]| of the exact value
- * (fp32 accumulation).  Tuned for M <= 8 (the per-token decode shape): vector
- * units at M <= 2; at M = 3..4 a matrix-core kernel where K holds at least
- * eight of its chunks (8 groups, or one 256-weight superblock, each); larger M
- * is processed on the vector units in passes of up to 8 rows.
+ * (fp32 accumulation).  The kernel is chosen per M, format and shape:
+ * vector units at M <= 2 (matrix cores where K is too long for their tuned
+ * launch shapes); at M = 3..4 a matrix-core decode kernel (where K
+ * holds at least eight of its chunks: 8 groups, or one 256-weight superblock,
+ * each) or, for int4, int8 and FP8, the small-batch matrix-core kernel of
+ * rq_gemm_smallm; from M = 5 on that small-batch kernel (M padded to a
+ * multiple of 16); the vector units, in passes of up to 8 rows, wherever K
+ * does not suit the matrix-core kernels.  The small-batch kernel runs here
+ * with K whole: this entry point never allocates or synchronizes.
  * Shape rules as for rq_dequant, plus 1 <= M <= RQ_MAX_M.
  */
 rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
@@ -152,10 +157,10 @@ rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
 /*
  * rq_gemv_batched -- `count` independent products, issued as few kernel
  * launches as possible: problems with the same K share one launch (up to 16
- * per launch below M = 16, up to 8 from M = 16 on).  Below M = 16 each
- * product is computed as rq_gemv would compute it; from M = 16 on, as
- * rq_gemm_smallm would (matrix cores; K is never split in a grouped launch),
- * except where K does not suit the matrix-core kernel.  This is the grouped
+ * per launch on the vector-unit and decode kernels, up to 8 on the
+ * small-batch matrix-core kernel).  Each group takes the kernel rq_gemv
+ * would take for M, its K and its total row count; K is never split.
+ * This is the grouped
  * form of the decode step's independent projections -- the package page
  * "RWKV-7 FP8 Quantized Inference" (section "Operator Optimization Details")
  * computes the receptance, key and value projections of a layer in a single
@@ -172,7 +177,8 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
  * matrix cores (fp16 MFMA on exact integer or FP8 codes, fp32 per-group
  * scaling; FP8 sums are scaled once by the matrix scale).  Every layout and
  * code width, 5- and 6-bit codes included.
- * Tuned for 16 <= M <= 64 (batched decode); smaller M is padded to 16.
+ * Tuned for 16 <= M <= 64 (batched decode); smaller M is padded to 16, which
+ * still beats the vector units from M = 5 on.
  * For some shapes the K dimension is split across workgroups; the partial sums
  * then pass through a workspace the library allocates once per (device,
  * stream) and keeps until the process ends (a call that needs a larger one

@@ -34,9 +34,11 @@ int rq_probe_empty(void* stream);
 
 /* Re-read the launch-shape override variables (RQ_GEMV_LPR, RQ_GEMV_CPL,
  * RQ_GEMV_NPASS, RQ_GEMM_PLAN (1-based index of a workgroup arrangement of
- * the matrix-core kernel), RQ_GEMM_SPLITS, RQ_GEMV_KERNEL (M <= 4 in rq_gemv
- * and rq_gemv_batched: 1 = vector-unit kernel, 2 = matrix-core decode kernel
- * where K holds at least eight of its chunks); unset or 0 = the library's own
+ * the matrix-core kernel), RQ_GEMM_SPLITS, RQ_GEMV_KERNEL (the kernel of
+ * rq_gemv and rq_gemv_batched at any M: 1 = vector-unit kernel, 2 = matrix-core
+ * decode kernel where M <= 4 and K holds at least eight of its chunks,
+ * 3 = small-batch matrix-core kernel where K suits it; 2 and 3 fall back to
+ * the vector-unit kernel elsewhere); unset or 0 = the library's own
  * choice).  They are read once, at the first call, otherwise.  For tuning
  * sweeps and tests; not thread-safe against concurrent products. */
 int rq_tuning_reload(void);

@@ -133,6 +133,24 @@ def test_product_parity_small(f, N, K, entry):
         T.assert_close(y, yr, b, f"{entry} {f.tag} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("f", T.ALL_FORMATS, ids=lambda f: f.tag)
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_vector_kernel_parity_small(tune, f, N, K):
+    """The vector-unit kernel forced at every M (rq_gemv takes the matrix
+    cores for most of these by itself), in passes of up to eight rows."""
+    if K % 256 and f.layout == S.LAYOUT_ASYM_SB:
+        pytest.skip("asymmetric K must be whole superblocks")
+    tune(RQ_GEMV_KERNEL=1)
+    p = small(f, N, K, tag=2)
+    for M in (2, 3, 5, 8, 9, 16, 33, 64):
+        T.say(f"vector {f.tag} M={M} N={N} K={K}")
+        x = x_for(M, K, seed=M * 1000 + N + 7)
+        y = torch.full((M, N), float("nan"), device="cuda")
+        T.run("gemv", p, x, y)
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"vector {f.tag} M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("N,K,f", [(50, 544, T.fmt("int4g32", 4, 32, S.LAYOUT_SYM)),
                                    (70, 64, S.INT4_G64), (20, 16, S.INT8_G16),
                                    (3, 48 * 16, S.INT8_G16)])
@@ -187,12 +205,12 @@ def chunk_k(f):
 
 
 @pytest.mark.parametrize("f", T.ALL_FORMATS, ids=lambda f: f.tag)
-@pytest.mark.parametrize("kern", ["vector", "matrix"])
+@pytest.mark.parametrize("kern", ["vector", "matrix", "smallm"])
 def test_decode_kernels(tune, f, kern):
-    """Both M <= 4 kernels of rq_gemv, forced: one chunk per wave, waves with
-    unequal chunk counts, several chunks per wave, a ragged last row block
-    and a single row.  Outputs start as NaN."""
-    tune(RQ_GEMV_KERNEL=1 if kern == "vector" else 2)
+    """The three kernels rq_gemv chooses from at M <= 4, forced: one chunk per
+    wave, waves with unequal chunk counts, several chunks per wave, a ragged
+    last row block and a single row.  Outputs start as NaN."""
+    tune(RQ_GEMV_KERNEL={"vector": 1, "matrix": 2, "smallm": 3}[kern])
     ck = chunk_k(f)
     for N, K in [(37, 8 * ck), (300, 13 * ck), (129, 32 * ck), (1, 9 * ck)]:
         p = small(f, N, K, tag=7)

@@ -3,8 +3,8 @@
 Each case builds one decode step of a workload (all layers, every quantized
 matrix, at its real shape and format) on the GPU from its seeds and runs it in
 the launch sequence the benchmark times (gemm_rwkv_decode_amd.step, kind
-"layer": grouped receptance/key/value launches below M = 16, the matrix-core
-entry point from M = 16 on).  The oracle then recomputes the outputs from the
+"layer": grouped receptance/key/value launches, then rq_gemv below M = 5 and
+rq_gemm_smallm from M = 5 on).  The oracle then recomputes the outputs from the
 very bytes the GPU consumed:
 
 * every output of every matrix for the 768-, 2048- and 2560-wide workloads;
@@ -13,7 +13,7 @@ very bytes the GPU consumed:
   row) of every other matrix, the head included.
 
 Layer 0 is also run through the other product entry point (rq_gemm_smallm
-below M = 16, rq_gemv from M = 16), so both are checked at full size at every M.
+below M = 5, rq_gemv from M = 5), so both are checked at full size at every M.
 Outputs start as NaN, so an output a kernel never wrote fails.
 """
 import pytest

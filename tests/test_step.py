@@ -49,7 +49,7 @@ def test_layer_schedule_at_m1(recorded):
     assert recorded[-1][1][6] == 65536  # the head is the last launch
 
 
-def test_matrix_cores_from_m16(recorded):
+def test_smallm_entry_from_m5(recorded):
     cfg = S.CONFIGS["rwkv7-2.9b"]
     mats, W, X, Y = fake_step(cfg, 16)
     ST.step_calls(mats, W, X, Y, "layer")
@@ -73,6 +73,12 @@ def test_matrix_and_batched_kinds(recorded):
     del recorded[:]
     ST.step_calls(mats, W, [torch.empty((16, 1))] * 72, Y, "batched")
     assert [(n, a[1]) for n, a in recorded] == [("rq_gemv_batched", 16)] * 2
+    del recorded[:]
+    ST.step_calls(mats, W, [torch.empty((5, 1))] * 72, Y, "layer")
+    assert [n for n, _ in recorded] == (["rq_gemv_batched"] + ["rq_gemm_smallm"] * 3) * 12
+    del recorded[:]
+    ST.step_calls(mats, W, X, Y, "layer")
+    assert [n for n, _ in recorded] == (["rq_gemv_batched"] + ["rq_gemv"] * 3) * 12
     with pytest.raises(ValueError):
         ST.step_calls(mats, W, X, Y, "fused")
     assert ST.step_calls([], [], [], [], "layer") == []
