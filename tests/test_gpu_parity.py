@@ -224,6 +224,31 @@ def test_decode_kernels(tune, f, kern):
             T.assert_close(y, yr, b, what)
 
 
+@pytest.mark.parametrize("f,K,M", [
+    (S.FP8_E4M3, 16384, 2),    # no tuned vector-unit shape: small-batch kernel
+    (S.INT8_G16, 32768, 1),    # the same at M = 1
+    (S.INT4_G64, 65536, 1),    # decode kernel
+    (S.ASYM4_G32, 65536, 1),   # decode kernel
+    (S.INT4_G64, 16384, 3),    # small-batch kernel at M = 3
+    (S.ASYM5_G32, 4096, 4),    # vector-unit kernel kept for 5-bit codes
+    (S.ASYM5_G32, 16384, 4),   # ... unless the row is too long for it
+], ids=lambda v: getattr(v, "tag", str(v)))
+def test_kernel_choice_long_rows(f, K, M):
+    """Rows too long for the vector-unit kernel's tuned launch shapes take a
+    matrix-core kernel by themselves (rq_gemv and rq_gemv_batched)."""
+    p = small(f, 70, K, tag=9)
+    x = x_for(M, K, seed=K + M)
+    yr, b = T.oracle_y(p, x)
+    T.say(f"kernel choice {f.tag} K={K} M={M}")
+    y = torch.full((M, 70), float("nan"), device="cuda")
+    T.run("gemv", p, x, y)
+    T.assert_close(y, yr, b, f"rq_gemv {f.tag} K={K} M={M}")
+    yb = torch.full((M, 70), float("nan"), device="cuda")
+    rq.rq_gemv_batched([(p.qweight, p.scales, p.zeros, x, yb, 70, K)], M, f.bits, f.group,
+                       f.layout)
+    T.assert_close(yb, yr, b, f"rq_gemv_batched {f.tag} K={K} M={M}")
+
+
 def test_matrix_decode_kernel_falls_back(tune):
     """Forcing the matrix-core decode kernel where K holds fewer than eight
     chunks leaves the vector-unit kernel in charge (still correct)."""
