@@ -220,7 +220,8 @@ enum Kernel { KERN_VECTOR, KERN_DECODE_MFMA, KERN_SMALLM_MFMA };
 // common decode case (M <= 2, a tuned vector-unit shape) returns after one
 // launch-shape search, so stream-mode callers pay little host time per call.
 Kernel pick_kernel(int fmt, int M, int N, int K, int group, rq::GemvCfg* gc) {
-  const int t = rq::tuning().gemv_kernel;
+  int t = rq::tuning().gemv_kernel;
+  if (t < 0 || t > 3) t = 0;  // unknown override values: the automatic choice
   if (t == 1 || (t == 0 && M <= 2)) {
     *gc = rq::choose_gemv(fmt, M, N, K);
     if (t == 1 || gc->lpr != 0) return KERN_VECTOR;
