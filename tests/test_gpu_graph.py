@@ -3,7 +3,8 @@ as direct launches, bit for bit, on every replay (the kernels are
 deterministic), with other GPU work between replays.  Covers the grouped
 vector-unit launch (M = 1), the matrix-core decode kernel (M = 4), grouped
 matrix-core launches (M = 16) and the split-K path with its reduce kernel
-(M = 64, few long rows)."""
+(M = 64, few long rows), and rq_gemv on the matrix cores captured as the
+first call on a fresh stream."""
 import pytest
 import torch
 
@@ -57,3 +58,39 @@ def test_graph_replays_match_direct_launches(wkey, M):
         torch.cuda.synchronize()
         for i, (y, e) in enumerate(zip(Y, eager)):
             assert torch.equal(y, e), f"replay {r}, matrix {i} {mats[i]}"
+
+
+@pytest.mark.parametrize("M", [8, 12])
+def test_rq_gemv_captures_as_first_call(M):
+    """rq_gemv takes the matrix cores from M = 5 on but never allocates, so it
+    can be captured as the first call on a fresh stream, also for long rows
+    that rq_gemm_smallm would split through its workspace."""
+    import gemm_rwkv_decode_amd as rq
+    from tests import rqtest as T
+    f = S.INT4_G64
+    N, K = 512, 16384
+    p = T.to_dev(S.gen_matrix("graph-first", 0, M, N, K, f))
+    g0 = torch.Generator().manual_seed(M)
+    x = torch.randn((M, K), generator=g0).half().cuda()
+    y = torch.full((M, N), float("nan"), device="cuda")
+    s = torch.cuda.Stream()
+    call = rq.prepare("rq_gemv", p.qweight, p.scales, None, x, y, M, N, K, f.bits, f.group,
+                      f.layout, stream=s)
+    say(f"[graph] rq_gemv first call captured, M={M}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    yr, b = T.oracle_y(p, x)
+    ye = torch.full((M, N), float("nan"), device="cuda")
+    rq.rq_gemv(p.qweight, p.scales, None, x, ye, M, N, K, f.bits, f.group, f.layout)
+    torch.cuda.synchronize()
+    T.assert_close(ye, yr, b, f"eager M={M}")
+    junk = torch.randn(1 << 20, device="cuda")
+    for r in range(3):
+        y.fill_(float("nan"))
+        junk.mul_(1.0001)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ye), f"replay {r}"
