@@ -543,7 +543,9 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
 }
 
 // Problems of one launch (they share the format, M, K and the group size):
-// workgroups [block_begin, next block_begin) along x belong to entry i.
+// workgroups [begin[i], begin[i+1]) along x belong to entry i.  The starts sit
+// in one array at the front, so a workgroup finds its problem from one scalar
+// load and compares, then reads that entry.
 struct MmEntry {
   const uint8_t* qw;
   const void* sc;
@@ -551,11 +553,11 @@ struct MmEntry {
   const _Float16* x;
   float* out;  // y, or the partial-sum workspace when K is split
   int N;
-  int block_begin;
 };
 struct MmBatch {
-  MmEntry e[MM_BATCH];
+  int begin[MM_BATCH];
   int count;
+  MmEntry e[MM_BATCH];
 };
 
 template <class S>
@@ -570,7 +572,7 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < MM_BATCH; i++)
-    if (i < bt.count && (int)blockIdx.x >= bt.e[i].block_begin) pi = i;
+    if (i < bt.count && (int)blockIdx.x >= bt.begin[i]) pi = i;
   const MmEntry& e = bt.e[pi];
   const uint8_t* __restrict__ qw = e.qw;
   const void* __restrict__ scales = e.sc;
@@ -587,7 +589,7 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
   // FP8: the matrix scale multiplies every finished sum (or partial sum)
   const float mscale = (S::FMT == FMT_F8) ? *static_cast<const float*>(scales) : 1.0f;
   const int nrounds = kr / S::ROUND;
-  const int row0 = ((int)blockIdx.x - e.block_begin) * S::ROWS;
+  const int row0 = ((int)blockIdx.x - bt.begin[pi]) * S::ROWS;
 
   if (wave >= S::W) {
     if (wave < S::W + MM_XP)
@@ -706,7 +708,8 @@ void launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
   for (int i = 0; i < count; i++) {
     bt.e[i] = MmEntry{static_cast<const uint8_t*>(p[i]->qweight), p[i]->scales, p[i]->zeros,
                       static_cast<const _Float16*>(p[i]->x), c.splits > 1 ? ws : p[i]->y,
-                      p[i]->N, blocks};
+                      p[i]->N};
+    bt.begin[i] = blocks;
     blocks += (p[i]->N + S::ROWS - 1) / S::ROWS;
   }
   bt.count = count;

@@ -148,7 +148,7 @@ __device__ __forceinline__ void load_pass(PassData<FMT, CPL>& pd,
 }
 
 // Problems of one launch: they share the format, K and M; blocks
-// [block_begin, next block_begin) belong to entry i.
+// [begin[i], begin[i+1]) belong to entry i.
 struct GemvEntry {
   const uint8_t* qw;
   const uint8_t* sc;
@@ -156,13 +156,16 @@ struct GemvEntry {
   const _Float16* x;
   float* y;
   int N;
-  int block_begin;
 };
 
+// The first workgroups of the problems sit in one array at the front, so a
+// workgroup finds its problem from one scalar load and compares, then reads
+// that problem's entry (two dependent loads, not one per problem).
 template <int B>
 struct GemvBatch {
-  GemvEntry e[B];
+  int begin[B];  // first workgroup of each problem
   int count;
+  GemvEntry e[B];
 };
 
 // Raw scale material of one chunk, kept undecoded until it is used so that
@@ -198,25 +201,18 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
   extern __shared__ float part[];  // [SK][RB][MT]
 
   // the problem this workgroup belongs to (uniform scan of the table)
-  const uint8_t* __restrict__ qw = bt.e[0].qw;
-  const uint8_t* __restrict__ scales = bt.e[0].sc;
-  const uint8_t* __restrict__ zeros = bt.e[0].zr;
-  const _Float16* __restrict__ x = bt.e[0].x;
-  float* __restrict__ y = bt.e[0].y;
-  int N = bt.e[0].N;
-  int block0 = 0;
+  int pi = 0;
 #pragma unroll
-  for (int i = 1; i < B; i++) {
-    if (i < bt.count && (int)blockIdx.x >= bt.e[i].block_begin) {
-      qw = bt.e[i].qw;
-      scales = bt.e[i].sc;
-      zeros = bt.e[i].zr;
-      x = bt.e[i].x;
-      y = bt.e[i].y;
-      N = bt.e[i].N;
-      block0 = bt.e[i].block_begin;
-    }
-  }
+  for (int i = 1; i < B; i++)
+    if (i < bt.count && (int)blockIdx.x >= bt.begin[i]) pi = i;
+  const GemvEntry& ent = bt.e[pi];
+  const uint8_t* __restrict__ qw = ent.qw;
+  const uint8_t* __restrict__ scales = ent.sc;
+  const uint8_t* __restrict__ zeros = ent.zr;
+  const _Float16* __restrict__ x = ent.x;
+  float* __restrict__ y = ent.y;
+  const int N = ent.N;
+  const int block0 = bt.begin[pi];
 
   // FP8: one binary32 scale for the matrix, applied to each finished sum
   const float mscale = (FMT == FMT_F8) ? *reinterpret_cast<const float*>(scales) : 1.0f;
@@ -522,13 +518,14 @@ static void launch_t(const Launch& L, hipStream_t s) {
   // code bytes per row : scale bytes per row = 2^ssh
   //   int4 sym: (K/2)/(2K/G) = G/4; int8 sym: K/(2K/G) = G/2; asym: (K/2)/(K/32) = 16
   const int ssh = is_asym(FMT) ? 4 : (FMT == FMT_S8 ? gsh - 1 : gsh - 2);
-  auto fill = [&](GemvEntry* e, int* blocks) {
+  auto fill = [&](GemvEntry* e, int* begin, int* blocks) {
     int b = 0;
     for (int i = 0; i < L.count; i++) {
       e[i] = GemvEntry{static_cast<const uint8_t*>(L.p[i]->qweight),
                        static_cast<const uint8_t*>(L.p[i]->scales),
                        static_cast<const uint8_t*>(L.p[i]->zeros), L.x[i], L.y[i],
-                       L.p[i]->N, b};
+                       L.p[i]->N};
+      begin[i] = b;
       b += (L.p[i]->N + rb - 1) / rb;
     }
     *blocks = b;
@@ -536,13 +533,13 @@ static void launch_t(const Launch& L, hipStream_t s) {
   int blocks = 0;
   if (L.count == 1) {
     GemvBatch<1> bt{};
-    fill(bt.e, &blocks);
+    fill(bt.e, bt.begin, &blocks);
     bt.count = 1;
     hipLaunchKernelGGL((k_gemv<FMT, LPR, CPL, MT, NP, 1>), dim3(blocks), dim3(64 * sk), lds,
                        s, bt, L.mrows, L.K, gsh, ssh);
   } else {
     GemvBatch<GEMV_BATCH> bt{};
-    fill(bt.e, &blocks);
+    fill(bt.e, bt.begin, &blocks);
     bt.count = L.count;
     hipLaunchKernelGGL((k_gemv<FMT, LPR, CPL, MT, NP, GEMV_BATCH>), dim3(blocks),
                        dim3(64 * sk), lds, s, bt, L.mrows, L.K, gsh, ssh);

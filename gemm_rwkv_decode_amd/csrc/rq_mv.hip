@@ -66,7 +66,9 @@ constexpr int mv_cg() {
   return FMT == FMT_A4 ? SUPERBLOCK / SB_GROUP : 8;
 }
 
-// One problem of a launch and the table of up to MV_BATCH problems.
+// One problem of a launch and the table of up to MV_BATCH problems.  The
+// first workgroups sit in one array at the front, so a workgroup finds its
+// problem from one scalar load and compares, then reads that entry.
 struct MvEntry {
   const uint8_t* qw;
   const void* sc;
@@ -74,12 +76,12 @@ struct MvEntry {
   const _Float16* x;
   float* y;
   int N;
-  int block_begin;  // first workgroup of this problem
 };
 template <int B>
 struct MvBatch {
-  MvEntry e[B];
+  int begin[B];  // first workgroup of each problem
   int count;
+  MvEntry e[B];
 };
 
 // Per-lane registers of one chunk: codes of CG groups, their scale material.
@@ -201,9 +203,9 @@ k_mv(const MvBatch<B> bt, int M, int K, int xstr) {
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < B; i++)
-    if (i < bt.count && (int)blockIdx.x >= bt.e[i].block_begin) pi = i;
+    if (i < bt.count && (int)blockIdx.x >= bt.begin[i]) pi = i;
   const MvEntry& e = bt.e[pi];
-  const int row0 = ((int)blockIdx.x - e.block_begin) * MV_ROWS;
+  const int row0 = ((int)blockIdx.x - bt.begin[pi]) * MV_ROWS;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -334,7 +336,8 @@ static hipError_t launch_mv_t(const Problem* const* p, int count, int M, hipStre
   int blocks = 0;
   for (int i = 0; i < count; i++) {
     bt.e[i] = MvEntry{static_cast<const uint8_t*>(p[i]->qweight), p[i]->scales, p[i]->zeros,
-                      static_cast<const _Float16*>(p[i]->x), p[i]->y, p[i]->N, blocks};
+                      static_cast<const _Float16*>(p[i]->x), p[i]->y, p[i]->N};
+    bt.begin[i] = blocks;
     blocks += (p[i]->N + MV_ROWS - 1) / MV_ROWS;
   }
   bt.count = count;
