@@ -214,6 +214,12 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
   const int N = ent.N;
   const int block0 = bt.begin[pi];
 
+  // Every argument in scalar registers before the first load.  Otherwise the
+  // compiler fetches the arguments that only the code loads use after it has
+  // issued the x loads: one more scalar round trip before the first code load.
+  asm volatile("" ::"s"(qw), "s"(scales), "s"(zeros), "s"(x), "s"(y), "s"(N), "s"(block0),
+               "s"(K), "s"(gsh), "s"(ssh), "s"(Mrows));
+
   // FP8: one binary32 scale for the matrix, applied to each finished sum
   const float mscale = (FMT == FMT_F8) ? *reinterpret_cast<const float*>(scales) : 1.0f;
 
