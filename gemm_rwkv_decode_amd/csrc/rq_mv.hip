@@ -206,6 +206,10 @@ k_mv(const MvBatch<B> bt, int M, int K, int xstr) {
     if (i < bt.count && (int)blockIdx.x >= bt.begin[i]) pi = i;
   const MvEntry& e = bt.e[pi];
   const int row0 = ((int)blockIdx.x - bt.begin[pi]) * MV_ROWS;
+  // the entry's fields and the launch arguments in scalar registers at once
+  // (one round trip after the table scan, not one per use)
+  asm volatile("" ::"s"(e.qw), "s"(e.sc), "s"(e.zr), "s"(e.x), "s"(e.y), "s"(e.N), "s"(row0),
+               "s"(M), "s"(K));
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
