@@ -389,7 +389,7 @@ def test_side_stream():
 
 # ------------------------------------------------------------ batched ---
 @pytest.mark.parametrize("f", [S.INT4_G64, S.INT8_G16, S.ASYM4_G32], ids=lambda f: f.tag)
-@pytest.mark.parametrize("M", [1, 3, 8, 17, 48])
+@pytest.mark.parametrize("M", [1, 3, 5, 8, 15, 17, 48])
 def test_batched_matches_oracle(f, M):
     """Mixed N and K in one call (K groups share launches), more problems than
     one launch holds, and a K the tuned kernel cannot split."""
