@@ -375,12 +375,18 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 
   if (SK > 1) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < RB * Mrows; idx += blockDim.x) {
-      const int r = idx / Mrows, m = idx % Mrows;
-      float v = 0.0f;
-      for (int ww = 0; ww < SK; ww++) v += part[(ww * RB + r) * MT + m];
+    // Each output (row r, activation row m) adds SK <= 16 partials: the 16
+    // lanes of a lane group read one each and add them across the group (one
+    // LDS read per lane instead of SK in a row).  Outputs are numbered
+    // m * RB + r; a group's lanes share o, so all of them take part in the
+    // cross-lane adds.
+    const int lg = threadIdx.x >> 4, wl = threadIdx.x & 15;
+    for (int o = lg; o < RB * Mrows; o += (int)(blockDim.x >> 4)) {
+      const int r = o % RB, m = o / RB;
+      const float pv = wl < SK ? part[(wl * RB + r) * MT + m] : 0.0f;
+      const float v = group_sum<16>(pv);
       const int n = row0 + r;
-      if (n < N) y[(u32)m * (u32)N + (u32)n] = v * mscale;
+      if (wl == 0 && n < N) y[(u32)m * (u32)N + (u32)n] = v * mscale;
     }
   }
 }
