@@ -92,6 +92,8 @@ CASES = [
     ("fp8 with zeros", dict(layout=2, bits=8, group=0, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
     ("fp8 row not whole 16 bytes", dict(layout=2, bits=8, group=0, K=264), rq.RQ_ERR_SHAPE),
     ("sym group 0", dict(group=0), rq.RQ_ERR_UNSUPPORTED),
+    ("int8 codes of exactly 2 GiB", dict(bits=8, group=16, N=131072, K=16384), rq.RQ_ERR_SHAPE),
+    ("int4 codes of exactly 2 GiB", dict(N=262144, K=16384), rq.RQ_ERR_SHAPE),
     ("asym group 64", dict(layout=1, group=64, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
     ("asym 8-bit", dict(layout=1, group=32, bits=8, z=A + (4 << 30)), rq.RQ_ERR_UNSUPPORTED),
     ("K not a multiple of group", dict(K=96), rq.RQ_ERR_SHAPE),
@@ -111,6 +113,8 @@ GEMV_ONLY = [
     ("null y", dict(y=None), rq.RQ_ERR_NULL),
     ("M zero", dict(M=0), rq.RQ_ERR_SHAPE),
     ("M above 64", dict(M=65), rq.RQ_ERR_SHAPE),
+    ("x of exactly 2 GiB", dict(M=64, K=1 << 24), rq.RQ_ERR_SHAPE),
+    ("y of exactly 2 GiB", dict(M=64, N=1 << 23), rq.RQ_ERR_SHAPE),
     ("misaligned x", dict(x=A + (2 << 30) + 2), rq.RQ_ERR_ALIGN),
     ("misaligned y", dict(y=A + (3 << 30) + 4), rq.RQ_ERR_ALIGN),
     ("y overlaps x", dict(y=A + (2 << 30) + 16), rq.RQ_ERR_ALIAS),
