@@ -90,8 +90,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single "
-              "MI355X and has no multi-GPU mode (run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the hot path runs on a single MI355X and "
+              "there is no multi-GPU mode (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -114,11 +114,11 @@ rq_status check_output(const void* out, size_t out_bytes, const void* qweight,
   return RQ_OK;
 }
 
-// The current device must be a gfx950; checked once per device (the verdict
-// is shared; each thread also remembers its last device and verdict).
+// The current device must be a gfx950; checked once per device (the result
+// is shared; each thread also remembers the last device that passed).
 rq_status check_device(int* dev_out) {
   static std::mutex mu;
-  static int verdict[64];  // 0 unknown, 1 ok, 2 unusable
+  static int arch_state[64];  // 0 unknown, 1 ok, 2 unusable
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
@@ -130,15 +130,15 @@ rq_status check_device(int* dev_out) {
     return RQ_OK;
   }
   std::lock_guard<std::mutex> lk(mu);
-  if (verdict[dev] == 0) {
+  if (arch_state[dev] == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
       (void)hipGetLastError();
       return RQ_ERR_DEVICE;
     }
-    verdict[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    arch_state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
   }
-  if (verdict[dev] != 1) return RQ_ERR_DEVICE;
+  if (arch_state[dev] != 1) return RQ_ERR_DEVICE;
   last_ok_dev = dev;
   *dev_out = dev;
   return RQ_OK;
