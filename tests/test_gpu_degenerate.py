@@ -3,7 +3,8 @@ return exactly +-0 there (the tolerance 1e-3 * sum_k |w x| vanishes): rows of
 all-zero codes, rows with zero scales (asymmetric: zero scale and zero shift),
 and all-zero activations.  The other rows of the same calls are checked
 against the oracle.  Both product entry points at M = 1..64, which covers the
-vector-unit, decode and matrix-core kernels."""
+vector-unit, decode and matrix-core kernels.  Also the smallest legal shapes of
+every format: one to three rows of the shortest row the interface accepts."""
 import pytest
 import torch
 
@@ -107,3 +108,44 @@ def test_zero_rows_in_a_grouped_launch():
             T.assert_close(yb, yr, b, f"grouped problem {i} M={M}")
         for i in (0, 2):
             assert bool((ys[i][:, zero_rows] == 0).all())
+
+
+def smallest_k(f):
+    """The shortest row the interface accepts: one group, a whole number of
+    16-byte code chunks, and whole 256-code superblocks for the asymmetric
+    layout."""
+    k = max(f.group, 16 * 8 // f.bits)
+    if f.layout == S.LAYOUT_ASYM_SB:
+        k = S.SUPERBLOCK
+    return k
+
+
+SMALL_FORMATS = T.ALL_FORMATS + [S.FP8_E4M3, S.FORMATS["asym5g32"], S.FORMATS["asym6g32"]]
+
+
+@pytest.mark.parametrize("f", SMALL_FORMATS, ids=lambda f: f.tag)
+def test_smallest_shapes(f):
+    """One to three rows of the shortest legal length (and twice that): dequant
+    and codes bit-exact, both product entry points within the tolerance."""
+    for N in (1, 2, 3):
+        for K in (smallest_k(f), 2 * smallest_k(f)):
+            p = T.to_dev(S.gen_matrix("tiny", N, K, N, K, f))
+            w = T.dequant(p).cpu().numpy()
+            assert (w.view("u4") == T.oracle_dequant(p).view("u4")).all(), f"{f.tag} {N}x{K}"
+            if f.layout != S.LAYOUT_FP8_TENSOR:
+                c = T.dequant(p, rq.RQ_OUT_CODES_I8).cpu().numpy()
+                assert (c == T.oracle_codes(p)).all(), f"{f.tag} {N}x{K} codes"
+            for M in (1, 2, 4, 5, 16, 64):
+                x = x_for_k(M, K, 40 + M)
+                yr, b = T.oracle_y(p, x)
+                for entry in ("gemv", "gemm"):
+                    T.say(f"smallest {entry} {f.tag} {N}x{K} M={M}")
+                    y = torch.full((M, N), float("nan"), device="cuda")
+                    T.run(entry, p, x, y)
+                    torch.cuda.synchronize()
+                    T.assert_close(y, yr, b, f"{entry} {f.tag} {N}x{K} M={M}")
+
+
+def x_for_k(M, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((M, k), generator=g).half().cuda()
