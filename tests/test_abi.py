@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import gemm_rwkv_decode_amd as rq
 
@@ -196,3 +197,31 @@ def test_batched_rejects(L, what, probs, count, M, status):
 def test_codes_of_2gib_rejected(L):
     # 65536 x 65536 int4 codes are exactly 2 GiB: beyond the 32-bit offsets
     assert L.rq_gemv(*gemv_args(N=65536, K=65536)) == rq.RQ_ERR_SHAPE
+
+
+def test_missing_library_raises(monkeypatch):
+    """No CPU fallback: without librq.so every entry point raises before any
+    work is done."""
+    import gemm_rwkv_decode_amd as pkg
+    monkeypatch.setattr(pkg, "_lib", None)
+    monkeypatch.setattr(pkg, "LIB_PATH", "/nonexistent/librq.so")
+    t = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(pkg.RqLibraryMissing):
+        pkg.rq_gemv(t, t, None, t, t, 1, 1, 32, 4, 32, 0)
+    with pytest.raises(pkg.RqLibraryMissing):
+        pkg.rq_gemm_smallm(t, t, None, t, t, 1, 1, 32, 4, 32, 0)
+    with pytest.raises(pkg.RqLibraryMissing):
+        pkg.rq_dequant(t, t, None, t, 1, 32, 4, 32, 0)
+    # the grouped call checks its problem table (device tensors only) first
+    with pytest.raises((pkg.RqLibraryMissing, ValueError)):
+        pkg.rq_gemv_batched([(t, t, None, t, t, 1, 32)], 1, 4, 32, 0)
+
+
+def test_host_tensors_are_refused(L):
+    """The binding hands the library device memory only; host tensors are
+    refused rather than computed on the CPU."""
+    t = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        rq.rq_gemv(t, t, None, t, t, 1, 1, 32, 4, 32, 0)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        rq.rq_dequant(t, t, None, t, 1, 32, 4, 32, 0)
