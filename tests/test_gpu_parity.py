@@ -408,6 +408,22 @@ def test_batched_matches_oracle(f, M):
         T.assert_close(y, yr, b, f"batched {f.tag} M={M} problem {i} {p.N}x{p.K}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 32])
+def test_batched_at_the_maximum_count(M):
+    """RQ_MAX_BATCH problems in one call: two K groups, several launches each."""
+    f = S.INT4_G64
+    shapes = [(64 + 8 * (i % 5), 1024 if i % 3 else 2048) for i in range(rq.RQ_MAX_BATCH)]
+    mats = [small(f, N, K, tag=400 + i) for i, (N, K) in enumerate(shapes)]
+    xs = [x_for(M, K, seed=500 + i) for i, (_, K) in enumerate(shapes)]
+    ys = [torch.full((M, N), float("nan"), device="cuda") for (N, _) in shapes]
+    T.say(f"batched maximum count M={M}")
+    rq.rq_gemv_batched([(p.qweight, p.scales, p.zeros, x, y, p.N, p.K)
+                        for p, x, y in zip(mats, xs, ys)], M, f.bits, f.group, f.layout)
+    for i, (p, x, y) in enumerate(zip(mats, xs, ys)):
+        yr, b = T.oracle_y(p, x)
+        T.assert_close(y, yr, b, f"batched maximum M={M} problem {i} {p.N}x{p.K}")
+
+
 def test_batched_rejects_overlapping_outputs():
     p = small(S.INT4_G64, 64, 256, tag=40)
     x = x_for(1, 256, seed=4)
