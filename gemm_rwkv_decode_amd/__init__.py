@@ -89,6 +89,9 @@ def lib():
             L.rq_probe_empty.restype = i
             L.rq_tuning_reload.argtypes = []
             L.rq_tuning_reload.restype = i
+            ip = ctypes.POINTER(ctypes.c_int)
+            L.rq_gemm_config.argtypes = [i, i, i, i, i, i, i, ip, ip]
+            L.rq_gemm_config.restype = i
             _lib = L
     return _lib
 
@@ -200,6 +203,20 @@ def prepare(name, *args, stream=None):
             raise RqError(name, st)
     call.args = cargs  # keeps the problem array alive
     return call
+
+
+def gemm_config(M, N, K, bits, group, layout, allow_split=True):
+    """(plan, splits) of the small-batch matrix-core kernel for one product
+    (plan 1-based, as RQ_GEMM_PLAN numbers them), or None when that kernel
+    cannot take the shape.  Host-only."""
+    plan, splits = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().rq_gemm_config(int(M), int(N), int(K), int(bits), int(group), int(layout),
+                              1 if allow_split else 0, ctypes.byref(plan), ctypes.byref(splits))
+    if st == RQ_ERR_UNSUPPORTED:
+        return None
+    if st != RQ_OK:
+        raise RqError("rq_gemm_config", st)
+    return plan.value, splits.value
 
 
 def tuning_reload():

@@ -144,43 +144,30 @@ rq_status check_device(int* dev_out) {
   return RQ_OK;
 }
 
-// Split-K workspace: one per (device, stream), grown on demand, never freed.
-// Calls on one stream are ordered, so they may share it; calls on different
-// streams get different buffers.
-struct Workspace {
-  float* partial = nullptr;
-  size_t floats = 0;
-};
-
-rq_status get_workspace(int dev, hipStream_t stream, size_t floats, Workspace* out) {
+// Split-K workspace: one per (device, stream), allocated by the first call on
+// that stream that splits K, at the largest size the chooser ever asks for
+// (rq::GEMM_WS_MAX_BYTES), and kept until the process ends: never regrown,
+// freed or reused for another stream, so no later call allocates or waits.
+// Calls on one stream are ordered, so they may share it.
+float* stream_workspace(int dev, hipStream_t stream) {
   static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, Workspace> cache;
+  static std::map<std::pair<int, hipStream_t>, float*> cache;
   std::lock_guard<std::mutex> lk(mu);
-  Workspace& w = cache[std::make_pair(dev, stream)];
-  if (w.floats >= floats) {
-    *out = w;
-    return RQ_OK;
-  }
+  auto it = cache.find(std::make_pair(dev, stream));
+  if (it != cache.end()) return it->second;
+  // hipMalloc is not a stream operation, but a stream under capture is left
+  // alone all the same: the caller then gets K kept whole
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (stream && hipStreamIsCapturing(stream, &cs) == hipSuccess &&
       cs != hipStreamCaptureStatusNone)
-    return RQ_ERR_DEVICE;  // cannot allocate while a graph is being captured
-  const size_t want = floats > ((size_t)4 << 20) ? floats : ((size_t)4 << 20);
-  // the old buffer may still be in use by work queued on this stream
-  if (w.partial) {
-    if (hipStreamSynchronize(stream) != hipSuccess) return RQ_ERR_DEVICE;
-    (void)hipFree(w.partial);
-  }
-  w = Workspace{};
+    return nullptr;
   float* p = nullptr;
-  if (hipMalloc(&p, want * sizeof(float)) != hipSuccess) {
+  if (hipMalloc(&p, rq::GEMM_WS_MAX_BYTES) != hipSuccess) {
     (void)hipGetLastError();
-    return RQ_ERR_DEVICE;
+    return nullptr;
   }
-  w.partial = p;
-  w.floats = want;
-  *out = w;
-  return RQ_OK;
+  cache[std::make_pair(dev, stream)] = p;
+  return p;
 }
 
 rq_status check_product(const void* qweight, const void* scales, const void* zeros,
@@ -384,13 +371,15 @@ rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* ze
     const rq::GemvCfg c = rq::choose_gemv(fmt, M, N, K);
     return rq::launch_gemv(p, c, s) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
   }
-  const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
-  Workspace w;
+  rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
+  float* ws = nullptr;
   if (c.splits > 1) {
-    st = get_workspace(dev, s, rq::gemm_workspace_floats(c, M, N), &w);
-    if (st != RQ_OK) return st;
+    ws = stream_workspace(dev, s);
+    // no workspace (first split call made under graph capture, or out of
+    // memory): keep K whole
+    if (!ws) c = rq::choose_gemm(fmt, M, N, K, group, 0, false);
   }
-  const hipError_t e = rq::launch_gemm(p, c, w.partial, s);
+  const hipError_t e = rq::launch_gemm(p, c, ws, s);
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 
@@ -403,12 +392,26 @@ const char* rq_status_string(int status) {
     case RQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case RQ_ERR_LAUNCH: return "the kernel launch failed";
     case RQ_ERR_ALIAS: return "an output overlaps an input";
-    case RQ_ERR_DEVICE: return "no usable gfx950 device or workspace";
+    case RQ_ERR_DEVICE: return "no usable gfx950 device";
     default: return "unknown status";
   }
 }
 
 int rq_version(void) { return (1 << 16) | 0; }
+
+int rq_gemm_config(int M, int N, int K, int bits, int group, int layout, int allow_split,
+                   int* plan, int* splits) {
+  if (!plan || !splits) return RQ_ERR_NULL;
+  const int fmt = format_of(layout, bits, group);
+  if (fmt < 0) return RQ_ERR_UNSUPPORTED;
+  if (M < 1 || M > RQ_MAX_M || N < 1 || K < 1) return RQ_ERR_SHAPE;
+  if (group > 0 && K % group != 0) return RQ_ERR_SHAPE;
+  if (!rq::gemm_supports(fmt, M, K, group)) return RQ_ERR_UNSUPPORTED;
+  const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group, 0, allow_split != 0);
+  *plan = c.plan + 1;
+  *splits = c.splits;
+  return RQ_OK;
+}
 
 int rq_tuning_reload(void) {
   rq::tuning();  // make sure the one-time read has happened

@@ -3,8 +3,8 @@
 
 namespace rq {
 
-void launch_gemm_fmt_a5(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s) {
-  launch_fmt<FMT_A5>(p, n, c, ws, s);
+hipError_t launch_gemm_fmt_a5(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s) {
+  return launch_fmt<FMT_A5>(p, n, c, ws, s);
 }
 
 }  // namespace rq

@@ -3,8 +3,8 @@
 
 namespace rq {
 
-void launch_gemm_fmt_f8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s) {
-  launch_fmt<FMT_F8>(p, n, c, ws, s);
+hipError_t launch_gemm_fmt_f8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s) {
+  return launch_fmt<FMT_F8>(p, n, c, ws, s);
 }
 
 }  // namespace rq

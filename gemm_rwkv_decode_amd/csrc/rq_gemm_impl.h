@@ -157,6 +157,35 @@ constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) 
   return d;
 }
 
+// Workgroup arrangements: row groups x K-slices x 16-row tiles per wave, and
+// the round size (rd = 2: half the default round).
+struct Plan {
+  int wr, wk, nt, rd;
+};
+static constexpr Plan kPlans[] = {
+    {1, 4, 1, 1},  // 0: 16 rows, 4 K-slices
+    {1, 8, 1, 1},  // 1: 16 rows, 8 K-slices
+    {4, 1, 1, 1},  // 2: 64 rows, whole chunks per wave
+    {2, 4, 1, 1},  // 3: 32 rows, 4 K-slices
+    {2, 2, 1, 1},  // 4: 32 rows, 2 K-slices
+    {4, 2, 1, 1},  // 5: 64 rows, 2 K-slices
+    {1, 4, 1, 2},  // 6: as 0, half rounds
+    {4, 2, 1, 2},  // 7: as 5, half rounds
+    {2, 4, 1, 2},  // 8: as 3, half rounds
+    {4, 1, 1, 2},  // 9: as 2, half rounds
+    // two 16-row tiles per wave: each A fragment read from LDS feeds two MFMAs
+    {2, 2, 2, 1},  // 10: 64 rows, 2 K-slices
+    {2, 4, 2, 1},  // 11: 64 rows, 4 K-slices
+    {1, 8, 2, 1},  // 12: 32 rows, 8 K-slices
+    {1, 4, 2, 1},  // 13: 32 rows, 4 K-slices
+    {4, 2, 2, 1},  // 14: 128 rows, 2 K-slices
+    // three row groups: 48-row workgroups (12288 rows -> 256 workgroups)
+    {3, 2, 1, 1},  // 15: 48 rows, 2 K-slices
+    {3, 2, 1, 2},  // 16: as 15, half rounds
+    {3, 4, 1, 1},  // 17: 48 rows, 4 K-slices
+};
+constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
+
 // Compile-time shape of one kernel instance.
 template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_>
 struct Mm {
@@ -673,45 +702,18 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
   }
 }
 
-// Workgroup arrangements: row groups x K-slices x 16-row tiles per wave, and
-// the round size (rd = 2: half the default round).
-struct Plan {
-  int wr, wk, nt, rd;
-};
-static constexpr Plan kPlans[] = {
-    {1, 4, 1, 1},  // 0: 16 rows, 4 K-slices
-    {1, 8, 1, 1},  // 1: 16 rows, 8 K-slices
-    {4, 1, 1, 1},  // 2: 64 rows, whole chunks per wave
-    {2, 4, 1, 1},  // 3: 32 rows, 4 K-slices
-    {2, 2, 1, 1},  // 4: 32 rows, 2 K-slices
-    {4, 2, 1, 1},  // 5: 64 rows, 2 K-slices
-    {1, 4, 1, 2},  // 6: as 0, half rounds
-    {4, 2, 1, 2},  // 7: as 5, half rounds
-    {2, 4, 1, 2},  // 8: as 3, half rounds
-    {4, 1, 1, 2},  // 9: as 2, half rounds
-    // two 16-row tiles per wave: each A fragment read from LDS feeds two MFMAs
-    {2, 2, 2, 1},  // 10: 64 rows, 2 K-slices
-    {2, 4, 2, 1},  // 11: 64 rows, 4 K-slices
-    {1, 8, 2, 1},  // 12: 32 rows, 8 K-slices
-    {1, 4, 2, 1},  // 13: 32 rows, 4 K-slices
-    {4, 2, 2, 1},  // 14: 128 rows, 2 K-slices
-    // three row groups: 48-row workgroups (12288 rows -> 256 workgroups)
-    {3, 2, 1, 1},  // 15: 48 rows, 2 K-slices
-    {3, 2, 1, 2},  // 16: as 15, half rounds
-    {3, 4, 1, 1},  // 17: 48 rows, 4 K-slices
-};
-constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
-
 // Adds the split-K partial sums into y (rq_gemm.hip).
 void launch_split_reduce(const float* ws, float* y, size_t count, int splits, hipStream_t s);
 
 // One launch over p[0..count), count <= MM_BATCH; K is split (c.splits > 1,
 // partial sums in ws) only for a single problem.
 template <class S>
-void launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
-                     hipStream_t s) {
+hipError_t launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
+                    hipStream_t s) {
   if constexpr (!S::FITS) {
-    return;  // never chosen (plan_ok)
+    // plan_ok never chooses such a plan; a caller that does gets an error
+    // instead of an output that was never written
+    return hipErrorInvalidValue;
   } else {
   MmBatch bt{};
   int blocks = 0;
@@ -726,38 +728,33 @@ void launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
   const int M = p[0]->M, K = p[0]->K;
   hipLaunchKernelGGL((k_mm<S>), dim3(blocks, c.splits), dim3(S::THREADS), 0, s, bt, M, K,
                      K / c.splits);
-  if (c.splits > 1) launch_split_reduce(ws, p[0]->y, (size_t)M * p[0]->N, c.splits, s);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && c.splits > 1) {
+    launch_split_reduce(ws, p[0]->y, (size_t)M * p[0]->N, c.splits, s);
+    e = hipGetLastError();
+  }
+  return e;
   }
 }
 
-template <int FMT, int MT, int G>
-void launch_plan(const Problem* const* p, int n, const GemmCfg& c, float* ws,
-                        hipStream_t s) {
-  switch (c.plan) {
-    case 0: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 1>>(p, n, c, ws, s);
-    case 1: return launch_s<Mm<FMT, MT, 1, 1, 8, G, 1>>(p, n, c, ws, s);
-    case 2: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 1>>(p, n, c, ws, s);
-    case 3: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 1>>(p, n, c, ws, s);
-    case 4: return launch_s<Mm<FMT, MT, 1, 2, 2, G, 1>>(p, n, c, ws, s);
-    case 5: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 1>>(p, n, c, ws, s);
-    case 6: return launch_s<Mm<FMT, MT, 1, 1, 4, G, 2>>(p, n, c, ws, s);
-    case 7: return launch_s<Mm<FMT, MT, 1, 4, 2, G, 2>>(p, n, c, ws, s);
-    case 8: return launch_s<Mm<FMT, MT, 1, 2, 4, G, 2>>(p, n, c, ws, s);
-    case 9: return launch_s<Mm<FMT, MT, 1, 4, 1, G, 2>>(p, n, c, ws, s);
-    case 10: return launch_s<Mm<FMT, MT, 2, 2, 2, G, 1>>(p, n, c, ws, s);
-    case 11: return launch_s<Mm<FMT, MT, 2, 2, 4, G, 1>>(p, n, c, ws, s);
-    case 12: return launch_s<Mm<FMT, MT, 2, 1, 8, G, 1>>(p, n, c, ws, s);
-    case 13: return launch_s<Mm<FMT, MT, 2, 1, 4, G, 1>>(p, n, c, ws, s);
-    case 14: return launch_s<Mm<FMT, MT, 2, 4, 2, G, 1>>(p, n, c, ws, s);
-    case 15: return launch_s<Mm<FMT, MT, 1, 3, 2, G, 1>>(p, n, c, ws, s);
-    case 16: return launch_s<Mm<FMT, MT, 1, 3, 2, G, 2>>(p, n, c, ws, s);
-    default: return launch_s<Mm<FMT, MT, 1, 3, 4, G, 1>>(p, n, c, ws, s);
+// The instance of plan P (an index into kPlans).
+template <int FMT, int MT, int G, int P>
+using MmPlan = Mm<FMT, MT, kPlans[P].nt, kPlans[P].wr, kPlans[P].wk, G, kPlans[P].rd>;
+
+template <int FMT, int MT, int G, int P = 0>
+hipError_t launch_plan(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                       hipStream_t s) {
+  if constexpr (P >= kNumPlans) {
+    return hipErrorInvalidValue;  // no such plan
+  } else {
+    if (c.plan == P) return launch_s<MmPlan<FMT, MT, G, P>>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, G, P + 1>(p, n, c, ws, s);
   }
 }
 
 template <int FMT, int MT>
-void launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
-                         hipStream_t s) {
+hipError_t launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                        hipStream_t s) {
   const int g = p[0]->group;
   if constexpr (FMT == FMT_F8) {
     return launch_plan<FMT, MT, MM_F8_GROUP>(p, n, c, ws, s);
@@ -775,8 +772,8 @@ void launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
 }
 
 template <int FMT>
-void launch_fmt(const Problem* const* p, int n, const GemmCfg& c, float* ws,
-                       hipStream_t s) {
+hipError_t launch_fmt(const Problem* const* p, int n, const GemmCfg& c, float* ws,
+                      hipStream_t s) {
   switch (c.mt) {
     case 1: return launch_group<FMT, 1>(p, n, c, ws, s);
     case 2: return launch_group<FMT, 2>(p, n, c, ws, s);
@@ -786,11 +783,11 @@ void launch_fmt(const Problem* const* p, int n, const GemmCfg& c, float* ws,
 }
 
 // One per format, each in its own translation unit (rq_gemm_<format>.hip).
-void launch_gemm_fmt_s4(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
-void launch_gemm_fmt_s8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
-void launch_gemm_fmt_a4(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
-void launch_gemm_fmt_a5(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
-void launch_gemm_fmt_a6(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
-void launch_gemm_fmt_f8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+hipError_t launch_gemm_fmt_s4(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+hipError_t launch_gemm_fmt_s8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+hipError_t launch_gemm_fmt_a4(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+hipError_t launch_gemm_fmt_a5(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+hipError_t launch_gemm_fmt_a6(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
+hipError_t launch_gemm_fmt_f8(const Problem* const* p, int n, const GemmCfg& c, float* ws, hipStream_t s);
 
 }  // namespace rq

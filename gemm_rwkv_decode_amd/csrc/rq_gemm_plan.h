@@ -1,0 +1,146 @@
+// rq_gemm_plan.h -- host side of the matrix-core kernel: which workgroup
+// arrangement (plan) runs a problem and whether K is split over workgroups.
+// Included by rq_gemm.hip (and by a host-only check of the plan table).
+#pragma once
+
+#include "rq_gemm_impl.h"
+
+#include <array>
+#include <utility>
+
+namespace rq {
+
+static int round_k(int fmt, int mt, int group, int plan) {
+  const Plan& q = kPlans[plan];
+  return mm_round(fmt, mt, q.wk, group, q.rd);
+}
+
+// Whether plan `plan` fits (LDS, registers, copy layout) for the format, M-tile
+// count and group: read from the kernel instance's own FITS, so the host and
+// the device cannot disagree.
+template <int FMT, int MT, int G, size_t... P>
+static constexpr std::array<bool, kNumPlans> fits_row(std::index_sequence<P...>) {
+  return {{MmPlan<FMT, MT, G, (int)P>::FITS...}};
+}
+template <int FMT, int MT, int G>
+static constexpr std::array<bool, kNumPlans> kFits =
+    fits_row<FMT, MT, G>(std::make_index_sequence<kNumPlans>{});
+
+template <int FMT, int MT>
+static bool fits_mt(int g, int plan) {
+  if constexpr (FMT == FMT_F8) {
+    return g == MM_F8_GROUP && kFits<FMT, MT, MM_F8_GROUP>[plan];
+  } else if constexpr (is_asym(FMT)) {
+    return g == SB_GROUP && kFits<FMT, MT, SB_GROUP>[plan];
+  } else if constexpr (FMT == FMT_S8) {
+    return g == 16 ? kFits<FMT, MT, 16>[plan]
+                   : (g == 32 ? kFits<FMT, MT, 32>[plan] : (g == 64 && kFits<FMT, MT, 64>[plan]));
+  } else {
+    return g == 32 ? kFits<FMT, MT, 32>[plan]
+                   : (g == 64 ? kFits<FMT, MT, 64>[plan] : (g == 128 && kFits<FMT, MT, 128>[plan]));
+  }
+}
+
+template <int FMT>
+static bool fits_fmt(int mt, int g, int plan) {
+  switch (mt) {
+    case 1: return fits_mt<FMT, 1>(g, plan);
+    case 2: return fits_mt<FMT, 2>(g, plan);
+    case 3: return fits_mt<FMT, 3>(g, plan);
+    case 4: return fits_mt<FMT, 4>(g, plan);
+    default: return false;
+  }
+}
+
+static bool plan_fits(int fmt, int mt, int g, int plan) {
+  if (plan < 0 || plan >= kNumPlans) return false;
+  switch (fmt) {
+    case FMT_S4: return fits_fmt<FMT_S4>(mt, g, plan);
+    case FMT_S8: return fits_fmt<FMT_S8>(mt, g, plan);
+    case FMT_A4: return fits_fmt<FMT_A4>(mt, g, plan);
+    case FMT_A5: return fits_fmt<FMT_A5>(mt, g, plan);
+    case FMT_A6: return fits_fmt<FMT_A6>(mt, g, plan);
+    case FMT_F8: return fits_fmt<FMT_F8>(mt, g, plan);
+    default: return false;
+  }
+}
+
+// The plan can run this problem: K is a whole number of rounds, a row's
+// scales are whole dwords, and the workgroup's layout fits the LDS.
+static bool plan_ok(int fmt, int mt, int group, int K, int plan) {
+  const int rk = round_k(fmt, mt, group, plan);
+  return K % rk == 0 && (K / group) % 2 == 0 && plan_fits(fmt, mt, group, plan);
+}
+
+size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
+  return c.splits > 1 ? (size_t)c.splits * M * N : 0;
+}
+
+bool gemm_supports(int fmt, int M, int K, int group) {
+  if (fmt == FMT_F8) group = MM_F8_GROUP;
+  const int mt = (M + 15) / 16;
+  for (int p = 0; p < kNumPlans; p++)
+    if (plan_ok(fmt, mt, group, K, p)) return true;
+  return false;
+}
+
+GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool allow_split) {
+  if (fmt == FMT_F8) group = MM_F8_GROUP;
+  GemmCfg c{};
+  c.mt = (M + 15) / 16;
+  c.splits = 1;
+  const Tuning& tu = tuning();
+  // Preference order by row count: with few rows, more K-slices per
+  // workgroup keep one workgroup per CU busy; with many rows, 64-row
+  // workgroups cut the x staging per row (every workgroup stages all of x,
+  // M*K*2 bytes, from L2).  Measured on MI355X for the RWKV-7 shapes, int4
+  // g64, weights cold in HBM.
+  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
+  // Few rows and long rows (K >= 16384) or a full M-tile stack (M > 48): the
+  // x staging of 16-row workgroups dominates, so 64-row workgroups with K
+  // split four ways (a second, small kernel adds the partial sums) -- at
+  // 4096x16384: 16.2 -> 15.0 us (M=16), 23.0 -> 18.8 us (M=32),
+  // 45.8 -> 25.0 us (M=64).
+  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
+  const bool split_k = allow_split && N < 8192 && (K >= 16384 || c.mt >= 4);
+  const int* order = split_k ? (c.mt == 1 ? split_n_m16 : split_n)
+                             : (N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n));
+  c.plan = -1;
+  if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
+      plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
+    c.plan = tu.gemm_plan - 1;
+  // 48-row workgroups where they make one wave of 224..256 row blocks (64-row
+  // ones leave a quarter of the CUs idle): one 12288x4096 product,
+  // 14.1 -> 11.2 us (M=16), 18.3 -> 12.1 us (M=32), 30.1 -> 20.3 us (M=64).
+  // Blocks are counted per problem: three 4096-row problems need 258, and
+  // the two past one wave nearly double the launch.
+  const int b48 = blocks48 > 0 ? blocks48 : (N + 47) / 48;
+  if (c.plan < 0 && !split_k && b48 >= 224 && b48 <= 256) {
+    const int p48 = c.mt <= 2 ? 17 : 15;
+    if (plan_ok(fmt, c.mt, group, K, p48)) c.plan = p48;
+  }
+  for (int i = 0; i < kNumPlans && c.plan < 0; i++)
+    if (plan_ok(fmt, c.mt, group, K, order[i])) c.plan = order[i];
+  // Splits divide K into whole rounds and the partial sums stay under 64 MiB.
+  // Automatic only in the case above, enough row blocks x K-ranges for 256
+  // CUs (at most 4); RQ_GEMM_SPLITS overrides.
+  const int rows = kPlans[c.plan].wr * kPlans[c.plan].nt * 16;
+  const int blocks = (N + rows - 1) / rows;
+  int want = 1;
+  if (split_k && rows == 64 && blocks < 256) want = (256 + blocks - 1) / blocks;
+  if (want > 4) want = 4;
+  if (tu.gemm_splits) want = tu.gemm_splits;
+  if (!allow_split) want = 1;
+  const int nr = K / round_k(fmt, c.mt, group, c.plan);
+  if (want > nr) want = nr;
+  if (want < 1) want = 1;
+  int sp = want;
+  while (sp > 1 && (nr % sp != 0 || (size_t)sp * M * N * 4 > GEMM_WS_MAX_BYTES)) sp--;
+  c.splits = sp;
+  return c;
+}
+
+}  // namespace rq

@@ -75,6 +75,8 @@ constexpr int MM_BATCH = 8;
 hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c, float* ws,
                             hipStream_t s);
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N);
+// Largest split-K workspace choose_gemm asks for (splits * M * N floats).
+constexpr size_t GEMM_WS_MAX_BYTES = (size_t)64 << 20;
 
 hipError_t launch_dequant(const void* qweight, const void* scales, const void* zeros,
                           void* out, int N, int K, int group, int fmt, int out_kind,

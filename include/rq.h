@@ -88,8 +88,7 @@ typedef enum {
     RQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
     RQ_ERR_LAUNCH = 5,      /* the kernel launch was rejected by the runtime    */
     RQ_ERR_ALIAS = 6,       /* an output range overlaps an input range          */
-    RQ_ERR_DEVICE = 7       /* no usable gfx950 device, or device memory for the
-                               split-K workspace could not be obtained           */
+    RQ_ERR_DEVICE = 7       /* no usable gfx950 device                           */
 } rq_status;
 
 typedef enum { RQ_LAYOUT_SYM = 0, RQ_LAYOUT_ASYM_SB = 1, RQ_LAYOUT_FP8_TENSOR = 2 } rq_layout;
@@ -175,16 +174,23 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
 /*
  * rq_gemm_smallm -- the same product and contract as rq_gemv, computed on the
  * matrix cores (fp16 MFMA on exact integer or FP8 codes, fp32 per-group
- * scaling; FP8 sums are scaled once by the matrix scale).  Every layout and
- * code width, 5- and 6-bit codes included.
+ * scaling; FP8 sums are scaled once by the matrix scale).  This is the
+ * batched-decode member of the kernel family the model card "RWKV-7 G1 1.5B --
+ * int4 GPTQ for rwkv-sglang" names in its "Speed" line (a small-M GEMM next
+ * to the GEMV, credited with beating fp16 at every batch up to 32).  Every
+ * layout and code width, 5- and 6-bit codes included.
  * Tuned for 16 <= M <= 64 (batched decode); smaller M is padded to 16, which
  * still beats the vector units from M = 5 on.
- * For some shapes the K dimension is split across workgroups; the partial sums
- * then pass through a workspace the library allocates once per (device,
- * stream) and keeps until the process ends (a call that needs a larger one
- * than the stream already has allocates it before enqueuing, which
- * synchronizes that device).  Partial sums are added in a fixed order, so
- * results are deterministic.
+ * Workspace.  For some shapes the K dimension is split across workgroups and
+ * the partial sums pass through a workspace of 64 MiB that the library
+ * allocates at the first such call on a (device, stream) pair and keeps until
+ * the process ends; it is never regrown, freed or shared with another stream,
+ * so no later call allocates, frees or synchronizes.  If that first call is
+ * made while the stream is being captured into a graph (or the allocation
+ * fails), the call keeps K whole instead.  Work that uses one stream's
+ * workspace must not run concurrently with other work that uses it (graphs
+ * captured on one stream and replayed on several at once race on it).
+ * Partial sums are added in a fixed order, so results are deterministic.
  */
 rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* zeros,
                          const void* x, float* y, int M, int N, int K, int bits,

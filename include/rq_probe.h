@@ -43,6 +43,18 @@ int rq_probe_empty(void* stream);
  * sweeps and tests; not thread-safe against concurrent products. */
 int rq_tuning_reload(void);
 
+/* The workgroup arrangement of the small-batch matrix-core kernel for one
+ * product: *plan receives its 1-based index (the numbering RQ_GEMM_PLAN
+ * uses), *splits the number of K-ranges split across workgroups.
+ * allow_split = 0 asks for the arrangement rq_gemv and rq_gemv_batched use
+ * (K kept whole), nonzero for rq_gemm_smallm's own choice (which keeps K whole
+ * too when it has no workspace).  Overrides in effect are applied, so a test
+ * can see whether a forced plan was taken.  Host-only; no GPU needed.
+ * Returns RQ_ERR_UNSUPPORTED when the matrix-core kernel cannot take the shape
+ * (rq_gemm_smallm then runs the vector-unit kernel). */
+int rq_gemm_config(int M, int N, int K, int bits, int group, int layout, int allow_split,
+                   int* plan, int* splits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,9 +61,11 @@ def oracle_codes(p: S.Packed):
 
 
 def run(entry, p: S.Packed, x: torch.Tensor, y=None):
+    """y = x W^T through rq_gemv ("gemv") or rq_gemm_smallm ("gemm").  A fresh
+    y starts as NaN, so an output no kernel wrote fails every comparison."""
     M = x.shape[0]
     if y is None:
-        y = torch.empty((M, p.N), dtype=torch.float32, device="cuda")
+        y = torch.full((M, p.N), float("nan"), dtype=torch.float32, device="cuda")
     f = rq.rq_gemv if entry == "gemv" else rq.rq_gemm_smallm
     f(p.qweight, p.scales, p.zeros, x, y, M, p.N, p.K, p.fmt.bits, p.fmt.group,
       p.fmt.layout)
@@ -71,8 +73,12 @@ def run(entry, p: S.Packed, x: torch.Tensor, y=None):
 
 
 def dequant(p: S.Packed, kind=rq.RQ_OUT_F32):
-    dt = torch.float32 if kind == rq.RQ_OUT_F32 else torch.int8
-    out = torch.empty((p.N, p.K), dtype=dt, device="cuda")
+    """rq_dequant into a fresh output that starts as NaN (binary32) or as the
+    byte 0x5A (codes), so an element no kernel wrote fails the comparison."""
+    if kind == rq.RQ_OUT_F32:
+        out = torch.full((p.N, p.K), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        out = torch.full((p.N, p.K), 0x5A, dtype=torch.int8, device="cuda")
     rq.rq_dequant(p.qweight, p.scales, p.zeros, out, p.N, p.K, p.fmt.bits, p.fmt.group,
                   p.fmt.layout, kind)
     return out

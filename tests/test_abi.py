@@ -18,7 +18,8 @@ A = 0x7F0000000000  # a 16-byte-aligned address that is never dereferenced
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    import glob
+    src = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(rq_[a-z_0-9]+)\s*\(", src)))
 
@@ -225,3 +226,20 @@ def test_host_tensors_are_refused(L):
         rq.rq_gemv(t, t, None, t, t, 1, 1, 32, 4, 32, 0)
     with pytest.raises(ValueError, match="GPU tensors only"):
         rq.rq_dequant(t, t, None, t, 1, 32, 4, 32, 0)
+
+
+def test_gemm_config_on_the_host(L):
+    """The plan query of rq_probe.h runs on the host: rq_gemm_smallm splits K
+    for few long rows, rq_gemv's choice keeps K whole, and a K the matrix-core
+    kernel cannot take (an odd number of groups) reports no plan."""
+    plan, splits = rq.gemm_config(32, 4096, 16384, 4, 64, 0)
+    assert 1 <= plan <= 18 and splits == 4
+    plan2, splits2 = rq.gemm_config(32, 4096, 16384, 4, 64, 0, allow_split=False)
+    assert 1 <= plan2 <= 18 and splits2 == 1
+    assert rq.gemm_config(32, 4096, 64 * 7, 4, 64, 0) is None
+    for M in (1, 16, 17, 32, 48, 49, 64):
+        for (N, K) in ((4096, 4096), (16384, 4096), (4096, 16384), (65536, 4096)):
+            p, s = rq.gemm_config(M, N, K, 4, 64, 0)
+            assert 1 <= p <= 18 and s >= 1 and s * M * N * 4 <= 64 << 20
+    with pytest.raises(rq.RqError):
+        rq.gemm_config(0, 64, 256, 4, 64, 0)

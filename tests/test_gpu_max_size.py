@@ -92,6 +92,8 @@ def test_dequant_max_rows(big, kind):
     out = torch.empty((p.N, K), dtype=dt, device="cuda")
     if kind == rq.RQ_OUT_F32:
         out.fill_(float("nan"))
+    else:
+        out.fill_(0x5A)
     rq.rq_dequant(p.qweight, p.scales, p.zeros, out, p.N, K, p.fmt.bits, p.fmt.group,
                   p.fmt.layout, kind)
     torch.cuda.synchronize()
