@@ -87,6 +87,12 @@ def lib():
             L.rq_probe_copy.restype = i
             L.rq_probe_empty.argtypes = [vp]
             L.rq_probe_empty.restype = i
+            L.rq_probe_signal.argtypes = [vp, i, i, vp]
+            L.rq_probe_signal.restype = i
+            L.rq_probe_barrier.argtypes = [vp, i, i, i, i, vp, vp]
+            L.rq_probe_barrier.restype = i
+            L.rq_probe_mfma.argtypes = [i, i, vp, vp]
+            L.rq_probe_mfma.restype = i
             L.rq_tuning_reload.argtypes = []
             L.rq_tuning_reload.restype = i
             ip = ctypes.POINTER(ctypes.c_int)

@@ -7,6 +7,12 @@ python -m gemm_rwkv_decode_amd.probe  prints one JSON object:
                 exceeds the 256 MB last-level cache (cold reads)
 Sizes default to one 4096x4096 and one 16384x4096 int4-g64 matrix (codes and
 scales) and 1 GiB.
+
+--sync adds "sync": the cost of cross-workgroup signalling (one arrival per
+workgroup after a __threadfence() against after device-scope coherent writes,
+per launch of 256..2048 workgroups) and the latency of one grid-wide barrier
+among co-resident workgroups, both ways, with the exchanged data checked.
+--mfma adds "mfma": the dense fp16 matrix-core rate (v_mfma_f32_16x16x32_f16).
 """
 import argparse
 import json
@@ -61,16 +67,87 @@ def probe(sizes=(8912896, 35651584, 1 << 30), cold_bytes=1 << 30,
     return out
 
 
+def sync_probe(grids=(256, 512, 1024, 2048), barrier_grids=(256, 512), rounds=1000,
+               spin=1 << 20):
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"signal": [], "barrier": []}
+    empty = _time_launches(lambda i: L.rq_probe_empty(stream), 500)
+    out["empty_us"] = empty * 1e6
+    for G in grids:
+        flags = torch.zeros(64 * (G + 1), dtype=torch.int32, device="cuda")
+        row = {"blocks": G}
+        for mode, name in ((0, "threadfence_us"), (1, "coherent_writes_us")):
+            def fn(i, mode=mode):
+                st = L.rq_probe_signal(flags.data_ptr(), mode, G, stream)
+                assert st == 0, st
+            fn(0)
+            row[name] = min(_time_launches(fn, 50) for _ in range(3)) * 1e6
+        row["fence_cost_per_workgroup_ns"] = (row["threadfence_us"] -
+                                              row["coherent_writes_us"]) * 1e3 / G
+        out["signal"].append(row)
+    for G in barrier_grids:
+        flags = torch.zeros(64 * (G + 1), dtype=torch.int32, device="cuda")
+        bad = torch.zeros(G, dtype=torch.int32, device="cuda")
+        row = {"blocks": G, "rounds": rounds, "barriers": 2 * rounds}
+        for mode, name in ((2, "coherent"), (3, "release_acquire")):
+            best = None
+            for _ in range(3):
+                flags.zero_()
+                bad.zero_()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                st = L.rq_probe_barrier(flags.data_ptr(), mode, G, rounds, spin,
+                                        bad.data_ptr(), stream)
+                b.record()
+                torch.cuda.synchronize()
+                if st != 0:
+                    row[name] = {"status": st}
+                    break
+                t = a.elapsed_time(b) * 1e-3
+                nb = bad.cpu()
+                r = {"us_per_barrier": t / (2 * rounds) * 1e6,
+                     "stale_reads": int((nb & 0xFFFF).sum()),
+                     "gave_up": int((nb >> 16).sum())}
+                if best is None or r["us_per_barrier"] < best["us_per_barrier"]:
+                    best = r
+            if best is not None:
+                row[name] = best
+        out["barrier"].append(row)
+    return out
+
+
+def mfma_probe(blocks=2048, iters=2000):
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    fn = lambda i: L.rq_probe_mfma(blocks, iters, sink.data_ptr(), stream)  # noqa: E731
+    fn(0)
+    t = min(_time_launches(fn, 5) for _ in range(3))
+    flops = blocks * 4 * iters * 8 * 16384
+    return {"instruction": "v_mfma_f32_16x16x32_f16", "blocks": blocks, "waves": blocks * 4,
+            "flops": flops, "us": t * 1e6, "tflops": flops / t / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--sizes", type=str, default=None,
                     help="comma-separated byte counts")
+    ap.add_argument("--sync", action="store_true")
+    ap.add_argument("--mfma", action="store_true")
+    ap.add_argument("--no-read", action="store_true")
     a = ap.parse_args()
     kw = {}
     if a.sizes:
         kw["sizes"] = tuple(int(s) for s in a.sizes.split(","))
     t = time.time()
-    r = probe(**kw)
+    r = {} if a.no_read else probe(**kw)
+    if a.mfma:
+        r["mfma"] = mfma_probe()
+    if a.sync:
+        r["sync"] = sync_probe()
     r["seconds"] = time.time() - t
     print(json.dumps(r), flush=True)
 

@@ -32,6 +32,32 @@ int rq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 /* One workgroup of 64 threads that does nothing. */
 int rq_probe_empty(void* stream);
 
+/* Cross-workgroup signalling cost.  `blocks` workgroups of 256 threads each
+ * write a 64-dword slot of `flags` and then count themselves in flags[0]:
+ * mode 0 with __threadfence() between the writes and the count (a device-scope
+ * release, which writes back the L2); mode 1 with device-scope coherent writes
+ * whose completion is awaited instead (no write-back).  flags: device memory
+ * of at least 64 * (blocks + 1) dwords, zeroed by the caller. */
+int rq_probe_signal(unsigned* flags, int mode, int blocks, void* stream);
+
+/* `rounds` grid-wide barriers among `blocks` co-resident workgroups (a
+ * cooperative launch: RQ_ERR_LAUNCH if they cannot all be resident).  Each
+ * round every workgroup writes its slot, arrives, waits for all, then reads
+ * its neighbour's slot; bad[b] (blocks entries) receives the number of stale
+ * values workgroup b read, plus 0x10000 if a wait gave up.  mode 2:
+ * device-scope coherent writes and reads, arrival once the writes are
+ * acknowledged; mode 3: plain writes, release arrival, acquire wait.  Every
+ * wait gives up after `spin` polls (about 1 us each) and then stops every
+ * workgroup, so the kernel always ends.  flags: at least 64 * (blocks + 1)
+ * dwords, zeroed by the caller. */
+int rq_probe_barrier(unsigned* flags, int mode, int blocks, int rounds, int spin,
+                     unsigned* bad, void* stream);
+
+/* Dense fp16 matrix-core rate: `blocks` workgroups of four waves, each wave
+ * issuing iters x 8 v_mfma_f32_16x16x32_f16 (16384 flops each) on eight
+ * independent accumulators.  sink: `blocks` floats (practically never written). */
+int rq_probe_mfma(int blocks, int iters, float* sink, void* stream);
+
 /* Re-read the launch-shape override variables (RQ_GEMV_LPR, RQ_GEMV_CPL,
  * RQ_GEMV_NPASS, RQ_GEMM_PLAN (1-based index of a workgroup arrangement of
  * the matrix-core kernel), RQ_GEMM_SPLITS, RQ_GEMV_KERNEL (the kernel of
