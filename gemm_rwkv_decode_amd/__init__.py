@@ -24,13 +24,14 @@ __all__ = [
     "RQ_OK", "RQ_LAYOUT_SYM", "RQ_LAYOUT_ASYM_SB", "RQ_LAYOUT_FP8_TENSOR", "RQ_OUT_F32",
     "RQ_OUT_CODES_I8",
     "RQ_MAX_M", "RQ_MAX_BATCH", "RqError", "RqLibraryMissing", "rq_dequant", "rq_gemv",
-    "rq_gemv_batched", "rq_gemm_smallm", "rq_status_string", "rq_version", "prepare",
-    "lib", "LIB_PATH",
+    "rq_gemv_batched", "rq_gemm_smallm", "rq_gemm_smallm_noalloc", "rq_status_string",
+    "rq_version", "prepare", "lib", "LIB_PATH",
 ]
 
 RQ_OK = 0
 RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED, RQ_ERR_ALIGN = 1, 2, 3, 4
-RQ_ERR_LAUNCH, RQ_ERR_ALIAS, RQ_ERR_DEVICE = 5, 6, 7
+RQ_ERR_LAUNCH, RQ_ERR_ALIAS, RQ_ERR_DEVICE, RQ_ERR_SCRATCH = 5, 6, 7, 8
+RQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 RQ_LAYOUT_SYM, RQ_LAYOUT_ASYM_SB, RQ_LAYOUT_FP8_TENSOR = 0, 1, 2
 RQ_OUT_F32, RQ_OUT_CODES_I8 = 0, 1
 RQ_MAX_M = 64
@@ -70,7 +71,7 @@ def lib():
             vp, i = ctypes.c_void_p, ctypes.c_int
             L.rq_dequant.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
             L.rq_dequant.restype = i
-            for name in ("rq_gemv", "rq_gemm_smallm"):
+            for name in ("rq_gemv", "rq_gemm_smallm", "rq_gemm_smallm_noalloc"):
                 f = getattr(L, name)
                 f.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
                 f.restype = i
@@ -159,6 +160,18 @@ def rq_gemm_smallm(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
                               _stream(stream, qweight))
     if st != RQ_OK:
         raise RqError("rq_gemm_smallm", st)
+    return y
+
+
+def rq_gemm_smallm_noalloc(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
+                           stream=None):
+    """rq_gemm_smallm with its split-K partial sums in the library's fixed
+    device array: never allocates; calls overlapping on one GPU race."""
+    st = lib().rq_gemm_smallm_noalloc(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x),
+                                      _ptr(y), int(M), int(N), int(K), int(bits), int(group),
+                                      int(layout), _stream(stream, qweight))
+    if st != RQ_OK:
+        raise RqError("rq_gemm_smallm_noalloc", st)
     return y
 
 

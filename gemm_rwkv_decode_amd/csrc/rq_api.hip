@@ -170,6 +170,33 @@ float* stream_workspace(int dev, hipStream_t stream) {
   return p;
 }
 
+// Split-K scratch of rq_gemm_smallm_noalloc: a fixed device array (each GPU
+// the library runs on holds its own copy until the process ends), so that
+// entry point never allocates.  Its size covers every split the automatic
+// choice makes (at most 4 K-ranges x 64 rows x 8191 outputs of binary32).
+constexpr size_t SCRATCH_BYTES = (size_t)RQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[SCRATCH_BYTES / sizeof(float)];
+
+// The device address of this GPU's `scratch`, looked up once per device with
+// that device current (host code must never pass the array's own name: on the
+// host it is only a stand-in).  NULL if the lookup fails.
+float* device_scratch(int dev) {
+  static std::mutex mu;
+  static float* addr[64];
+  static bool looked[64];
+  std::lock_guard<std::mutex> lk(mu);
+  if (!looked[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = static_cast<float*>(p);
+    looked[dev] = true;
+  }
+  return addr[dev];
+}
+
 rq_status check_product(const void* qweight, const void* scales, const void* zeros,
                         const void* x, float* y, int M, int N, int K, int bits, int group,
                         int layout, int* fmt) {
@@ -383,6 +410,35 @@ rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* ze
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 
+rq_status rq_gemm_smallm_noalloc(const void* qweight, const void* scales, const void* zeros,
+                                 const void* x, float* y, int M, int N, int K, int bits,
+                                 int group, int layout, void* stream) {
+  int fmt = -1;
+  rq_status st =
+      check_product(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, &fmt);
+  if (st != RQ_OK) return st;
+  int dev;
+  st = check_device(&dev);
+  if (st != RQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  rq::Problem p{qweight, scales, zeros, x, y, M, N, K, group, fmt};
+  if (!rq::gemm_supports(fmt, M, K, group)) {
+    const rq::GemvCfg c = rq::choose_gemv(fmt, M, N, K);
+    return rq::launch_gemv(p, c, s) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
+  }
+  // the same arrangement rq_gemm_smallm chooses, partial sums in `scratch`
+  const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
+  float* ws = nullptr;
+  if (c.splits > 1) {
+    if (rq::gemm_workspace_floats(c, M, N) * sizeof(float) > SCRATCH_BYTES)
+      return RQ_ERR_SCRATCH;
+    ws = device_scratch(dev);
+    if (!ws) return RQ_ERR_DEVICE;
+  }
+  const hipError_t e = rq::launch_gemm(p, c, ws, s);
+  return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
+}
+
 const char* rq_status_string(int status) {
   switch (status) {
     case RQ_OK: return "success";
@@ -393,6 +449,7 @@ const char* rq_status_string(int status) {
     case RQ_ERR_LAUNCH: return "the kernel launch failed";
     case RQ_ERR_ALIAS: return "an output overlaps an input";
     case RQ_ERR_DEVICE: return "no usable gfx950 device";
+    case RQ_ERR_SCRATCH: return "the call needs more scratch than the fixed device array holds";
     default: return "unknown status";
   }
 }

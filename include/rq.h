@@ -88,7 +88,9 @@ typedef enum {
     RQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
     RQ_ERR_LAUNCH = 5,      /* the kernel launch was rejected by the runtime    */
     RQ_ERR_ALIAS = 6,       /* an output range overlaps an input range          */
-    RQ_ERR_DEVICE = 7       /* no usable gfx950 device                           */
+    RQ_ERR_DEVICE = 7,      /* no usable gfx950 device                           */
+    RQ_ERR_SCRATCH = 8      /* rq_gemm_smallm_noalloc: the partial sums would not
+                               fit its fixed scratch array                       */
 } rq_status;
 
 typedef enum { RQ_LAYOUT_SYM = 0, RQ_LAYOUT_ASYM_SB = 1, RQ_LAYOUT_FP8_TENSOR = 2 } rq_layout;
@@ -195,6 +197,27 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
 rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* zeros,
                          const void* x, float* y, int M, int N, int K, int bits,
                          int group, int layout, void* stream);
+
+/* Bytes of the fixed device array behind rq_gemm_smallm_noalloc. */
+#define RQ_NOALLOC_SCRATCH_BYTES (8 << 20)
+
+/*
+ * rq_gemm_smallm_noalloc -- rq_gemm_smallm for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation): same arguments, same kernels, same arrangement and
+ * K split, same results bit for bit, but the split-K partial sums go to a
+ * fixed device array of RQ_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends.  The call never allocates, frees
+ * or synchronizes.  The array covers every split the automatic choice makes;
+ * a call whose partial sums would exceed it (only with a forced split count)
+ * returns RQ_ERR_SCRATCH and enqueues nothing.  Every partial sum is written
+ * before it is read, so nothing needs clearing between calls, but all calls
+ * on one GPU share the array: calls that may overlap in time on one GPU (on
+ * different streams, or graphs replayed concurrently) race on it.
+ */
+rq_status rq_gemm_smallm_noalloc(const void* qweight, const void* scales, const void* zeros,
+                                 const void* x, float* y, int M, int N, int K, int bits,
+                                 int group, int layout, void* stream);
 
 /* A static, NUL-terminated English description of a status value. */
 const char* rq_status_string(int status);

@@ -47,7 +47,7 @@ def test_exports_every_declared_function(L):
 
 def test_status_values_match_header():
     for n in ["RQ_OK", "RQ_ERR_NULL", "RQ_ERR_SHAPE", "RQ_ERR_UNSUPPORTED", "RQ_ERR_ALIGN",
-              "RQ_ERR_LAUNCH", "RQ_ERR_ALIAS", "RQ_ERR_DEVICE", "RQ_LAYOUT_SYM",
+              "RQ_ERR_LAUNCH", "RQ_ERR_ALIAS", "RQ_ERR_DEVICE", "RQ_ERR_SCRATCH", "RQ_LAYOUT_SYM",
               "RQ_LAYOUT_ASYM_SB", "RQ_LAYOUT_FP8_TENSOR", "RQ_OUT_F32", "RQ_OUT_CODES_I8"]:
         assert getattr(rq, n) == header_enum(n), n
     assert rq.RQ_MAX_M == int(re.search(r"#define RQ_MAX_M (\d+)", open(HEADER).read()).group(1))
@@ -56,7 +56,7 @@ def test_status_values_match_header():
 def test_version_and_strings(L):
     assert rq.rq_version() == (1 << 16)
     seen = set()
-    for s in range(8):
+    for s in range(9):
         t = rq.rq_status_string(s)
         assert t and t not in seen
         seen.add(t)
@@ -125,7 +125,7 @@ GEMV_ONLY = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["rq_gemv", "rq_gemm_smallm"])
+@pytest.mark.parametrize("fn", ["rq_gemv", "rq_gemm_smallm", "rq_gemm_smallm_noalloc"])
 @pytest.mark.parametrize("what,kw,status", CASES + GEMV_ONLY, ids=[c[0] for c in CASES + GEMV_ONLY])
 def test_product_rejects(L, fn, what, kw, status):
     assert getattr(L, fn)(*gemv_args(**kw)) == status, what
@@ -153,6 +153,7 @@ def test_valid_call_without_gpu_reports_device(L):
         pytest.skip("a GPU is present")
     assert L.rq_gemv(*gemv_args()) == rq.RQ_ERR_DEVICE
     assert L.rq_gemm_smallm(*gemv_args(M=32)) == rq.RQ_ERR_DEVICE
+    assert L.rq_gemm_smallm_noalloc(*gemv_args(M=32)) == rq.RQ_ERR_DEVICE
     assert L.rq_dequant(*dq_args()) == rq.RQ_ERR_DEVICE
 
 
