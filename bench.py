@@ -2,18 +2,22 @@
 13.3B-shaped RWKV-7 model (61 layers x 6 quantized matrices at width 4096,
 FFN 16384), on one MI355X.
 
-One step = one pass of the decode hot path: every one of the 367 matrices (366
-layer matrices and the 65536x4096 head) is multiplied by its own activation
-row (M = 1), in dependency order, on one stream (gemm_rwkv_decode_amd.step,
-kind "layer": receptance/key/value of a layer in one rq_gemv_batched launch,
-the rest through rq_gemv).  Inputs (6.67 GB of packed codes and scales, the
-activations) are generated on the GPU from their seeds and are resident in HBM
-before the timed region.  The same step at M = 16, 32 and 64 (rq_gemm_smallm,
-matrix cores) gives the TFLOP/s figures; M = 32 is the headline one.
+One step = one pass of the decode hot path: every one of the 366 layer
+matrices is multiplied by its own activation row (M = 1), in dependency order,
+on one stream (gemm_rwkv_decode_amd.step, kind "layer": receptance/key/value
+of a layer in one rq_gemv_batched launch, the rest through rq_gemv).  The same
+step followed by the 65536x4096 vocabulary head (6.68 GB) is reported beside
+it.  Inputs (packed codes and scales, the activations) are generated on the
+GPU from their seeds and are resident in HBM before the timed region.  The
+same step at M = 16, 32 and 64 (rq_gemm_smallm, matrix cores) gives the
+TFLOP/s figures; M = 32 is the headline one.
 
 Prints one JSON line (rank 0):
-  value       algorithmic bytes per step / step time, GB/s (M = 1)
-  roofline    the dominant kernel (FFN 16384x4096 or 4096x16384) against 8 TB/s
+  value       algorithmic bytes per step / step time, GB/s (M = 1, no head)
+  roofline    the dominant kernel (FFN 4096x16384 or 16384x4096) against 8 TB/s:
+              algorithmic bytes of one launch / its average time, from events
+              around back-to-back launches of that shape (the per-shape leg;
+              `--roofline-only` runs that leg alone, for the kernel trace)
   cpu_baseline the CPU oracle, single-threaded, on a bounded sample of the same
               step (its first layers), GB/s of algorithmic bytes
 """
@@ -28,12 +32,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "int4-g64 GEMV HBM GB/s (% of peak) at D=4096 M=1; TFLOP/s at M=32"
-# HBM bytes per launch of the dominant kernel, measured with rocprofv3 memory
-# counters; valid only while the kernel sources hash to the recorded value.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rq_gemv_int4g64_4096x16384_m1_traffic.json")
+# The dominant kernel's record from rocprofv3 (its duration in a trace of the
+# per-shape leg alone, and HBM bytes per launch from the memory counters);
+# valid only while the kernel's sources hash to the recorded value.
+RECORD_FILE = os.path.join(ROOT, "profiles", "rq_gemv_int4g64_4096x16384_m1_roofline.json")
 KERNEL_SOURCES = ["gemm_rwkv_decode_amd/csrc/rq_gemv.hip",
-                  "gemm_rwkv_decode_amd/csrc/rq_common.h",
-                  "gemm_rwkv_decode_amd/csrc/rq_internal.h"]
+                  "gemm_rwkv_decode_amd/csrc/rq_common.h"]
 
 
 def kernel_source_hash():
@@ -45,17 +49,17 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(shape):
-    """Counter-measured bytes per launch for `shape`, or None if absent or the
-    kernel has changed since the counters were taken."""
+def recorded(shape):
+    """The rocprofv3 record of the dominant kernel for `shape`, or {} if absent
+    or the kernel has changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(RECORD_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("source_sha256") != kernel_source_hash() or t.get("shape") != shape:
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    return t
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
@@ -84,7 +88,30 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 64 MiB with rq_probe_copy (the reference kernel "
                          "for scaling the memory-traffic counters)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="run only the per-shape leg whose dominant kernel gives the "
+                         "roofline (for tracing exactly those launches)")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the 768-wide single-matrix and 0.1B-shaped step legs")
     return ap.parse_args()
+
+
+def host_cpu():
+    """Model name and usable core count of the host CPU."""
+    name = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": name, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
 
 
 def main():
@@ -111,26 +138,33 @@ def main():
         del a, b
     cfg = S.CONFIGS["rwkv7-13.3b"]
     fmt = S.INT4_G64
-    mats = cfg.matrices()
+    mats_all = cfg.matrices(with_head=True)
     if args.layers is not None:
-        mats = [m for m in mats if m[0] < args.layers]
-    nlayers = len({m[0] for m in mats if m[1] != ST.HEAD})
-    mfma_ms = [16, 32, 64]
+        mats_all = [m for m in mats_all if m[0] < args.layers or m[1] == ST.HEAD]
+    nlayers = len({m[0] for m in mats_all if m[1] != ST.HEAD})
+    mfma_ms = [] if args.roofline_only else [16, 32, 64]
 
     # ---- inputs, resident in HBM --------------------------------------------
     t0 = time.time()
-    W = [S.gen_matrix(cfg.key, l, mi, N, K, fmt, device=dev) for (l, mi, N, K) in mats]
-    X = {M: [S.gen_x(cfg, l, mi, M, K, device=dev) for (l, mi, N, K) in mats]
-         for M in [1] + mfma_ms}
-    Y = {M: [torch.empty((M, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
-         for M in [1] + mfma_ms}
+    W_all = [S.gen_matrix(cfg.key, l, mi, N, K, fmt, device=dev) for (l, mi, N, K) in mats_all]
+    X_all = {M: [S.gen_x(cfg, l, mi, M, K, device=dev) for (l, mi, N, K) in mats_all]
+             for M in [1] + mfma_ms}
+    Y_all = {M: [torch.empty((M, N), dtype=torch.float32, device=dev)
+                 for (_, _, N, _) in mats_all] for M in [1] + mfma_ms}
     torch.cuda.synchronize()
-    log(f"generated {len(mats)} matrices in {time.time() - t0:.1f}s")
+    log(f"generated {len(mats_all)} matrices in {time.time() - t0:.1f}s")
+    # the headline step: the layer matrices (the head is timed beside it)
+    lay = [i for i, m in enumerate(mats_all) if m[1] != ST.HEAD]
+    mats = [mats_all[i] for i in lay]
+    W = [W_all[i] for i in lay]
+    X = {M: [X_all[M][i] for i in lay] for M in X_all}
+    Y = {M: [Y_all[M][i] for i in lay] for M in Y_all}
 
-    weight_bytes = sum(fmt.weight_bytes(N, K) for (_, _, N, K) in mats)
+    def bytes_of(ms, M):
+        return sum(fmt.weight_bytes(N, K) + 2 * M * K + 4 * M * N for (_, _, N, K) in ms)
 
     def step_bytes(M):
-        return weight_bytes + sum(2 * M * K + 4 * M * N for (_, _, N, K) in mats)
+        return bytes_of(mats, M)
 
     flops_per_m = sum(2 * N * K for (_, _, N, K) in mats)
 
@@ -170,13 +204,22 @@ def main():
 
     # ---- M = 1: the headline (dependency-ordered decode step) ---------------
     scheds = {}
-    for kind in ST.KINDS:
-        log(f"timing M=1 schedule {kind}")
-        sec, ncalls = timed(kind, 1, args.steps, args.warmup, args.graph)
-        scheds[kind] = {"launch_calls": ncalls, "ms_per_step": round(sec * 1e3, 4),
-                        "GBps": round(step_bytes(1) / sec / 1e9, 2)}
-    sec1 = scheds["layer"]["ms_per_step"] * 1e-3
-    gbs = step_bytes(1) / sec1 / 1e9
+    with_head = None
+    if not args.roofline_only:
+        for kind in ST.KINDS:
+            log(f"timing M=1 schedule {kind}")
+            sec, ncalls = timed(kind, 1, args.steps, args.warmup, args.graph)
+            scheds[kind] = {"launch_calls": ncalls, "ms_per_step": round(sec * 1e3, 4),
+                            "GBps": round(step_bytes(1) / sec / 1e9, 2)}
+        log("timing M=1 step with the head")
+        sec, ncalls = timed("layer", 1, args.steps, args.warmup, args.graph,
+                            step=(mats_all, W_all, X_all[1], Y_all[1]))
+        hb = bytes_of(mats_all, 1)
+        with_head = {"matrices": len(mats_all), "launch_calls": ncalls, "bytes_per_step": hb,
+                     "ms_per_step": round(sec * 1e3, 4), "GBps": round(hb / sec / 1e9, 2),
+                     "pct_of_hbm_peak": round(100 * hb / sec / 1e9 / HBM_PEAK_GBS, 2)}
+        sec1 = scheds["layer"]["ms_per_step"] * 1e-3
+        gbs = step_bytes(1) / sec1 / 1e9
 
     # ---- per-shape launch time: events around back-to-back launches of one
     # shape over all layers (distinct, cold matrices), same stream -----------
@@ -190,11 +233,12 @@ def main():
         nbytes[key] = b
 
     by_layer = {}
-    for i, (l, mi, N, K) in enumerate(mats):
+    for i, (l, mi, N, K) in enumerate(mats_all):
         by_layer.setdefault(l, {})[mi] = i
+    mats_pl, W_pl, X_pl, Y_pl = mats_all, W_all, X_all[1], Y_all[1]
 
     def mbytes(i):
-        _, _, N, K = mats[i]
+        _, _, N, K = mats_pl[i]
         return fmt.weight_bytes(N, K) + 2 * K + 4 * N
 
     for l in sorted(by_layer):
@@ -202,14 +246,14 @@ def main():
         if ST.RECEPTANCE in ix:
             rkv = [ix[m] for m in (ST.RECEPTANCE, ST.KEY, ST.VALUE)]
             add("rkv batched 3x(4096x4096)",
-                ST.step_calls([mats[i] for i in rkv], [W[i] for i in rkv],
-                              [X[1][i] for i in rkv], [Y[1][i] for i in rkv], "layer")[0],
+                ST.step_calls([mats_pl[i] for i in rkv], [W_pl[i] for i in rkv],
+                              [X_pl[i] for i in rkv], [Y_pl[i] for i in rkv], "layer")[0],
                 sum(mbytes(i) for i in rkv))
         for m in (ST.OUTPUT, ST.FFN_KEY, ST.FFN_VALUE, ST.HEAD):
             if m in ix:
                 i = ix[m]
-                _, _, N, K = mats[i]
-                add(f"{N}x{K}", ST.step_calls([mats[i]], [W[i]], [X[1][i]], [Y[1][i]],
+                _, _, N, K = mats_pl[i]
+                add(f"{N}x{K}", ST.step_calls([mats_pl[i]], [W_pl[i]], [X_pl[i]], [Y_pl[i]],
                                                "matrix")[0], mbytes(i))
     stream = torch.cuda.current_stream()
     for key, calls in groups.items():
@@ -228,8 +272,48 @@ def main():
         avg = min(ts)
         per_kernel[key] = {"us_per_launch": round(avg * 1e6, 3), "launches_per_step": len(calls),
                            "bytes": nbytes[key], "GBps": round(nbytes[key] / avg / 1e9, 1)}
-    dom_name, dom_v = max(per_kernel.items(),
+    # the dominant kernel of the headline step (the head is not in it)
+    dom_name, dom_v = max(((k, v) for k, v in per_kernel.items() if k != "65536x4096"),
                           key=lambda kv: kv[1]["us_per_launch"] * kv[1]["launches_per_step"])
+    roofline = {"bound": "hbm", "kernel": f"int4 g64 GEMV {dom_name}, M=1",
+                "achieved": dom_v["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_v["GBps"] / HBM_PEAK_GBS, 4),
+                "us_per_launch": dom_v["us_per_launch"], "bytes_per_launch": dom_v["bytes"],
+                "timing": "HIP events around back-to-back launches of the shape over the "
+                          "61 layers (distinct, cold matrices) on the launch stream",
+                "traffic": recorded(dom_name).get("bytes_per_launch"),
+                "traffic_unit": "HBM bytes per launch: FETCH_SIZE and WRITE_SIZE per "
+                                "dispatch, each scaled by what it reads for a 64 MiB copy",
+                "trace_avg_us": recorded(dom_name).get("trace_avg_us"),
+                "trace_frac": (round(dom_v["bytes"] / recorded(dom_name)["trace_avg_us"]
+                                     / 1e6 / HBM_PEAK_GBS * 1e3, 4)
+                               if recorded(dom_name).get("trace_avg_us") else None),
+                "trace_record": os.path.relpath(RECORD_FILE, ROOT)}
+    if args.roofline_only:
+        print(json.dumps({"metric": METRIC, "roofline_only": True, "roofline": roofline,
+                          "per_shape_m1": per_kernel}), flush=True)
+        return
+
+    # ---- the dense fp16 matrix-core rate of this GPU (rq_probe_mfma) --------
+    sink = torch.zeros(2048, dtype=torch.float32, device=dev)
+    pk = {}
+    for shape, name in ((0, "v_mfma_f32_16x16x32_f16"), (1, "v_mfma_f32_32x32x16_f16")):
+        fn = lambda: rq.lib().rq_probe_mfma(2048, 2000, shape, sink.data_ptr(),  # noqa: E731
+                                            torch.cuda.current_stream().cuda_stream)
+        fn()
+        torch.cuda.synchronize()
+        best = 1e9
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(e) * 1e-3)
+        pk[name] = round(2048 * 4 * 2000 * 8 * 16384 / best / 1e12, 1)
+    mfma_peak = max(pk.values())
+    del sink
 
     # ---- M = 16, 32, 64 (matrix cores) ---------------------------------------
     mfma = {}
@@ -237,12 +321,77 @@ def main():
         log(f"timing M={M}")
         sec, ncalls = timed("layer", M, args.m32_steps, 2, args.graph)
         tf = M * flops_per_m / sec / 1e12
+        sb = step_bytes(M)
         mfma[str(M)] = {"entry": "rq_gemm_smallm", "launch_calls": ncalls,
                         "ms_per_step": round(sec * 1e3, 4), "tflops": round(tf, 2),
                         "pct_of_fp16_mfma_peak": round(100 * tf / FP16_MFMA_PEAK_TFLOPS, 2),
-                        "GBps": round(step_bytes(M) / sec / 1e9, 2),
-                        "pct_of_hbm_peak": round(100 * step_bytes(M) / sec / 1e9 / HBM_PEAK_GBS,
-                                                 2)}
+                        "pct_of_measured_fp16_mfma_peak": round(100 * tf / mfma_peak, 2),
+                        "GBps": round(sb / sec / 1e9, 2),
+                        "pct_of_hbm_peak": round(100 * sb / sec / 1e9 / HBM_PEAK_GBS, 2),
+                        "hbm_bound_ms": round(sb / HBM_PEAK_GBS / 1e6, 4),
+                        "frac_of_hbm_roofline": round(sb / HBM_PEAK_GBS / 1e9 / sec, 4)}
+
+    # ---- the 768-wide workloads: one 768x768 matrix, and the 0.1B-shaped
+    # step (12 layers x 6 matrices) ---------------------------------------------
+    small = None
+    if not args.no_small:
+        small = {}
+        c0 = S.CONFIGS["gemv768"]
+        w0 = S.gen_matrix(c0.key, 0, 0, 768, 768, fmt, device=dev)
+        x0 = S.gen_x(c0, 0, 0, 1, 768, device=dev)
+        y0 = torch.empty((1, 768), dtype=torch.float32, device=dev)
+        b0 = fmt.weight_bytes(768, 768) + 2 * 768 + 4 * 768
+        n_warm = 200
+        log("768x768: one matrix, back-to-back calls")
+        sec, _ = timed("matrix", 1, args.steps, 2, True,
+                       step=([(i, 0, 768, 768) for i in range(n_warm)], [w0] * n_warm,
+                             [x0] * n_warm, [y0] * n_warm))
+        reps0 = 2000
+        log(f"768x768: {reps0} distinct matrices")
+        w0s = [S.gen_matrix(c0.key + "-replica", r, 0, 768, 768, fmt, device=dev)
+               for r in range(reps0)]
+        secc, _ = timed("matrix", 1, max(2, args.steps // 10), 1, True,
+                        step=([(i, 0, 768, 768) for i in range(reps0)], w0s, [x0] * reps0,
+                              [y0] * reps0))
+        del w0s
+        small["gemv768"] = {
+            "workload": "single int4 g64 GEMV 768x768, M=1",
+            "bytes_per_call": b0,
+            "us_per_call_same_matrix": round(sec / n_warm * 1e6, 3),
+            "cold": {"matrices": reps0, "bytes": reps0 * b0,
+                     "us_per_call": round(secc / reps0 * 1e6, 3),
+                     "GBps": round(reps0 * b0 / secc / 1e9, 1)},
+            "timing": "graph replay of back-to-back rq_gemv calls"}
+        c1 = S.CONFIGS["rwkv7-0.1b"]
+        m1 = c1.matrices()
+        nrep = 12
+        log(f"0.1B-shaped step: {nrep} replicas")
+        W1 = [[S.gen_matrix(f"{c1.key}-replica{r}", l, mi, N, K, fmt, device=dev)
+               for (l, mi, N, K) in m1] for r in range(nrep)]
+        X1 = [S.gen_x(c1, l, mi, 1, K, device=dev) for (l, mi, N, K) in m1]
+        Y1 = [torch.empty((1, N), dtype=torch.float32, device=dev) for (_, _, N, _) in m1]
+        b1 = bytes_of(m1, 1)
+        sec_w, nc = timed("layer", 1, args.steps, args.warmup, args.graph,
+                          step=(m1, W1[0], X1, Y1))
+        mc = [(l + c1.layers * r, mi, N, K) for r in range(nrep) for (l, mi, N, K) in m1]
+        sec_c, _ = timed("layer", 1, max(2, args.steps // 4), 2, args.graph,
+                         step=(mc, [w for r in range(nrep) for w in W1[r]], X1 * nrep,
+                               Y1 * nrep))
+        sec_c /= nrep
+        del W1
+        small["rwkv7-0.1b"] = {
+            "workload": "RWKV-7 0.1B-shaped decode step, int4 g64, M=1: 12 layers x "
+                        "(4 x 768x768, 3072x768, 768x3072)",
+            "launch_calls": nc, "bytes_per_step": b1,
+            "cache_resident": {"ms_per_step": round(sec_w * 1e3, 4),
+                               "GBps": round(b1 / sec_w / 1e9, 1),
+                               "note": "the same 45 MB replica every step (fits the "
+                                       "256 MB last-level cache)"},
+            "cold": {"replicas": nrep, "ms_per_step": round(sec_c * 1e3, 4),
+                     "GBps": round(b1 / sec_c / 1e9, 1),
+                     "note": f"{nrep} distinct replicas in turn "
+                             f"({nrep * b1 / 1e6:.0f} MB between reuses)"}}
+        torch.cuda.empty_cache()
 
     # ---- FP8 E4M3 per-tensor weights (W8A16), M = 1 --------------------------
     # The page's FP8 model shape: width 4096, 32 layers.  Eight distinct weight
@@ -459,7 +608,7 @@ def main():
         dt = time.perf_counter() - t
         sb = sum(fmt.weight_bytes(N, K) + 2 * K + 4 * N for (_, _, _, (_, _, N, K)) in host)
         cpu = {"value": round(sb / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
+               "kind": "oracle", "host_cpu": host_cpu(),
                "sample": f"first {args.cpu_layers} layers ({len(sample)} matrices, "
                          f"{sb / 1e6:.1f} MB) of the same M=1 step, single thread, "
                          f"{dt:.1f} s"}
@@ -489,25 +638,28 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "launch_mode": "graph" if args.graph else "stream",
         "schedule": "per layer: one grouped launch for receptance/key/value, then output, "
-                    f"FFN key, FFN value; the head last ({scheds['layer']['launch_calls']} "
-                    "launches per step)",
+                    f"FFN key, FFN value ({scheds['layer']['launch_calls']} launches per "
+                    "step)",
         "schedules_m1": scheds,
         "config": {"workload": "RWKV-7 13.3B-shaped decode weight stream, int4 sym g64: "
-                               "61 layers x (4 x 4096x4096, 16384x4096, 4096x16384) "
-                               "+ head 65536x4096",
+                               "61 layers x (4 x 4096x4096, 16384x4096, 4096x16384)",
                    "layers": nlayers, "matrices": len(mats), "M": 1,
                    "bytes_per_step": step_bytes(1)},
+        "with_head_m1": dict(with_head, workload="the same step followed by the 65536x4096 "
+                                                 "vocabulary head"),
         "m32": mfma["32"],
         "mfma_m": mfma,
+        "fp16_mfma_peak_measured_tflops": {"best": mfma_peak, "by_instruction": pk,
+                                           "probe": "rq_probe_mfma, 2048 workgroups"},
+        "mfma_utilization_m64": {
+            "value": round(mfma["64"]["tflops"] / mfma_peak, 4),
+            "what": "achieved TFLOP/s of the M=64 step / measured dense fp16 peak; the "
+                    "matrix-core busy cycles from counters are in profiles/"},
+        "small_workloads_m1": small,
         "fp8_w8a16_m1": fp8,
         "asym_5_6_bit_m1": hib,
         "per_shape_m1": per_kernel,
-        "roofline": {"bound": "hbm", "kernel": f"int4 g64 GEMV {dom_name}, M=1",
-                     "achieved": dom_v["GBps"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_v["GBps"] / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(dom_name),
-                     "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, "
-                                     "scaled by a 64 MiB copy)"},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_oracle_threads": cpu_threads,
         "vs_fp16_dense": dense,

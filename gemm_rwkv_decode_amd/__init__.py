@@ -92,7 +92,7 @@ def lib():
             L.rq_probe_signal.restype = i
             L.rq_probe_barrier.argtypes = [vp, i, i, i, i, vp, vp]
             L.rq_probe_barrier.restype = i
-            L.rq_probe_mfma.argtypes = [i, i, vp, vp]
+            L.rq_probe_mfma.argtypes = [i, i, i, vp, vp]
             L.rq_probe_mfma.restype = i
             L.rq_tuning_reload.argtypes = []
             L.rq_tuning_reload.restype = i

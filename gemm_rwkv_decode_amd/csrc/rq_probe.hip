@@ -86,92 +86,127 @@ __global__ void __launch_bounds__(256) k_probe_signal(unsigned* flags, int mode)
   if (t == 0) __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Layout of the barrier probe's flags buffer (dwords): arrival counters
+// (one per 128-byte line), the abort flag, one arrival word per workgroup
+// (contiguous), then the 64-dword data slots.
+constexpr int BAR_CTR_LINE = 32;
+constexpr int BAR_NCTR = 32;
+constexpr int BAR_ABORT = BAR_CTR_LINE * BAR_NCTR;
+constexpr int BAR_WGFLAG = BAR_ABORT + 64;
+
+__device__ __forceinline__ unsigned wave_sum(unsigned v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One barrier phase for workgroup b of G: arrive (after this workgroup's
+// writes), then wait until every workgroup has arrived `phase` times.  Wave 0
+// does the arriving and polling; the others wait at the workgroup barrier.
+// Returns false if the wait gave up (after `spin` polls) or another
+// workgroup did.
+//   mode 2: one counter, relaxed device-scope atomics, coherent writes;
+//   mode 3: one counter, release arrival and acquire polls;
+//   mode 4: 32 counters on separate lines (workgroup b arrives on b mod 32),
+//           the poll sums them with one load per lane;
+//   mode 5: no atomics: workgroup b stores `phase` in its own word, the poll
+//           reads all words (G/64 loads per lane) and checks them all.
+__device__ bool bar_phase(unsigned* flags, int mode, unsigned phase, int spin) {
+  const int t = threadIdx.x;
+  const unsigned G = gridDim.x, b = blockIdx.x;
+  __shared__ int ok;
+  if (t < 64) {
+    const int lane = t;
+    if (lane == 0) {
+      if (mode == 2) {
+        __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (mode == 3) {
+        __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (mode == 4) {
+        __hip_atomic_fetch_add(flags + (b % BAR_NCTR) * BAR_CTR_LINE, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        store_agent(flags + BAR_WGFLAG + b, phase);
+      }
+    }
+    int n = 0;
+    bool done = false, gave_up = false;
+    while (!done) {
+      if (mode == 2 || mode == 3) {
+        const unsigned c = mode == 2 ? load_agent(flags)
+                                     : __hip_atomic_load(flags, __ATOMIC_ACQUIRE,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+        done = c >= phase * G;
+      } else if (mode == 4) {
+        const unsigned c = lane < BAR_NCTR ? load_agent(flags + lane * BAR_CTR_LINE) : 0u;
+        done = wave_sum(c) >= phase * G;
+      } else {
+        bool all = true;
+        for (unsigned w = lane; w < G; w += 64) all &= load_agent(flags + BAR_WGFLAG + w) >= phase;
+        done = __all(all);
+      }
+      if (done) break;
+      if (load_agent(flags + BAR_ABORT) != 0u || ++n >= spin) {
+        if (lane == 0) store_agent(flags + BAR_ABORT, 1u);
+        gave_up = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) ok = gave_up ? 0 : 1;
+  }
+  __syncthreads();
+  return ok != 0;
+}
+
 // `rounds` grid-wide barriers; every workgroup must be resident (cooperative
-// launch).  In round r each workgroup writes r + 1 into its slot, arrives, waits
-// until all have arrived, then reads its neighbour's slot and counts values
-// other than r + 1 into bad[blockIdx].  mode 2: device-scope stores and loads,
-// arrival after the stores are acknowledged; mode 3: plain stores, release
-// arrival, acquire wait.  Every wait is bounded: after `spin` polls the
-// workgroup raises the abort flag, and every workgroup stops at the next poll.
+// launch).  In round r each workgroup writes r + 1 into its 64-dword slot,
+// passes a barrier, reads its neighbour's slot and counts values other than
+// r + 1 into bad[blockIdx], then passes a second barrier before the slot is
+// rewritten.  Writes and reads of the slots are device-scope coherent (mode 3:
+// plain, ordered by the release/acquire of the barrier); a write is awaited
+// before the arrival.  Every wait is bounded: after `spin` polls a workgroup
+// raises the abort flag, and every workgroup stops at its next poll.
 __global__ void __launch_bounds__(256)
 k_probe_barrier(unsigned* flags, int mode, int rounds, int spin, unsigned* bad) {
   const int t = threadIdx.x;
   const unsigned G = gridDim.x;
-  unsigned* slot = flags + SYNC_SLOT + SYNC_SLOT * blockIdx.x;
-  const unsigned* peer = flags + SYNC_SLOT + SYNC_SLOT * ((blockIdx.x + 1) % G);
+  const unsigned gpad = (G + 63) / 64 * 64;
+  unsigned* slots = flags + BAR_WGFLAG + gpad;
+  unsigned* slot = slots + SYNC_SLOT * blockIdx.x;
+  const unsigned* peer = slots + SYNC_SLOT * ((blockIdx.x + 1) % G);
   unsigned nbad = 0;
-  __shared__ int stop;
-  if (t == 0) stop = 0;
-  __syncthreads();
-  for (int r = 0; r < rounds; r++) {
+  bool stopped = false;
+  for (int r = 0; r < rounds && !stopped; r++) {
     if (t < SYNC_SLOT) {
-      if (mode == 2) store_agent(slot + t, (unsigned)r + 1);
-      else slot[t] = (unsigned)r + 1;
+      if (mode == 3) slot[t] = (unsigned)r + 1;
+      else store_agent(slot + t, (unsigned)r + 1);
     }
-    if (mode == 2) __builtin_amdgcn_s_waitcnt(0);
+    if (mode != 3) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t == 0) {
-      if (mode == 2)
-        __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      // two arrivals per workgroup and round: after the first of round r
-      // the count reaches (2r + 1) G
-      const unsigned want = (unsigned)(2 * r + 1) * G;
-      int n = 0;
-      for (;;) {
-        const unsigned c = mode == 2
-            ? load_agent(flags)
-            : __hip_atomic_load(flags, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        if (c >= want) break;
-        if (load_agent(flags + 1) != 0u || ++n >= spin) {
-          store_agent(flags + 1, 1u);
-          stop = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
+    if (!bar_phase(flags, mode, 2u * r + 1u, spin)) {
+      stopped = true;
+      break;
     }
-    __syncthreads();
-    if (stop) break;
     if (t < SYNC_SLOT) {
-      const unsigned v = mode == 2 ? load_agent(peer + t) : peer[t];
+      const unsigned v = mode == 3 ? peer[t] : load_agent(peer + t);
       nbad += (v != (unsigned)r + 1);
     }
-    // nobody overwrites a slot before its reader is done with it
-    __syncthreads();
-    if (t == 0) {
-      if (mode == 2)
-        __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        __hip_atomic_fetch_add(flags, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned want = (unsigned)(2 * r + 2) * G;
-      int n = 0;
-      for (;;) {
-        const unsigned c = load_agent(flags);
-        if (c >= want) break;
-        if (load_agent(flags + 1) != 0u || ++n >= spin) {
-          store_agent(flags + 1, 1u);
-          stop = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    __syncthreads();
-    if (stop) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // nobody rewrites a slot before its reader is done
+    if (!bar_phase(flags, mode, 2u * r + 2u, spin)) stopped = true;
   }
   for (int o = 32; o >= 1; o >>= 1) nbad += __shfl_xor(nbad, o, 64);
   __shared__ unsigned wb[4];
   if ((t & 63) == 0) wb[t >> 6] = nbad;
   __syncthreads();
-  if (t == 0) bad[blockIdx.x] = wb[0] + wb[1] + wb[2] + wb[3] + (stop ? 0x10000u : 0u);
+  if (t == 0) bad[blockIdx.x] = wb[0] + wb[1] + wb[2] + wb[3] + (stopped ? 0x10000u : 0u);
 }
 
 // Dense fp16 matrix-core rate: every wave runs `iters` x 8 independent
-// v_mfma_f32_16x16x32_f16 (eight accumulator chains), then folds its
-// accumulators into sink so nothing is dropped.
-__global__ void __launch_bounds__(256) k_probe_mfma(int iters, float* sink) {
+// v_mfma_f32_16x16x32_f16 (shape 0: eight accumulator chains, 16384 flops
+// each) or iters x 4 v_mfma_f32_32x32x16_f16 (shape 1: four chains, 32768
+// flops each), then folds its accumulators so nothing is dropped.
+__global__ void __launch_bounds__(256) k_probe_mfma(int iters, int shape, float* sink) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
@@ -180,16 +215,36 @@ __global__ void __launch_bounds__(256) k_probe_mfma(int iters, float* sink) {
     a[i] = (_Float16)((lane + i) & 3);
     b[i] = (_Float16)((lane * 3 + i) & 3);
   }
-  f4 c[8];
-#pragma unroll
-  for (int j = 0; j < 8; j++) c[j] = f4{0, 0, 0, 0};
-  for (int it = 0; it < iters; it++) {
-#pragma unroll
-    for (int j = 0; j < 8; j++) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[j], 0, 0, 0);
-  }
   float s = 0.0f;
+  if (shape == 0) {
+    f4 c[8];
 #pragma unroll
-  for (int j = 0; j < 8; j++) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    for (int j = 0; j < 8; j++) c[j] = f4{0, 0, 0, 0};
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        c[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  } else {
+    // v_mfma_f32_32x32x16_f16: the same 16384 flops... x2 (32768), four chains
+    typedef float f16v __attribute__((ext_vector_type(16)));
+    f16v c[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) c[j][i] = 0.0f;
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) s += c[j][i];
+  }
   if (s == 1234.5f) sink[blockIdx.x] = s;  // practically never true; keeps the work live
 }
 
@@ -239,7 +294,8 @@ int rq_probe_signal(unsigned* flags, int mode, int blocks, void* stream) {
 int rq_probe_barrier(unsigned* flags, int mode, int blocks, int rounds, int spin,
                      unsigned* bad, void* stream) {
   if (!flags || !bad) return RQ_ERR_NULL;
-  if ((mode != 2 && mode != 3) || blocks < 1 || rounds < 1 || spin < 1) return RQ_ERR_SHAPE;
+  if (mode < 2 || mode > 5 || blocks < 1 || blocks > 4096 || rounds < 1 || spin < 1)
+    return RQ_ERR_SHAPE;
   void* args[] = {&flags, &mode, &rounds, &spin, &bad};
   // cooperative: the runtime refuses the launch unless every workgroup can be
   // resident at once, which the waits need
@@ -253,11 +309,11 @@ int rq_probe_barrier(unsigned* flags, int mode, int blocks, int rounds, int spin
   return RQ_OK;
 }
 
-int rq_probe_mfma(int blocks, int iters, float* sink, void* stream) {
+int rq_probe_mfma(int blocks, int iters, int shape, float* sink, void* stream) {
   if (!sink) return RQ_ERR_NULL;
-  if (blocks < 1 || iters < 1) return RQ_ERR_SHAPE;
+  if (blocks < 1 || iters < 1 || (shape != 0 && shape != 1)) return RQ_ERR_SHAPE;
   hipLaunchKernelGGL(k_probe_mfma, dim3(blocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), iters, sink);
+                     static_cast<hipStream_t>(stream), iters, shape, sink);
   return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 

@@ -67,7 +67,7 @@ def probe(sizes=(8912896, 35651584, 1 << 30), cold_bytes=1 << 30,
     return out
 
 
-def sync_probe(grids=(256, 512, 1024, 2048), barrier_grids=(256, 512), rounds=1000,
+def sync_probe(grids=(256, 512, 1024, 2048), barrier_grids=(256, 512, 1024), rounds=1000,
                spin=1 << 20):
     L = lib()
     stream = torch.cuda.current_stream().cuda_stream
@@ -87,10 +87,11 @@ def sync_probe(grids=(256, 512, 1024, 2048), barrier_grids=(256, 512), rounds=10
                                               row["coherent_writes_us"]) * 1e3 / G
         out["signal"].append(row)
     for G in barrier_grids:
-        flags = torch.zeros(64 * (G + 1), dtype=torch.int32, device="cuda")
+        flags = torch.zeros(2048 + 65 * G, dtype=torch.int32, device="cuda")
         bad = torch.zeros(G, dtype=torch.int32, device="cuda")
         row = {"blocks": G, "rounds": rounds, "barriers": 2 * rounds}
-        for mode, name in ((2, "coherent"), (3, "release_acquire")):
+        for mode, name in ((2, "coherent"), (3, "release_acquire"),
+                           (4, "coherent_32_counters"), (5, "coherent_per_workgroup_words")):
             best = None
             for _ in range(3):
                 flags.zero_()
@@ -123,12 +124,16 @@ def mfma_probe(blocks=2048, iters=2000):
     L = lib()
     stream = torch.cuda.current_stream().cuda_stream
     sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
-    fn = lambda i: L.rq_probe_mfma(blocks, iters, sink.data_ptr(), stream)  # noqa: E731
-    fn(0)
-    t = min(_time_launches(fn, 5) for _ in range(3))
-    flops = blocks * 4 * iters * 8 * 16384
-    return {"instruction": "v_mfma_f32_16x16x32_f16", "blocks": blocks, "waves": blocks * 4,
-            "flops": flops, "us": t * 1e6, "tflops": flops / t / 1e12}
+    out = {"blocks": blocks, "waves": blocks * 4, "shapes": []}
+    for shape, name in ((0, "v_mfma_f32_16x16x32_f16"), (1, "v_mfma_f32_32x32x16_f16")):
+        fn = lambda i: L.rq_probe_mfma(blocks, iters, shape, sink.data_ptr(), stream)  # noqa: E731
+        fn(0)
+        t = min(_time_launches(fn, 5) for _ in range(3))
+        flops = blocks * 4 * iters * 8 * 16384
+        out["shapes"].append({"instruction": name, "flops": flops, "us": t * 1e6,
+                              "tflops": flops / t / 1e12})
+    out["tflops"] = max(r["tflops"] for r in out["shapes"])
+    return out
 
 
 def main():

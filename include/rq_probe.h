@@ -40,23 +40,28 @@ int rq_probe_empty(void* stream);
  * of at least 64 * (blocks + 1) dwords, zeroed by the caller. */
 int rq_probe_signal(unsigned* flags, int mode, int blocks, void* stream);
 
-/* `rounds` grid-wide barriers among `blocks` co-resident workgroups (a
- * cooperative launch: RQ_ERR_LAUNCH if they cannot all be resident).  Each
- * round every workgroup writes its slot, arrives, waits for all, then reads
- * its neighbour's slot; bad[b] (blocks entries) receives the number of stale
- * values workgroup b read, plus 0x10000 if a wait gave up.  mode 2:
- * device-scope coherent writes and reads, arrival once the writes are
- * acknowledged; mode 3: plain writes, release arrival, acquire wait.  Every
- * wait gives up after `spin` polls (about 1 us each) and then stops every
- * workgroup, so the kernel always ends.  flags: at least 64 * (blocks + 1)
- * dwords, zeroed by the caller. */
+/* `rounds` grid-wide barriers among `blocks` (at most 4096) co-resident
+ * workgroups (a cooperative launch: RQ_ERR_LAUNCH if they cannot all be
+ * resident).  Each round every workgroup writes its 64-dword data slot,
+ * passes a barrier, reads its neighbour's slot, and passes a second barrier;
+ * bad[b] (blocks entries) receives the number of stale values workgroup b
+ * read, plus 0x10000 if a wait gave up.  Arrival schemes: mode 2, one counter
+ * with relaxed device-scope atomics and coherent slot writes awaited before
+ * arriving; mode 3, one counter with release arrivals and acquire polls and
+ * plain slot writes; mode 4, as 2 with 32 counters on separate cache lines;
+ * mode 5, as 2 with no atomics (one arrival word per workgroup, polled all at
+ * once).  Every wait gives up after `spin` polls (about 1 us each) and then
+ * stops every workgroup, so the kernel always ends.  flags: at least
+ * 2048 + 65 * blocks dwords, zeroed by the caller. */
 int rq_probe_barrier(unsigned* flags, int mode, int blocks, int rounds, int spin,
                      unsigned* bad, void* stream);
 
 /* Dense fp16 matrix-core rate: `blocks` workgroups of four waves, each wave
- * issuing iters x 8 v_mfma_f32_16x16x32_f16 (16384 flops each) on eight
- * independent accumulators.  sink: `blocks` floats (practically never written). */
-int rq_probe_mfma(int blocks, int iters, float* sink, void* stream);
+ * issuing 8 x 16384 flops per iteration for `iters` iterations: shape 0, eight
+ * independent chains of v_mfma_f32_16x16x32_f16; shape 1, four chains of
+ * v_mfma_f32_32x32x16_f16.  sink: `blocks` floats (practically never
+ * written). */
+int rq_probe_mfma(int blocks, int iters, int shape, float* sink, void* stream);
 
 /* Re-read the launch-shape override variables (RQ_GEMV_LPR, RQ_GEMV_CPL,
  * RQ_GEMV_NPASS, RQ_GEMM_PLAN (1-based index of a workgroup arrangement of
