@@ -31,7 +31,7 @@ __all__ = [
 RQ_OK = 0
 RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED, RQ_ERR_ALIGN = 1, 2, 3, 4
 RQ_ERR_LAUNCH, RQ_ERR_ALIAS, RQ_ERR_DEVICE, RQ_ERR_SCRATCH = 5, 6, 7, 8
-RQ_NOALLOC_SCRATCH_BYTES = 8 << 20
+RQ_NOALLOC_SCRATCH_BYTES = (8 << 20) + (64 << 10)
 RQ_LAYOUT_SYM, RQ_LAYOUT_ASYM_SB, RQ_LAYOUT_FP8_TENSOR = 0, 1, 2
 RQ_OUT_F32, RQ_OUT_CODES_I8 = 0, 1
 RQ_MAX_M = 64

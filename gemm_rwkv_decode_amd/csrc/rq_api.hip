@@ -166,14 +166,22 @@ float* stream_workspace(int dev, hipStream_t stream) {
     (void)hipGetLastError();
     return nullptr;
   }
+  // the split-K arrival counters start at zero (each launch leaves them so)
+  if (hipMemset(p, 0, rq::SPLIT_COUNTERS * sizeof(unsigned)) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    return nullptr;
+  }
   cache[std::make_pair(dev, stream)] = p;
   return p;
 }
 
 // Split-K scratch of rq_gemm_smallm_noalloc: a fixed device array (each GPU
 // the library runs on holds its own copy until the process ends), so that
-// entry point never allocates.  Its size covers every split the automatic
-// choice makes (at most 4 K-ranges x 64 rows x 8191 outputs of binary32).
+// entry point never allocates.  It holds the split-K arrival counters (zero
+// at load, and every launch leaves them zero) and partial sums for every
+// split the automatic choice makes (at most 4 K-ranges x 64 rows x 8191
+// outputs of binary32).
 constexpr size_t SCRATCH_BYTES = (size_t)RQ_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) float scratch[SCRATCH_BYTES / sizeof(float)];
 

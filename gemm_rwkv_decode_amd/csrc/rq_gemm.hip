@@ -1,28 +1,10 @@
 // rq_gemm.hip -- y = x W^T on the matrix cores for small batches (M <= 64):
-// plan choice, the split-K reduce, and the dispatch to the per-format
-// instances (rq_gemm_<format>.hip).  The kernel and its design are in
+// the dispatch to the per-format instances (rq_gemm_<format>.hip); the plan
+// choice is in rq_gemm_plan.h.  The kernel and its design are in
 // rq_gemm_impl.h.
 #include "rq_gemm_plan.h"
 
 namespace rq {
-
-// y[i] = sum over K-ranges s = 0..splits-1 (in order) of ws[s][i], i < count.
-__global__ void __launch_bounds__(256)
-k_split_reduce(const float* __restrict__ ws, float* __restrict__ y, size_t count,
-               int splits) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
-       i += (size_t)gridDim.x * blockDim.x) {
-    float v = 0.0f;
-    for (int sp = 0; sp < splits; sp++) v += ws[(size_t)sp * count + i];
-    y[i] = v;
-  }
-}
-
-void launch_split_reduce(const float* ws, float* y, size_t count, int splits, hipStream_t s) {
-  size_t rb = (count + 255) / 256;
-  if (rb > 1024) rb = 1024;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)rb), dim3(256), 0, s, ws, y, count, splits);
-}
 
 hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c, float* ws,
                             hipStream_t s) {

@@ -37,11 +37,18 @@
 // the price of a partial-sum workspace and a reduce kernel, used only where
 // that wins.
 //
-// Split-K reduction.  When the K dimension is split, every K-range writes its
-// partial tile to a workspace with plain stores and a second, small kernel
-// adds the partials in K-range order into y.  Results are deterministic; no
-// workgroup waits for another and no device-wide fence is needed (a fence per
-// workgroup costs tens of microseconds: it writes the L2 back).
+// Split-K reduction, in the same launch.  When the K dimension is split, each
+// multiplying wave that stores a 16-row tile writes its partial tile to the
+// workspace with device-scope (coherent) stores, waits until they are
+// acknowledged, and counts itself on the tile's counter with one relaxed
+// device-scope atomic.  The wave that arrives last -- it reads splits - 1 --
+// loads the other K-ranges' partials with device-scope loads, adds them in
+// K-range order (its own from registers: the value it stored) and writes y,
+// then resets the counter to 0 for the next launch.  No wave ever waits for
+// another, so no launch order or residency is assumed, and the sum is the same
+// whichever wave is last: results are deterministic.  No fence is used: a
+// __threadfence() writes the L2 back and costs about 50 ns per workgroup,
+// serialized over the device; coherent stores need no write-back.
 #pragma once
 
 #include "rq_common.h"
@@ -138,18 +145,19 @@ constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd)
 // come first (at least 2 rounds), then as many x rounds as fit (at most
 // MM_MAX_XDEPTH), then the rest of the LDS goes to more code rounds; each
 // copying wave's pending copies must fit its counter (63).
-constexpr int mm_xdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
+constexpr int mm_xdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd, int occ) {
+  const int lds = LDS_LIMIT / occ;
   const int xs = mm_xslot(fmt, mt, g, wk, rd), cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
   const int xpp = (mm_xcopies(fmt, mt, g, wk, rd) + MM_XP - 1) / MM_XP;
-  int dcmin = (MM_CODE_AHEAD + cs - 1) / cs;
+  int dcmin = (MM_CODE_AHEAD / occ + cs - 1) / cs;
   dcmin = dcmin < 2 ? 2 : (dcmin > MM_MAX_CDEPTH ? MM_MAX_CDEPTH : dcmin);
   int d = MM_MAX_XDEPTH;
-  while (d > 0 && ((d + 1) * xs + (dcmin + 1) * cs > LDS_LIMIT || (d - 1) * xpp > 63)) d--;
+  while (d > 0 && ((d + 1) * xs + (dcmin + 1) * cs > lds || (d - 1) * xpp > 63)) d--;
   return d;
 }
-constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
-  const int left = LDS_LIMIT - (mm_xdepth(fmt, mt, g, wr, wk, nt, rd) + 1) *
-                                   mm_xslot(fmt, mt, g, wk, rd);
+constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd, int occ) {
+  const int left = LDS_LIMIT / occ - (mm_xdepth(fmt, mt, g, wr, wk, nt, rd, occ) + 1) *
+                                         mm_xslot(fmt, mt, g, wk, rd);
   const int cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
   const int cpp = (mm_ccopies(fmt, mt, g, wr, wk, nt, rd) + MM_CP - 1) / MM_CP;
   int d = MM_MAX_CDEPTH;
@@ -157,10 +165,12 @@ constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd) 
   return d;
 }
 
-// Workgroup arrangements: row groups x K-slices x 16-row tiles per wave, and
-// the round size (rd = 2: half the default round).
+// Workgroup arrangements: row groups x K-slices x 16-row tiles per wave, the
+// round size (rd = 2: half the default round) and the workgroups meant to
+// share a CU (occ = 2: each takes at most half the LDS and of the registers).
 struct Plan {
   int wr, wk, nt, rd;
+  int occ = 1;
 };
 static constexpr Plan kPlans[] = {
     {1, 4, 1, 1},  // 0: 16 rows, 4 K-slices
@@ -183,19 +193,28 @@ static constexpr Plan kPlans[] = {
     {3, 2, 1, 1},  // 15: 48 rows, 2 K-slices
     {3, 2, 1, 2},  // 16: as 15, half rounds
     {3, 4, 1, 1},  // 17: 48 rows, 4 K-slices
+    // two workgroups per CU (half the LDS each), half rounds
+    {1, 8, 1, 2, 2},  // 18: 16 rows, 8 K-slices
+    {1, 4, 1, 2, 2},  // 19: 16 rows, 4 K-slices
+    {4, 2, 1, 2, 2},  // 20: 64 rows, 2 K-slices
+    {2, 4, 1, 2, 2},  // 21: 32 rows, 4 K-slices
+    {2, 2, 2, 2, 2},  // 22: 64 rows, 2 K-slices, two tiles per wave
+    {3, 2, 1, 2, 2},  // 23: 48 rows, 2 K-slices
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
 // Compile-time shape of one kernel instance.
-template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_>
+template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_, int OCC_ = 1>
 struct Mm {
   static constexpr int FMT = FMT_, MT = MT_, NT = NT_, WR = WR_, WK = WK_, G = G_, RD = RD_;
+  static constexpr int OCC = OCC_;                  // workgroups meant to share a CU
+  static constexpr int LDS_MAX = LDS_LIMIT / OCC;   // LDS bytes this workgroup may take
   static constexpr int W = WR * WK;                 // multiplying waves
   static constexpr int THREADS = 64 * (W + MM_XP + MM_CP);
   static constexpr int KC = mm_kc(FMT, MT, WK, G, RD);  // k per wave chunk
   static constexpr int ROUND = WK * KC;             // k per round
-  static constexpr int DX = mm_xdepth(FMT, MT, G, WR, WK, NT, RD);  // x rounds ahead
-  static constexpr int DC = mm_cdepth(FMT, MT, G, WR, WK, NT, RD);  // code rounds ahead
+  static constexpr int DX = mm_xdepth(FMT, MT, G, WR, WK, NT, RD, OCC);  // x rounds ahead
+  static constexpr int DC = mm_cdepth(FMT, MT, G, WR, WK, NT, RD, OCC);  // code rounds ahead
   static constexpr int MP = 16 * MT;                // padded activation rows
   static constexpr int TR = 16 * NT;                // rows per wave
   static constexpr int ROWS = TR * WR;              // rows per workgroup
@@ -249,10 +268,11 @@ struct Mm {
       (is_asym(FMT) || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
       SEG_LANES <= 64 && ROUND * 2 % SEG == 0;
   // accumulator tiles per wave the register file holds without spilling:
-  // 12 waves per workgroup leave 168 registers a lane
-  static constexpr bool REGS = NT * MT <= (THREADS > 512 ? 4 : 8);
+  // 12 waves per workgroup leave 168 registers a lane (half that with two
+  // workgroups per CU)
+  static constexpr bool REGS = NT * MT * OCC <= (THREADS > 512 ? 4 : 8);
   static constexpr bool FITS = VALID && REGS && DX >= 1 && DC >= 1 &&
-                               LDS_BYTES <= LDS_LIMIT && RED * 4 <= LDS_LIMIT;
+                               LDS_BYTES <= LDS_MAX && RED * 4 <= LDS_MAX;
   static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
                           CHN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
                 "copy counts");
@@ -581,8 +601,18 @@ struct MmEntry {
   const void* zr;
   const _Float16* x;
   float* out;  // y, or the partial-sum workspace when K is split
+  float* y;    // y (the split-K result goes here)
   int N;
 };
+
+// Split-K workspace layout: SPLIT_COUNTERS arrival counters (one per 16-row
+// tile, zero between launches), then the partial tiles [split][M][N].
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 struct MmBatch {
   int begin[MM_BATCH];
   int count;
@@ -590,8 +620,8 @@ struct MmBatch {
 };
 
 template <class S>
-__global__ void __launch_bounds__(S::THREADS)
-k_mm(const MmBatch bt, int M, int K, int kr) {
+__global__ void __launch_bounds__(S::THREADS, S::OCC)
+k_mm(const MmBatch bt, int M, int K, int kr, unsigned* counters) {
   constexpr int NT = S::NT, MT = S::MT;
   static_assert(S::FITS, "LDS budget and prefetch depth");
   constexpr int LDS_BYTES = S::LDS_BYTES > S::RED * 4 ? S::LDS_BYTES : S::RED * 4;
@@ -682,6 +712,22 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
             acc[nt][mt][i] = v;
           }
     }
+    const int splits = gridDim.y;
+    if (splits == 1) {
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        const int n = row0 + wr * S::TR + nt * 16 + col;
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int m = mt * 16 + 4 * h + i;
+            if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i] * mscale;
+          }
+      }
+      return;
+    }
+    // ---- K split: partial tile, arrival, and the last wave's sum
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
       const int n = row0 + wr * S::TR + nt * 16 + col;
@@ -690,7 +736,61 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int m = mt * 16 + 4 * h + i;
-          if (m < M && n < N) y[(size_t)m * N + n] = acc[nt][mt][i] * mscale;
+          if (m < M && n < N) store_coherent(&y[(size_t)m * N + n], acc[nt][mt][i] * mscale);
+        }
+    }
+    // the stores are acknowledged before the arrival is counted
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    unsigned* ctr = counters + (row0 + wr * S::TR) / 16;
+    unsigned before = 0;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != (unsigned)(splits - 1)) return;
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float* __restrict__ yf = e.y;
+    const size_t plane = (size_t)M * N;
+    // the K-ranges' partials added in K-range order; each range's loads are
+    // issued together before any is used
+    float sum[NT][MT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) sum[nt][mt][i] = 0.0f;
+    for (int sp = 0; sp < splits; sp++) {
+      float part[NT][MT][4];
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        const int n = min(row0 + wr * S::TR + nt * 16 + col, N - 1);
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int m = min(mt * 16 + 4 * h + i, M - 1);
+            part[nt][mt][i] = sp == split ? acc[nt][mt][i] * mscale
+                                          : load_coherent(out + sp * plane + (size_t)m * N + n);
+          }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) sum[nt][mt][i] += part[nt][mt][i];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int n = row0 + wr * S::TR + nt * 16 + col;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = mt * 16 + 4 * h + i;
+          if (m < M && n < N) yf[(size_t)m * N + n] = sum[nt][mt][i];
         }
     }
     return;
@@ -702,11 +802,8 @@ k_mm(const MmBatch bt, int M, int K, int kr) {
   }
 }
 
-// Adds the split-K partial sums into y (rq_gemm.hip).
-void launch_split_reduce(const float* ws, float* y, size_t count, int splits, hipStream_t s);
-
 // One launch over p[0..count), count <= MM_BATCH; K is split (c.splits > 1,
-// partial sums in ws) only for a single problem.
+// counters and partial sums in ws) only for a single problem.
 template <class S>
 hipError_t launch_s(const Problem* const* p, int count, const GemmCfg& c, float* ws,
                     hipStream_t s) {
@@ -719,27 +816,24 @@ hipError_t launch_s(const Problem* const* p, int count, const GemmCfg& c, float*
   int blocks = 0;
   for (int i = 0; i < count; i++) {
     bt.e[i] = MmEntry{static_cast<const uint8_t*>(p[i]->qweight), p[i]->scales, p[i]->zeros,
-                      static_cast<const _Float16*>(p[i]->x), c.splits > 1 ? ws : p[i]->y,
-                      p[i]->N};
+                      static_cast<const _Float16*>(p[i]->x),
+                      c.splits > 1 ? ws + SPLIT_COUNTERS : p[i]->y, p[i]->y, p[i]->N};
     bt.begin[i] = blocks;
     blocks += (p[i]->N + S::ROWS - 1) / S::ROWS;
   }
   bt.count = count;
   const int M = p[0]->M, K = p[0]->K;
+  unsigned* counters = c.splits > 1 ? reinterpret_cast<unsigned*>(ws) : nullptr;
   hipLaunchKernelGGL((k_mm<S>), dim3(blocks, c.splits), dim3(S::THREADS), 0, s, bt, M, K,
-                     K / c.splits);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && c.splits > 1) {
-    launch_split_reduce(ws, p[0]->y, (size_t)M * p[0]->N, c.splits, s);
-    e = hipGetLastError();
-  }
-  return e;
+                     K / c.splits, counters);
+  return hipGetLastError();
   }
 }
 
 // The instance of plan P (an index into kPlans).
 template <int FMT, int MT, int G, int P>
-using MmPlan = Mm<FMT, MT, kPlans[P].nt, kPlans[P].wr, kPlans[P].wk, G, kPlans[P].rd>;
+using MmPlan =
+    Mm<FMT, MT, kPlans[P].nt, kPlans[P].wr, kPlans[P].wk, G, kPlans[P].rd, kPlans[P].occ>;
 
 template <int FMT, int MT, int G, int P = 0>
 hipError_t launch_plan(const Problem* const* p, int n, const GemmCfg& c, float* ws,

@@ -73,7 +73,7 @@ static bool plan_ok(int fmt, int mt, int group, int K, int plan) {
 }
 
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
-  return c.splits > 1 ? (size_t)c.splits * M * N : 0;
+  return c.splits > 1 ? SPLIT_COUNTERS + (size_t)c.splits * M * N : 0;
 }
 
 bool gemm_supports(int fmt, int M, int K, int group) {
@@ -95,19 +95,39 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   // workgroups cut the x staging per row (every workgroup stages all of x,
   // M*K*2 bytes, from L2).  Measured on MI355X for the RWKV-7 shapes, int4
   // g64, weights cold in HBM.
-  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17};
-  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17};
-  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
+  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
   // Few rows and long rows (K >= 16384) or a full M-tile stack (M > 48): the
   // x staging of 16-row workgroups dominates, so 64-row workgroups with K
-  // split four ways (a second, small kernel adds the partial sums) -- at
-  // 4096x16384: 16.2 -> 15.0 us (M=16), 23.0 -> 18.8 us (M=32),
-  // 45.8 -> 25.0 us (M=64).
-  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
-  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17};
+  // split four ways (the last wave to finish a tile adds the partial sums) --
+  // at 4096x16384: 16.2 -> 13.6 us (M=16), 23.0 -> 15.9 us (M=32),
+  // 45.8 -> 23.7 us (M=64).
+  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  // 12288..16383 rows (the grouped receptance/key/value launch): 64-row
+  // workgroups, about 192 of them, halve the x staging of 32-row ones --
+  // three 4096x4096 products in one launch: 11.65 -> 9.18 us (M=16, 32 rows
+  // with two workgroups per CU), 15.66 -> 11.18 us (M=32, 64 rows as two
+  // 16-row tiles per wave), 25.64 -> 17.37 us (M=64)
+  static const int wide_m16[] = {21, 7, 5, 3, 8, 4, 1, 0, 6, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 22, 23};
+  static const int wide_m32[] = {11, 5, 20, 10, 3, 8, 4, 1, 0, 6, 7, 2, 9, 12, 13, 14, 15, 16, 17, 18, 19, 21, 22, 23};
+  static const int wide_m64[] = {5, 10, 2, 3, 8, 4, 1, 0, 6, 7, 9, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  // 16384 rows and more at M = 17..32: two 16-row tiles per wave
+  // (16384x4096: 13.28 -> 12.69 us)
+  static const int large_n_m32[] = {11, 5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
   const bool split_k = allow_split && N < 8192 && (K >= 16384 || c.mt >= 4);
-  const int* order = split_k ? (c.mt == 1 ? split_n_m16 : split_n)
-                             : (N >= 16384 ? large_n : (N >= 8192 ? mid_n : small_n));
+  const int* order;
+  if (split_k)
+    order = c.mt == 1 ? split_n_m16 : split_n;
+  else if (N >= 16384)
+    order = c.mt == 2 ? large_n_m32 : large_n;
+  else if (N >= 12288)
+    order = c.mt == 1 ? wide_m16 : (c.mt == 2 ? wide_m32 : wide_m64);
+  else if (N >= 8192)
+    order = mid_n;
+  else
+    order = small_n;
   c.plan = -1;
   if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
       plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
@@ -138,7 +158,10 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   if (want > nr) want = nr;
   if (want < 1) want = 1;
   int sp = want;
-  while (sp > 1 && (nr % sp != 0 || (size_t)sp * M * N * 4 > GEMM_WS_MAX_BYTES)) sp--;
+  const size_t part_max = GEMM_WS_MAX_BYTES - SPLIT_COUNTERS * sizeof(unsigned);
+  while (sp > 1 && (nr % sp != 0 || (size_t)sp * M * N * 4 > part_max)) sp--;
+  // one arrival counter per 16-row tile
+  if ((N + 15) / 16 > SPLIT_COUNTERS) sp = 1;
   c.splits = sp;
   return c;
 }

@@ -66,8 +66,9 @@ bool gemm_supports(int fmt, int M, int K, int group);
 // whole (no workspace) and picks the plan for that.
 GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48 = 0,
                     bool allow_split = true);
-// ws: float workspace of at least splits*M*N entries (unused when
-// splits == 1).
+// ws: workspace of gemm_workspace_floats() floats (unused when splits == 1):
+// SPLIT_COUNTERS arrival counters, zero between launches, then the partial
+// sums.
 hipError_t launch_gemm(const Problem& p, const GemmCfg& c, float* ws, hipStream_t s);
 // count problems sharing fmt, M, K and group, MM_BATCH per launch (splits must
 // be 1 when count > 1)
@@ -75,7 +76,11 @@ constexpr int MM_BATCH = 8;
 hipError_t launch_gemm_many(const Problem* const* p, int count, const GemmCfg& c, float* ws,
                             hipStream_t s);
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N);
-// Largest split-K workspace choose_gemm asks for (splits * M * N floats).
+// Split-K arrival counters at the front of a workspace: one per 16-row tile,
+// so K is split only for N <= 16 * SPLIT_COUNTERS.
+constexpr int SPLIT_COUNTERS = 16384;
+// Largest split-K workspace choose_gemm asks for: the counters and at most
+// GEMM_WS_MAX_BYTES - 64 KiB of partial sums (splits * M * N floats).
 constexpr size_t GEMM_WS_MAX_BYTES = (size_t)64 << 20;
 
 hipError_t launch_dequant(const void* qweight, const void* scales, const void* zeros,

@@ -185,9 +185,10 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
  * still beats the vector units from M = 5 on.
  * Workspace.  For some shapes the K dimension is split across workgroups and
  * the partial sums pass through a workspace of 64 MiB that the library
- * allocates at the first such call on a (device, stream) pair and keeps until
- * the process ends; it is never regrown, freed or shared with another stream,
- * so no later call allocates, frees or synchronizes.  If that first call is
+ * allocates (and zeroes its arrival counters) at the first such call on a
+ * (device, stream) pair and keeps until the process ends; it is never
+ * regrown, freed or shared with another stream, so no later call allocates,
+ * frees or synchronizes.  If that first call is
  * made while the stream is being captured into a graph (or the allocation
  * fails), the call keeps K whole instead.  Work that uses one stream's
  * workspace must not run concurrently with other work that uses it (graphs
@@ -199,19 +200,20 @@ rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* ze
                          int group, int layout, void* stream);
 
 /* Bytes of the fixed device array behind rq_gemm_smallm_noalloc. */
-#define RQ_NOALLOC_SCRATCH_BYTES (8 << 20)
+#define RQ_NOALLOC_SCRATCH_BYTES ((8 << 20) + (64 << 10))
 
 /*
  * rq_gemm_smallm_noalloc -- rq_gemm_smallm for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses
  * that forbid allocation): same arguments, same kernels, same arrangement and
- * K split, same results bit for bit, but the split-K partial sums go to a
- * fixed device array of RQ_NOALLOC_SCRATCH_BYTES that the library holds on
- * each GPU it runs on until the process ends.  The call never allocates, frees
- * or synchronizes.  The array covers every split the automatic choice makes;
- * a call whose partial sums would exceed it (only with a forced split count)
- * returns RQ_ERR_SCRATCH and enqueues nothing.  Every partial sum is written
- * before it is read, so nothing needs clearing between calls, but all calls
+ * K split, same results bit for bit, but the split-K arrival counters and
+ * partial sums go to a fixed device array of RQ_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends.  The call
+ * never allocates, frees or synchronizes.  The array covers every split the
+ * automatic choice makes; a call whose partial sums would exceed it (only
+ * with a forced split count) returns RQ_ERR_SCRATCH and enqueues nothing.
+ * Every partial sum is written before it is read and every launch leaves the
+ * counters at zero, so nothing needs clearing between calls, but all calls
  * on one GPU share the array: calls that may overlap in time on one GPU (on
  * different streams, or graphs replayed concurrently) race on it.
  */

@@ -31,21 +31,22 @@ static bool restated_fits(int fmt, int mt, int g, const Plan& q) {
   const int rows = 16 * q.nt * q.wr;
   const int waves = q.wr * q.wk;
   const int threads = 64 * (waves + MM_XP + MM_CP);
-  const int dx = mm_xdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
-  const int dc = mm_cdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
+  const int dx = mm_xdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd, q.occ);
+  const int dc = mm_cdepth(fmt, mt, g, q.wr, q.wk, q.nt, q.rd, q.occ);
+  const int lds = LDS_LIMIT / q.occ;  // two workgroups per CU share its LDS
   const int row_bytes = mm_byte(fmt) ? round : round / 2;  // code bytes per row and round
   const int pieces = row_bytes / 16;
   // binary32 partial tiles of every multiplying wave: 64 lanes x 4 floats per tile
   const long red_bytes = q.wk > 1 ? (long)waves * 64 * q.nt * mt * 4 * 4 : 0;
   if (kc % g != 0 || kc / g < 1 || kc / g > 8) return false;
-  if (q.nt * mt > (threads > 512 ? 4 : 8)) return false;
+  if (q.nt * mt * q.occ > (threads > 512 ? 4 : 8)) return false;
   if (is_asym(fmt) && (SUPERBLOCK % kc != 0 || round % SUPERBLOCK != 0)) return false;
   if (!is_asym(fmt) && (round / g) % 2 != 0) return false;
   if (pieces < 8 || (pieces & (pieces - 1)) != 0) return false;
   if ((rows * pieces) % 64 != 0) return false;
   const long ring = (long)(dx + 1) * (16 * mt) * (round + 8) * 2 +
                     (long)(dc + 1) * mm_cslot(fmt, mt, g, q.wr, q.wk, q.nt, q.rd);
-  return dx >= 1 && dc >= 1 && ring <= LDS_LIMIT && red_bytes <= LDS_LIMIT;
+  return dx >= 1 && dc >= 1 && ring <= lds && red_bytes <= lds;
 }
 
 template <int FMT, int MT, int G, int P = 0>
@@ -91,6 +92,6 @@ int main() {
   // group sizes a format does not have are never accepted
   if (plan_fits(FMT_S4, 1, 16, 0) || plan_fits(FMT_A4, 1, 64, 0) || plan_fits(FMT_F8, 1, 32, 0))
     bad++;
-  printf("fitting=%d mismatches=%d\n", fitting, bad);
+  printf("plans=%d fitting=%d mismatches=%d\n", kNumPlans, fitting, bad);
   return bad ? 1 : 0;
 }

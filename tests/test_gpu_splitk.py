@@ -1,6 +1,6 @@
-"""K split over workgroups on the matrix-core kernel (rq_gemm.hip): partial
-tiles in the per-stream workspace, added in K-range order by the reduce
-kernel.  Against the oracle: forced and automatic splits, calls back to back
+"""K split over workgroups on the matrix-core kernel: partial tiles in the
+per-stream workspace, added in K-range order by the wave that finishes each
+16-row tile last (same launch; arrival counters reset by that wave).  Against the oracle: forced and automatic splits, calls back to back
 that reuse the workspace (with changing splits, M and shapes, and a grouped
 launch in between), bit-identical repeats, and the width-4096 FFN-value
 shape at full size.  Products within |y - y_ref| <= 1e-3 * sum_k |w x|;

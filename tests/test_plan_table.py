@@ -58,3 +58,12 @@ def test_48_row_four_slice_plan_fits_past_48_rows(table):
     for int4 group 64: its K-slice reduction takes 48 KiB, well inside the LDS
     (a byte count taken four times too large once excluded it)."""
     assert "fits int4 mt=4 g=64 plan=17 " in table.stdout
+
+
+def test_gpu_tests_cover_every_plan(table):
+    """The GPU plan tests force every plan the table holds."""
+    import re
+    n = int(re.search(r"plans=(\d+)", table.stdout).group(1))
+    src = open(os.path.join(ROOT, "tests", "test_gpu_parity.py")).read()
+    hi = int(re.search(r"GEMM_PLANS = \[str\(i\) for i in range\(1, (\d+)\)\]", src).group(1))
+    assert hi - 1 == n
