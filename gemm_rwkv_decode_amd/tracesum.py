@@ -7,6 +7,8 @@ python -m gemm_rwkv_decode_amd.tracesum trace DIR   per-kernel durations from th
 python -m gemm_rwkv_decode_amd.tracesum pmc DIR COUNTER...   per-dispatch medians
     of the listed counters from the counter-collection CSV under DIR, grouped
     the same way.
+python -m gemm_rwkv_decode_amd.tracesum mfma DIR   matrix-core busy fraction and
+    issued fp16 work per matrix-core kernel instance (counter CSV under DIR).
 python -m gemm_rwkv_decode_amd.tracesum record TRACE_DIR FETCH_DIR WRITE_DIR KERNEL
     GRID SHAPE ALG_BYTES   the roofline record of one kernel instance (name
     containing KERNEL, grid GRID): its average and median duration in the trace,
@@ -125,11 +127,38 @@ def record(trace_dir, fetch_dir, write_dir, kernel, grid, shape, alg_bytes):
         "source_sha256": h.hexdigest()}, indent=1))
 
 
+def mfma(d):
+    """Matrix-core busy fraction per matrix-core kernel instance and grid:
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), and the
+    issued fp16 work (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 flops)."""
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "GRBM_GUI_ACTIVE")
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    for f in _find(d, "counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                c = r.get("Counter_Name")
+                if c not in need or "k_mm" not in r["Kernel_Name"]:
+                    continue
+                per[(r["Kernel_Name"], r.get("Grid_Size"))][r.get("Dispatch_Id")][c] += \
+                    float(r["Counter_Value"])
+    print(f"{'kernel':<70} {'grid':>10} {'n':>6} {'mfma_util':>10} {'issued_GFLOP':>13}")
+    for (k, g), disp in sorted(per.items()):
+        util = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8 * 1024)
+                for v in disp.values() if v["GRBM_GUI_ACTIVE"] > 0]
+        gf = [v["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / 1e9 for v in disp.values()]
+        k = k.replace("void rq::", "rq::")
+        k = k if len(k) <= 70 else k[:67] + "..."
+        print(f"{k:<70} {g:>10} {len(disp):>6} {100 * statistics.median(util):>9.1f}% "
+              f"{statistics.median(gf):>13.2f}")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "trace":
         trace(sys.argv[2])
     elif len(sys.argv) >= 4 and sys.argv[1] == "pmc":
         pmc(sys.argv[2], sys.argv[3:])
+    elif len(sys.argv) == 3 and sys.argv[1] == "mfma":
+        mfma(sys.argv[2])
     elif len(sys.argv) == 9 and sys.argv[1] == "record":
         record(*sys.argv[2:9])
     else:
