@@ -100,6 +100,7 @@ constexpr int MM_CP = 1;           // waves copying codes and scale material
 constexpr int MM_MAX_XDEPTH = 6;   // x rounds copied ahead (x comes from L2)
 constexpr int MM_MAX_CDEPTH = 13;  // code rounds copied ahead (codes come from HBM)
 constexpr int MM_CODE_AHEAD = 32 * 1024;  // code bytes to keep in flight, at least
+constexpr int MM_MAX_SPLITS = 8;          // K-ranges a product may be split into
 
 // Bytes of one x round slot ([MP][ROUND+8] halves) and of one code round
 // slot (the workgroup's code rows [ROWS][ROUND*bits/8], then its scale
@@ -200,6 +201,11 @@ static constexpr Plan kPlans[] = {
     {2, 4, 1, 2, 2},  // 21: 32 rows, 4 K-slices
     {2, 2, 2, 2, 2},  // 22: 64 rows, 2 K-slices, two tiles per wave
     {3, 2, 1, 2, 2},  // 23: 48 rows, 2 K-slices
+    // 128 rows per workgroup (a quarter of the x staging per row of 32-row
+    // ones), half rounds; meant for K split over workgroups
+    {8, 1, 1, 2},  // 24: 8 row groups, whole chunks per wave
+    {4, 2, 2, 2},  // 25: 4 row groups of two tiles, 2 K-slices
+    {4, 1, 2, 2},  // 26: 4 row groups of two tiles, whole chunks per wave
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
@@ -752,46 +758,35 @@ k_mm(const MmBatch bt, int M, int K, int kr, unsigned* counters) {
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float* __restrict__ yf = e.y;
     const size_t plane = (size_t)M * N;
-    // the K-ranges' partials added in K-range order; each range's loads are
-    // issued together before any is used
-    float sum[NT][MT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) sum[nt][mt][i] = 0.0f;
-    for (int sp = 0; sp < splits; sp++) {
-      float part[NT][MT][4];
-#pragma unroll
-      for (int nt = 0; nt < NT; nt++) {
-        const int n = min(row0 + wr * S::TR + nt * 16 + col, N - 1);
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int m = min(mt * 16 + 4 * h + i, M - 1);
-            part[nt][mt][i] = sp == split ? acc[nt][mt][i] * mscale
-                                          : load_coherent(out + sp * plane + (size_t)m * N + n);
-          }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) sum[nt][mt][i] += part[nt][mt][i];
-    }
+    // the K-ranges' partials added in K-range order, one 16x16 tile at a time;
+    // a tile's loads of every other K-range are issued together (at most
+    // MM_MAX_SPLITS ranges) before any is used
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
       const int n = row0 + wr * S::TR + nt * 16 + col;
+      const int nc = min(n, N - 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++)
+      for (int mt = 0; mt < MT; mt++) {
+        float part[MM_MAX_SPLITS][4];
+#pragma unroll
+        for (int sp = 0; sp < MM_MAX_SPLITS; sp++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int mc = min(mt * 16 + 4 * h + i, M - 1);
+            part[sp][i] = (sp < splits && sp != split)
+                              ? load_coherent(out + sp * plane + (size_t)mc * N + nc)
+                              : acc[nt][mt][i] * mscale;
+          }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int m = mt * 16 + 4 * h + i;
-          if (m < M && n < N) yf[(size_t)m * N + n] = sum[nt][mt][i];
+          float v = 0.0f;
+#pragma unroll
+          for (int sp = 0; sp < MM_MAX_SPLITS; sp++)
+            if (sp < splits) v += part[sp][i];
+          if (m < M && n < N) yf[(size_t)m * N + n] = v;
         }
+      }
     }
     return;
   }

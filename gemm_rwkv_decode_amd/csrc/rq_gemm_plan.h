@@ -95,27 +95,27 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   // workgroups cut the x staging per row (every workgroup stages all of x,
   // M*K*2 bytes, from L2).  Measured on MI355X for the RWKV-7 shapes, int4
   // g64, weights cold in HBM.
-  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
-  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
-  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int small_n[] = {1, 0, 6, 3, 8, 4, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
+  static const int mid_n[] = {3, 8, 4, 1, 0, 6, 5, 7, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
+  static const int large_n[] = {5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
   // Few rows and long rows (K >= 16384) or a full M-tile stack (M > 48): the
   // x staging of 16-row workgroups dominates, so 64-row workgroups with K
   // split four ways (the last wave to finish a tile adds the partial sums) --
   // at 4096x16384: 16.2 -> 13.6 us (M=16), 23.0 -> 15.9 us (M=32),
   // 45.8 -> 23.7 us (M=64).
-  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
-  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int split_n_m16[] = {7, 5, 9, 2, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
+  static const int split_n[] = {5, 2, 7, 9, 8, 3, 4, 0, 6, 1, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
   // 12288..16383 rows (the grouped receptance/key/value launch): 64-row
   // workgroups, about 192 of them, halve the x staging of 32-row ones --
   // three 4096x4096 products in one launch: 11.65 -> 9.18 us (M=16, 32 rows
   // with two workgroups per CU), 15.66 -> 11.18 us (M=32, 64 rows as two
   // 16-row tiles per wave), 25.64 -> 17.37 us (M=64)
-  static const int wide_m16[] = {21, 7, 5, 3, 8, 4, 1, 0, 6, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 22, 23};
-  static const int wide_m32[] = {11, 5, 20, 10, 3, 8, 4, 1, 0, 6, 7, 2, 9, 12, 13, 14, 15, 16, 17, 18, 19, 21, 22, 23};
-  static const int wide_m64[] = {5, 10, 2, 3, 8, 4, 1, 0, 6, 7, 9, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int wide_m16[] = {21, 7, 5, 3, 8, 4, 1, 0, 6, 2, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 22, 23, 24, 25, 26};
+  static const int wide_m32[] = {11, 5, 20, 10, 3, 8, 4, 1, 0, 6, 7, 2, 9, 12, 13, 14, 15, 16, 17, 18, 19, 21, 22, 23, 24, 25, 26};
+  static const int wide_m64[] = {5, 10, 2, 3, 8, 4, 1, 0, 6, 7, 9, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
   // 16384 rows and more at M = 17..32: two 16-row tiles per wave
   // (16384x4096: 13.28 -> 12.69 us)
-  static const int large_n_m32[] = {11, 5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23};
+  static const int large_n_m32[] = {11, 5, 7, 2, 9, 8, 3, 4, 0, 6, 1, 10, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26};
   const bool split_k = allow_split && N < 8192 && (K >= 16384 || c.mt >= 4);
   const int* order;
   if (split_k)
@@ -153,6 +153,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   if (split_k && rows == 64 && blocks < 256) want = (256 + blocks - 1) / blocks;
   if (want > 4) want = 4;
   if (tu.gemm_splits) want = tu.gemm_splits;
+  if (want > MM_MAX_SPLITS) want = MM_MAX_SPLITS;
   if (!allow_split) want = 1;
   const int nr = K / round_k(fmt, c.mt, group, c.plan);
   if (want > nr) want = nr;

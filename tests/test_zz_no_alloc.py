@@ -113,8 +113,8 @@ def test_k_kept_whole():
 
 
 def test_too_large_for_the_scratch_is_rejected(tune):
-    f, N, K, M = S.INT4_G64, 4096, 16384, 64
-    tune(RQ_GEMM_SPLITS=16)
+    f, N, K, M = S.INT4_G64, 8192, 16384, 64
+    tune(RQ_GEMM_SPLITS=8)
     cfg = rq.gemm_config(M, N, K, f.bits, f.group, f.layout)
     assert cfg[1] * M * N * 4 > rq.RQ_NOALLOC_SCRATCH_BYTES
     p = mat(f, N, K, 10)
