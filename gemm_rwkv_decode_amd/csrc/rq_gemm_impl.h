@@ -272,7 +272,7 @@ struct Mm {
       GPC >= 1 && GPC <= 8 && KC % G == 0 &&
       (!is_asym(FMT) || (SUPERBLOCK % KC == 0 && ROUND % SUPERBLOCK == 0)) &&
       (is_asym(FMT) || (ROUND / G) % 2 == 0) && PR >= 8 && (PR & (PR - 1)) == 0 &&
-      SEG_LANES <= 64 && ROUND * 2 % SEG == 0;
+      SEG_LANES <= 64 && ROUND * 2 % SEG == 0 && THREADS <= 1024;
   // accumulator tiles per wave the register file holds without spilling:
   // 12 waves per workgroup leave 168 registers a lane (half that with two
   // workgroups per CU)

@@ -39,6 +39,7 @@ static bool restated_fits(int fmt, int mt, int g, const Plan& q) {
   // binary32 partial tiles of every multiplying wave: 64 lanes x 4 floats per tile
   const long red_bytes = q.wk > 1 ? (long)waves * 64 * q.nt * mt * 4 * 4 : 0;
   if (kc % g != 0 || kc / g < 1 || kc / g > 8) return false;
+  if (threads > 1024) return false;  // a workgroup holds at most 16 waves
   if (q.nt * mt * q.occ > (threads > 512 ? 4 : 8)) return false;
   if (is_asym(fmt) && (SUPERBLOCK % kc != 0 || round % SUPERBLOCK != 0)) return false;
   if (!is_asym(fmt) && (round / g) % 2 != 0) return false;
