@@ -36,14 +36,20 @@ METRIC = "int4-g64 GEMV HBM GB/s (% of peak) at D=4096 M=1; TFLOP/s at M=32"
 # per-shape leg alone, and HBM bytes per launch from the memory counters);
 # valid only while the kernel's sources hash to the recorded value.
 RECORD_FILE = os.path.join(ROOT, "profiles", "rq_gemv_int4g64_4096x16384_m1_roofline.json")
+# matrix-core busy fractions of the M = 64 step from rocprofv3 counters; valid
+# only while the matrix-core kernel's sources hash to the recorded value
+MFMA_RECORD_FILE = os.path.join(ROOT, "profiles", "rq_gemm_int4g64_m64_mfma_record.json")
+MM_SOURCES = ["gemm_rwkv_decode_amd/csrc/rq_gemm_impl.h",
+              "gemm_rwkv_decode_amd/csrc/rq_gemm_plan.h",
+              "gemm_rwkv_decode_amd/csrc/rq_common.h"]
 KERNEL_SOURCES = ["gemm_rwkv_decode_amd/csrc/rq_gemv.hip",
                   "gemm_rwkv_decode_amd/csrc/rq_common.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=None):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -60,6 +66,21 @@ def recorded(shape):
     if t.get("source_sha256") != kernel_source_hash() or t.get("shape") != shape:
         return {}
     return t
+
+
+def recorded_mfma_busy():
+    """{kernel instance: matrix-core busy fraction} of the M = 64 step, or None
+    if absent or the kernel has changed since the counters were taken."""
+    try:
+        with open(MFMA_RECORD_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash(MM_SOURCES):
+        return None
+    return {k: v["mfma_busy"] for k, v in t.get("kernels", {}).items()}
+
+
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 
@@ -653,8 +674,11 @@ def main():
                                            "probe": "rq_probe_mfma, 2048 workgroups"},
         "mfma_utilization_m64": {
             "value": round(mfma["64"]["tflops"] / mfma_peak, 4),
-            "what": "achieved TFLOP/s of the M=64 step / measured dense fp16 peak; the "
-                    "matrix-core busy cycles from counters are in profiles/"},
+            "what": "achieved TFLOP/s of the M=64 step / measured dense fp16 peak",
+            "counter_busy": recorded_mfma_busy(),
+            "counter_busy_what": "SQ_VALU_MFMA_BUSY_CYCLES per SIMD-cycle of each M=64 "
+                                 "kernel instance (rocprofv3 record "
+                                 + os.path.relpath(MFMA_RECORD_FILE, ROOT) + ")"},
         "small_workloads_m1": small,
         "fp8_w8a16_m1": fp8,
         "asym_5_6_bit_m1": hib,

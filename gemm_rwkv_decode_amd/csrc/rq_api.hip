@@ -166,8 +166,10 @@ float* stream_workspace(int dev, hipStream_t stream) {
     (void)hipGetLastError();
     return nullptr;
   }
-  // the split-K arrival counters start at zero (each launch leaves them so)
-  if (hipMemset(p, 0, rq::SPLIT_COUNTERS * sizeof(unsigned)) != hipSuccess) {
+  // the split-K arrival counters start at zero (each launch leaves them so);
+  // cleared on the caller's stream, ahead of the launch that will use them
+  // (the stream is not capturing here, so no graph records this memset)
+  if (hipMemsetAsync(p, 0, rq::SPLIT_COUNTERS * sizeof(unsigned), stream) != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(p);
     return nullptr;

@@ -758,35 +758,58 @@ k_mm(const MmBatch bt, int M, int K, int kr, unsigned* counters) {
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float* __restrict__ yf = e.y;
     const size_t plane = (size_t)M * N;
-    // the K-ranges' partials added in K-range order, one 16x16 tile at a time;
-    // a tile's loads of every other K-range are issued together (at most
-    // MM_MAX_SPLITS ranges) before any is used
+    // the K-ranges' partials added in K-range order, four K-ranges at a time:
+    // the loads of four ranges for every tile of the wave are issued together
+    // before any is used (one round trip per four ranges)
+    constexpr int SB = 4;
+    float sum[NT][MT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) sum[nt][mt][i] = 0.0f;
+#pragma unroll
+    for (int s0 = 0; s0 < MM_MAX_SPLITS; s0 += SB) {
+      if (s0 >= splits) break;
+      float part[SB][NT][MT][4];
+#pragma unroll
+      for (int q = 0; q < SB; q++)
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+          const int nc = min(row0 + wr * S::TR + nt * 16 + col, N - 1);
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int sp = s0 + q;
+              const int mc = min(mt * 16 + 4 * h + i, M - 1);
+              part[q][nt][mt][i] =
+                  (sp < splits && sp != split)
+                      ? load_coherent(out + sp * plane + (size_t)mc * N + nc)
+                      : acc[nt][mt][i] * mscale;
+            }
+        }
+#pragma unroll
+      for (int q = 0; q < SB; q++)
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+              if (s0 + q < splits) sum[nt][mt][i] += part[q][nt][mt][i];
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
       const int n = row0 + wr * S::TR + nt * 16 + col;
-      const int nc = min(n, N - 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) {
-        float part[MM_MAX_SPLITS][4];
-#pragma unroll
-        for (int sp = 0; sp < MM_MAX_SPLITS; sp++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int mc = min(mt * 16 + 4 * h + i, M - 1);
-            part[sp][i] = (sp < splits && sp != split)
-                              ? load_coherent(out + sp * plane + (size_t)mc * N + nc)
-                              : acc[nt][mt][i] * mscale;
-          }
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int m = mt * 16 + 4 * h + i;
-          float v = 0.0f;
-#pragma unroll
-          for (int sp = 0; sp < MM_MAX_SPLITS; sp++)
-            if (sp < splits) v += part[sp][i];
-          if (m < M && n < N) yf[(size_t)m * N + n] = v;
+          if (m < M && n < N) yf[(size_t)m * N + n] = sum[nt][mt][i];
         }
-      }
     }
     return;
   }

@@ -132,6 +132,37 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
       plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
     c.plan = tu.gemm_plan - 1;
+  // Measured best arrangements for the RWKV-7 matrices of the 1.5B- and
+  // 2.9B-shaped workloads (one product, weights cold; sweeps of every plan x
+  // split count at M = 4..32), where the rules below miss by more than 5%.
+  struct Tuned {
+    int fmt, group, mt, N, K, plan, splits;
+  };
+  static const Tuned tuned[] = {
+      // 4-bit asymmetric, width 2560 (FFN key 10240x2560: 14.85 -> 10.63 us at
+      // M = 8, 18.19 -> 12.45 us at M = 32)
+      {FMT_A4, 32, 1, 2560, 2560, 18, 1},  {FMT_A4, 32, 2, 2560, 2560, 0, 1},
+      {FMT_A4, 32, 1, 10240, 2560, 18, 1}, {FMT_A4, 32, 2, 10240, 2560, 17, 1},
+      {FMT_A4, 32, 1, 2560, 10240, 18, 1}, {FMT_A4, 32, 2, 2560, 10240, 17, 4},
+      // 8-bit group 16, width 2048 (FFN value 2048x8192: 14.3 -> 11.6 us at M = 32)
+      {FMT_S8, 16, 1, 2048, 2048, 19, 1},  {FMT_S8, 16, 2, 2048, 2048, 0, 1},
+      {FMT_S8, 16, 1, 8192, 2048, 19, 1},  {FMT_S8, 16, 2, 8192, 2048, 21, 1},
+      {FMT_S8, 16, 1, 2048, 8192, 19, 4},  {FMT_S8, 16, 2, 2048, 8192, 21, 4},
+      // 4-bit group 64, width 2048 (FFN value 2048x8192: 11.1 -> 10.2 us at M = 32)
+      {FMT_S4, 64, 1, 2048, 2048, 19, 1},  {FMT_S4, 64, 1, 8192, 2048, 21, 1},
+      {FMT_S4, 64, 1, 2048, 8192, 21, 4},  {FMT_S4, 64, 2, 2048, 8192, 3, 4},
+  };
+  int tuned_splits = 0;
+  if (c.plan < 0 && blocks48 == 0) {
+    for (const Tuned& t : tuned) {
+      if (t.fmt == fmt && t.group == group && t.mt == c.mt && t.N == N && t.K == K &&
+          plan_ok(fmt, c.mt, group, K, t.plan)) {
+        c.plan = t.plan;
+        tuned_splits = t.splits;
+        break;
+      }
+    }
+  }
   // 48-row workgroups where they make one wave of 224..256 row blocks (64-row
   // ones leave a quarter of the CUs idle): one 12288x4096 product,
   // 14.1 -> 11.2 us (M=16), 18.3 -> 12.1 us (M=32), 30.1 -> 20.3 us (M=64).
@@ -152,6 +183,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   int want = 1;
   if (split_k && rows == 64 && blocks < 256) want = (256 + blocks - 1) / blocks;
   if (want > 4) want = 4;
+  if (tuned_splits > 0) want = tuned_splits;
   if (tu.gemm_splits) want = tu.gemm_splits;
   if (want > MM_MAX_SPLITS) want = MM_MAX_SPLITS;
   if (!allow_split) want = 1;

@@ -9,6 +9,8 @@ python -m gemm_rwkv_decode_amd.tracesum pmc DIR COUNTER...   per-dispatch median
     the same way.
 python -m gemm_rwkv_decode_amd.tracesum mfma DIR   matrix-core busy fraction and
     issued fp16 work per matrix-core kernel instance (counter CSV under DIR).
+python -m gemm_rwkv_decode_amd.tracesum mfma-record DIR   the same for the
+    M = 64 instances as a JSON record with the hash of the kernel's sources.
 python -m gemm_rwkv_decode_amd.tracesum record TRACE_DIR FETCH_DIR WRITE_DIR KERNEL
     GRID SHAPE ALG_BYTES   the roofline record of one kernel instance (name
     containing KERNEL, grid GRID): its average and median duration in the trace,
@@ -127,10 +129,18 @@ def record(trace_dir, fetch_dir, write_dir, kernel, grid, shape, alg_bytes):
         "source_sha256": h.hexdigest()}, indent=1))
 
 
-def mfma(d):
+# the matrix-core kernel's sources, hashed into its counter record
+MM_SOURCES = ("gemm_rwkv_decode_amd/csrc/rq_gemm_impl.h",
+              "gemm_rwkv_decode_amd/csrc/rq_gemm_plan.h",
+              "gemm_rwkv_decode_amd/csrc/rq_common.h")
+
+
+def mfma(d, as_json=False):
     """Matrix-core busy fraction per matrix-core kernel instance and grid:
     SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), and the
-    issued fp16 work (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 flops)."""
+    issued fp16 work (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 flops).  as_json: a
+    record of the M = 64 (four M-tile) instances with the hash of the
+    matrix-core kernel's sources."""
     need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "GRBM_GUI_ACTIVE")
     per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
     for f in _find(d, "counter_collection.csv"):
@@ -141,6 +151,27 @@ def mfma(d):
                     continue
                 per[(r["Kernel_Name"], r.get("Grid_Size"))][r.get("Dispatch_Id")][c] += \
                     float(r["Counter_Value"])
+    if as_json:
+        import hashlib
+        import json
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        h = hashlib.sha256()
+        for f in MM_SOURCES:
+            with open(os.path.join(root, f), "rb") as fh:
+                h.update(fh.read())
+        rec = {}
+        for (k, g), disp in sorted(per.items()):
+            if "Mm<0, 4," not in k:
+                continue
+            util = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8 * 1024)
+                    for v in disp.values() if v["GRBM_GUI_ACTIVE"] > 0]
+            name = k.replace("void rq::", "rq::").split("(")[0]
+            rec[f"{name} grid {g}"] = {"dispatches": len(disp),
+                                        "mfma_busy": round(statistics.median(util), 4)}
+        print(json.dumps({"what": "matrix-core busy fraction of the int4-g64 M=64 step's "
+                                  "kernel instances (medians per dispatch)",
+                          "kernels": rec, "source_sha256": h.hexdigest()}, indent=1))
+        return
     print(f"{'kernel':<70} {'grid':>10} {'n':>6} {'mfma_util':>10} {'issued_GFLOP':>13}")
     for (k, g), disp in sorted(per.items()):
         util = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8 * 1024)
@@ -159,6 +190,8 @@ if __name__ == "__main__":
         pmc(sys.argv[2], sys.argv[3:])
     elif len(sys.argv) == 3 and sys.argv[1] == "mfma":
         mfma(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "mfma-record":
+        mfma(sys.argv[2], as_json=True)
     elif len(sys.argv) == 9 and sys.argv[1] == "record":
         record(*sys.argv[2:9])
     else:
