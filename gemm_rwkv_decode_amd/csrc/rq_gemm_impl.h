@@ -408,6 +408,25 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
   constexpr int KS = MfmaT<FMT>::KS;
   constexpr int QPL = G / 4;  // k per lane group per group
   const _Float16* xb = reinterpret_cast<const _Float16*>(xsl);
+  // asymmetric: the chunk lies inside one superblock, so each row's scale and
+  // zero records are read and split once per chunk: the binary16 bases
+  // converted, the 48-bit sub-code fields moved down to the chunk's first group
+  float dbase[NT], mbase[NT];
+  uint64_t sfield[NT], zfield[NT];
+  if constexpr (is_asym(FMT)) {
+    const int kin0 = kb % S::ROUND;  // the chunk's first k within the round
+    const int sb = kin0 / SUPERBLOCK, jb = (kin0 % SUPERBLOCK) / SB_GROUP;
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int n = wr * S::TR + nt * 16 + col;
+      const u32* sr = reinterpret_cast<const u32*>(sl + S::S_OFF) + n * S::SRD + 2 * sb;
+      const u32* zr = reinterpret_cast<const u32*>(sl + S::Z_OFF) + n * S::SRD + 2 * sb;
+      dbase[nt] = half_lo(sr[0]);
+      mbase[nt] = half_lo(zr[0]);
+      sfield[nt] = ((((uint64_t)sr[1] << 32) | sr[0]) >> 16) >> (6 * jb);
+      zfield[nt] = ((((uint64_t)zr[1] << 32) | zr[0]) >> 16) >> (6 * jb);
+    }
+  }
 #pragma unroll
   for (int g = 0; g < S::GPC; g++) {
     // this lane's codes: row n, bytes [cb0 + g*GB + h*BPL, +BPL) of the row
@@ -513,12 +532,11 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
       const int n = wr * S::TR + nt * 16 + col;
       float sc, t = 0.0f;
       if constexpr (is_asym(FMT)) {
-        const int kin = (kb % S::ROUND) + g * G;  // k within the round
-        const int sb = kin / SUPERBLOCK, j = (kin % SUPERBLOCK) / SB_GROUP;
-        const u32* sr = reinterpret_cast<const u32*>(sl + S::S_OFF) + n * S::SRD + 2 * sb;
-        const u32* zr = reinterpret_cast<const u32*>(sl + S::Z_OFF) + n * S::SRD + 2 * sb;
-        sc = record_value(u32x2{sr[0], sr[1]}, j);
-        t = record_value(u32x2{zr[0], zr[1]}, j);
+        // group g of the chunk: sub-codes at bits 6g..6g+5 of the moved fields;
+        // d * sc_j and m * mn_j are exact in binary32 (11 + 6 significant bits)
+        (void)n;
+        sc = dbase[nt] * (float)(u32)((sfield[nt] >> (6 * g)) & 0x3Fu);
+        t = mbase[nt] * (float)(u32)((zfield[nt] >> (6 * g)) & 0x3Fu);
       } else {
         const int j = j0 + g;  // group within the round
         const u32 pair = reinterpret_cast<const u32*>(sl + S::S_OFF)[n * S::SRD + j / 2];

@@ -139,11 +139,11 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
     int fmt, group, mt, N, K, plan, splits;
   };
   static const Tuned tuned[] = {
-      // 4-bit asymmetric, width 2560 (FFN key 10240x2560: 14.85 -> 10.63 us at
-      // M = 8, 18.19 -> 12.45 us at M = 32)
+      // 4-bit asymmetric, width 2560 (FFN key 10240x2560: 14.85 -> 9.31 us at
+      // M = 8, 18.19 -> 10.91 us at M = 32)
       {FMT_A4, 32, 1, 2560, 2560, 18, 1},  {FMT_A4, 32, 2, 2560, 2560, 0, 1},
-      {FMT_A4, 32, 1, 10240, 2560, 18, 1}, {FMT_A4, 32, 2, 10240, 2560, 17, 1},
-      {FMT_A4, 32, 1, 2560, 10240, 18, 1}, {FMT_A4, 32, 2, 2560, 10240, 17, 4},
+      {FMT_A4, 32, 1, 10240, 2560, 21, 1}, {FMT_A4, 32, 2, 10240, 2560, 17, 1},
+      {FMT_A4, 32, 1, 2560, 10240, 19, 1}, {FMT_A4, 32, 2, 2560, 10240, 17, 4},
       // 8-bit group 16, width 2048 (FFN value 2048x8192: 14.3 -> 11.6 us at M = 32)
       {FMT_S8, 16, 1, 2048, 2048, 19, 1},  {FMT_S8, 16, 2, 2048, 2048, 0, 1},
       {FMT_S8, 16, 1, 8192, 2048, 19, 1},  {FMT_S8, 16, 2, 8192, 2048, 21, 1},
