@@ -315,6 +315,33 @@ def main():
                           "per_shape_m1": per_kernel}), flush=True)
         return
 
+    # ---- what this GPU sustains for the same step at M = 1: each launch's
+    # bytes read by the plain streaming-read probe (cold, best launch shape),
+    # and a graph of as many dependent empty launches ------------------------
+    log("measured M=1 ceiling")
+    from gemm_rwkv_decode_amd import probe as PR
+    ceil_shapes = {}
+    read_step_us = 0.0
+    for key, v in per_kernel.items():
+        if key == "65536x4096":
+            continue
+        t = PR.read_us(v["bytes"])
+        ceil_shapes[key] = {"bytes": v["bytes"], "read_probe_us": round(t, 3),
+                            "kernel_us": v["us_per_launch"],
+                            "kernel_over_read": round(v["us_per_launch"] / t, 3)}
+        read_step_us += t * v["launches_per_step"]
+    chain = PR.chain_us(scheds["layer"]["launch_calls"])
+    ceiling = {
+        "read_probe_step_ms": round(read_step_us / 1e3, 4),
+        "read_probe_step_GBps": round(step_bytes(1) / (read_step_us * 1e-6) / 1e9, 1),
+        "headline_frac_of_read_probe_step": round(read_step_us * 1e-6 / sec1, 4),
+        "empty_launch_chain_ms": round(chain / 1e3, 4),
+        "per_shape": ceil_shapes,
+        "what": "read_probe_step: the step's launches, each replaced by one plain streaming "
+                "read of its bytes (rq_probe_read, cold buffers), back to back; "
+                "empty_launch_chain: one graph replay of the step's launch count of "
+                "dependent empty kernels (rq_probe_empty)"}
+
     # ---- the dense fp16 matrix-core rate of this GPU (rq_probe_mfma) --------
     sink = torch.zeros(2048, dtype=torch.float32, device=dev)
     pk = {}
@@ -683,6 +710,7 @@ def main():
         "fp8_w8a16_m1": fp8,
         "asym_5_6_bit_m1": hib,
         "per_shape_m1": per_kernel,
+        "measured_ceiling_m1": ceiling,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_oracle_threads": cpu_threads,

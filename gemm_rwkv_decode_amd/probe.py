@@ -67,6 +67,55 @@ def probe(sizes=(8912896, 35651584, 1 << 30), cold_bytes=1 << 30,
     return out
 
 
+def read_us(size, cold_bytes=1 << 30,
+            shapes=((512, 256), (1024, 256), (2048, 256), (1024, 512), (512, 1024))):
+    """Best time (us) of one streaming read of `size` bytes over a few launch
+    shapes, launches rotating over buffers whose total exceeds the last-level
+    cache (cold reads)."""
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    nbuf = max(2, -(-cold_bytes // size))
+    bufs = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    for b in bufs:
+        b.fill_(1)
+    best = None
+    for blocks, threads in shapes:
+        def fn(i, blocks=blocks, threads=threads):
+            L.rq_probe_read(bufs[i % nbuf].data_ptr(), size, sink.data_ptr(), blocks,
+                            threads, stream)
+        fn(0)
+        t = min(_time_launches(fn, 2 * nbuf) for _ in range(2))
+        best = t if best is None else min(best, t)
+    del bufs
+    torch.cuda.empty_cache()
+    return best * 1e6
+
+
+def chain_us(launches, replays=20):
+    """Time (us) of one graph replay of `launches` dependent empty launches:
+    the floor a step of that many launches pays before moving any byte."""
+    L = lib()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            L.rq_probe_empty(s.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(launches):
+                L.rq_probe_empty(s.cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t) / replays * 1e6
+
+
 def sync_probe(grids=(256, 512, 1024, 2048), barrier_grids=(256, 512, 1024), rounds=1000,
                spin=1 << 20):
     L = lib()
