@@ -310,13 +310,25 @@ __device__ __forceinline__ void wait_vm_rounds(int k) {
   }
 }
 
-__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
-                                   0);
+// Global->LDS copies as buffer loads: the array's base in a buffer resource
+// and the round's offset in scalar registers, the lane's offset (fixed for
+// the whole launch) in a vector register, so a copy needs no address
+// arithmetic of its own (a global load with a 64-bit address costs one VALU
+// add per copy).  The resource's range is the whole 32-bit offset space; the
+// host keeps every array below 2 GiB.  Word 3: 32-bit data format, which
+// untyped loads require on this architecture.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mm_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
 }
-__device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0,
-                                   0);
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* dst, u32 voff,
+                                           u32 soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, void* dst, u32 voff,
+                                          u32 soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4,
+                                           voff, soff, 0, 0);
 }
 
 // Copy c of a round, c in [0, COPIES): x row segments first (rows >= M
@@ -327,7 +339,7 @@ __device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
 // dwords (row n's dword d at n*SRD + d; asym: scale records, then zero
 // records).  The lanes past the last row repeat it into the region's padding.
 // copy_off gives this lane's byte offset from the copy's base,
-// which does not change from round to round; copy_src/copy_dst the uniform
+// which does not change from round to round; copy_soff/copy_dst the uniform
 // parts.
 template <class S>
 __device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, int lane) {
@@ -362,22 +374,16 @@ __device__ __forceinline__ u32 copy_off(int c, int M, int K, int N, int row0, in
   }
 }
 
-// Source base of copy c in round t (k0: the round's first k).
+// The round's byte offset of copy c from its array's base (k0: the round's
+// first k): x, the codes, the high-bit plane (which follows every row's
+// nibbles), the scales (asym: and the zero records).
 template <class S>
-__device__ __forceinline__ const char* copy_src(int c, int k0, const _Float16* x,
-                                                const uint8_t* qw, const void* scales,
-                                                const void* zeros, int N, int K) {
-  if (c < S::XN) return reinterpret_cast<const char*>(x) + (size_t)k0 * 2;
-  if (c < S::XN + S::CN)
-    return reinterpret_cast<const char*>(qw) + (size_t)(mm_byte(S::FMT) ? k0 : k0 / 2);
-  if (c < S::XN + S::CHN)  // the high-bit plane follows every row's nibbles
-    return reinterpret_cast<const char*>(qw) + (size_t)N * (K / 2) + (size_t)(k0 / 8) * S::HB;
-  if constexpr (is_asym(S::FMT)) {
-    const bool zr = (c - S::XN - S::CHN) >= S::SNK;
-    return reinterpret_cast<const char*>(zr ? zeros : scales) + (size_t)(k0 / SUPERBLOCK) * 8;
-  } else {
-    return reinterpret_cast<const char*>(scales) + (size_t)(k0 / S::G) * 2;
-  }
+__device__ __forceinline__ u32 copy_soff(int c, u32 k0) {
+  if (c < S::XN) return k0 * 2u;
+  if (c < S::XN + S::CN) return mm_byte(S::FMT) ? k0 : k0 / 2u;
+  if (c < S::XN + S::CHN) return k0 / 8u * (u32)S::HB;
+  if constexpr (is_asym(S::FMT)) return k0 / (u32)SUPERBLOCK * 8u;
+  else return k0 / (u32)S::G * 2u;
 }
 
 // Destination offset of copy c within its slot.
@@ -580,18 +586,21 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
   u32 off[NC];
 #pragma unroll
   for (int i = 0; i < NC; i++) off[i] = copy_off<S>(cidx(i), M, K, N, row0, lane);
+  const __amdgpu_buffer_rsrc_t rx = mm_rsrc(x), rc = mm_rsrc(qw), rs = mm_rsrc(scales),
+                               rz = mm_rsrc(zeros),
+                               rh = mm_rsrc(qw + (S::HB > 0 ? (size_t)N * (K / 2) : 0));
   auto issue = [&](int t) {
     char* slot = XW ? lds + (t % (S::DX + 1)) * S::XSLOT
                     : lds + S::CRING + (t % (S::DC + 1)) * S::CSLOT;
-    const int k0 = k_begin + t * S::ROUND;
+    const u32 k0 = (u32)(k_begin + t * S::ROUND);
 #pragma unroll
     for (int i = 0; i < NC; i++) {
       const int c = cidx(i);
-      const char* src = copy_src<S>(c, k0, x, qw, scales, zeros, N, K) + off[i];
       char* dst = slot + copy_dst<S>(c);
       if constexpr (XW) {
         // every x copy of a round has the same lane count
-        if (S::SEG_LANES == 64 || lane < S::SEG_LANES) lds_copy16(src, dst);
+        if (S::SEG_LANES == 64 || lane < S::SEG_LANES)
+          lds_copy16(rx, dst, off[i], copy_soff<S>(c, k0));
       } else {
         // Code, high-bit and scale copies are whole-wave instructions with no
         // lane predicate: the code rows are whole copies, the other regions
@@ -599,8 +608,15 @@ __device__ __forceinline__ void copy_rounds(int p, char* lds, const _Float16* x,
         // counts in one unrolled sequence were once merged by the compiler
         // into a block that issued some of them under another copy's mask.)
         const int cc = S::XN + (i < S::CHN + S::SN ? i : S::CHN + S::SN - 1);
-        if (cc >= S::XN + S::CHN) lds_copy4(src, dst);
-        else lds_copy16(src, dst);
+        const u32 so = copy_soff<S>(cc, k0);
+        if (cc < S::XN + S::CN) {
+          lds_copy16(rc, dst, off[i], so);
+        } else if (cc < S::XN + S::CHN) {
+          lds_copy16(rh, dst, off[i], so);
+        } else {
+          const bool zr = is_asym(S::FMT) && (cc - S::XN - S::CHN) >= S::SNK;
+          lds_copy4(zr ? rz : rs, dst, off[i], so);
+        }
       }
     }
   };
