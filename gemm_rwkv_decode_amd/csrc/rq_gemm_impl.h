@@ -102,14 +102,19 @@ constexpr int MM_MAX_CDEPTH = 13;  // code rounds copied ahead (codes come from 
 constexpr int MM_CODE_AHEAD = 32 * 1024;  // code bytes to keep in flight, at least
 constexpr int MM_MAX_SPLITS = 8;          // K-ranges a product may be split into
 
+// Rows of x staged per round: 16 per M-tile, or 4 / 8 when M <= 4 / 8 (one
+// M-tile whose MFMA rows past them re-read the staged rows: their outputs are
+// never stored); xr = 0 means 16 * mt.
+constexpr int mm_xr(int mt, int xr) { return xr > 0 ? xr : 16 * mt; }
+
 // Bytes of one x round slot ([MP][ROUND+8] halves) and of one code round
 // slot (the workgroup's code rows [ROWS][ROUND*bits/8], then its scale
 // material).
 constexpr int mm_round(int fmt, int mt, int wk, int g, int rd) {
   return wk * mm_kc(fmt, mt, wk, g, rd);
 }
-constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd) {
-  return (16 * mt) * (mm_round(fmt, mt, wk, g, rd) + 8) * 2;
+constexpr int mm_xslot(int fmt, int mt, int g, int wk, int rd, int xr = 0) {
+  return mm_xr(mt, xr) * (mm_round(fmt, mt, wk, g, rd) + 8) * 2;
 }
 // Scale material is copied in whole 64-lane copies of 4-byte elements; each
 // kind's region is padded to whole copies (the lanes past the last row copy
@@ -129,10 +134,10 @@ constexpr int mm_cslot(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
   return codes + (is_asym(fmt) ? 2 : 1) * region;
 }
 // copy instructions per round: x row segments; code pieces and scale dwords
-constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd) {
+constexpr int mm_xcopies(int fmt, int mt, int g, int wk, int rd, int xr = 0) {
   const int round = mm_round(fmt, mt, wk, g, rd);
   const int seg = round * 2 < 1024 ? round * 2 : 1024;
-  return (16 * mt) * (round * 2 / seg);
+  return mm_xr(mt, xr) * (round * 2 / seg);
 }
 constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd) {
   const int round = mm_round(fmt, mt, wk, g, rd);
@@ -146,19 +151,21 @@ constexpr int mm_ccopies(int fmt, int mt, int g, int wr, int wk, int nt, int rd)
 // come first (at least 2 rounds), then as many x rounds as fit (at most
 // MM_MAX_XDEPTH), then the rest of the LDS goes to more code rounds; each
 // copying wave's pending copies must fit its counter (63).
-constexpr int mm_xdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd, int occ) {
+constexpr int mm_xdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd, int occ,
+                        int xr = 0) {
   const int lds = LDS_LIMIT / occ;
-  const int xs = mm_xslot(fmt, mt, g, wk, rd), cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
-  const int xpp = (mm_xcopies(fmt, mt, g, wk, rd) + MM_XP - 1) / MM_XP;
+  const int xs = mm_xslot(fmt, mt, g, wk, rd, xr), cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
+  const int xpp = (mm_xcopies(fmt, mt, g, wk, rd, xr) + MM_XP - 1) / MM_XP;
   int dcmin = (MM_CODE_AHEAD / occ + cs - 1) / cs;
   dcmin = dcmin < 2 ? 2 : (dcmin > MM_MAX_CDEPTH ? MM_MAX_CDEPTH : dcmin);
   int d = MM_MAX_XDEPTH;
   while (d > 0 && ((d + 1) * xs + (dcmin + 1) * cs > lds || (d - 1) * xpp > 63)) d--;
   return d;
 }
-constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd, int occ) {
-  const int left = LDS_LIMIT / occ - (mm_xdepth(fmt, mt, g, wr, wk, nt, rd, occ) + 1) *
-                                         mm_xslot(fmt, mt, g, wk, rd);
+constexpr int mm_cdepth(int fmt, int mt, int g, int wr, int wk, int nt, int rd, int occ,
+                        int xr = 0) {
+  const int left = LDS_LIMIT / occ - (mm_xdepth(fmt, mt, g, wr, wk, nt, rd, occ, xr) + 1) *
+                                         mm_xslot(fmt, mt, g, wk, rd, xr);
   const int cs = mm_cslot(fmt, mt, g, wr, wk, nt, rd);
   const int cpp = (mm_ccopies(fmt, mt, g, wr, wk, nt, rd) + MM_CP - 1) / MM_CP;
   int d = MM_MAX_CDEPTH;
@@ -210,18 +217,21 @@ static constexpr Plan kPlans[] = {
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
 // Compile-time shape of one kernel instance.
-template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_, int OCC_ = 1>
+template <int FMT_, int MT_, int NT_, int WR_, int WK_, int G_, int RD_, int OCC_ = 1,
+          int XR_ = 0>
 struct Mm {
   static constexpr int FMT = FMT_, MT = MT_, NT = NT_, WR = WR_, WK = WK_, G = G_, RD = RD_;
+  static constexpr int XR = mm_xr(MT_, XR_);        // x rows staged per round
+  static_assert(XR == 16 * MT || (MT == 1 && (XR == 4 || XR == 8)), "x rows");
   static constexpr int OCC = OCC_;                  // workgroups meant to share a CU
   static constexpr int LDS_MAX = LDS_LIMIT / OCC;   // LDS bytes this workgroup may take
   static constexpr int W = WR * WK;                 // multiplying waves
   static constexpr int THREADS = 64 * (W + MM_XP + MM_CP);
   static constexpr int KC = mm_kc(FMT, MT, WK, G, RD);  // k per wave chunk
   static constexpr int ROUND = WK * KC;             // k per round
-  static constexpr int DX = mm_xdepth(FMT, MT, G, WR, WK, NT, RD, OCC);  // x rounds ahead
-  static constexpr int DC = mm_cdepth(FMT, MT, G, WR, WK, NT, RD, OCC);  // code rounds ahead
-  static constexpr int MP = 16 * MT;                // padded activation rows
+  static constexpr int DX = mm_xdepth(FMT, MT, G, WR, WK, NT, RD, OCC, XR);  // x rounds ahead
+  static constexpr int DC = mm_cdepth(FMT, MT, G, WR, WK, NT, RD, OCC, XR);  // code rounds ahead
+  static constexpr int MP = XR;                     // staged activation rows
   static constexpr int TR = 16 * NT;                // rows per wave
   static constexpr int ROWS = TR * WR;              // rows per workgroup
   static constexpr int XSTR = ROUND + 8;            // halves per LDS row of x
@@ -243,7 +253,7 @@ struct Mm {
   static constexpr int HRS = ROUND / 8 * HB;
   static constexpr int HPR = HRS / 16;              // 16-byte pieces per row and round
   // LDS: x ring (DX+1 slots), then code ring (DC+1 slots)
-  static constexpr int XSLOT = mm_xslot(FMT, MT, G, WK, RD);
+  static constexpr int XSLOT = mm_xslot(FMT, MT, G, WK, RD, XR);
   static constexpr int CSLOT = mm_cslot(FMT, MT, G, WR, WK, NT, RD);
   static constexpr int CRING = (DX + 1) * XSLOT;    // byte offset of the code ring
   static constexpr int C_OFF = 0;                   // within a code slot
@@ -279,7 +289,7 @@ struct Mm {
   static constexpr bool REGS = NT * MT * OCC <= (THREADS > 512 ? 4 : 8);
   static constexpr bool FITS = VALID && REGS && DX >= 1 && DC >= 1 &&
                                LDS_BYTES <= LDS_MAX && RED * 4 <= LDS_MAX;
-  static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD) &&
+  static_assert(!FITS || (XN == mm_xcopies(FMT, MT, G, WK, RD, XR) &&
                           CHN + SN == mm_ccopies(FMT, MT, G, WR, WK, NT, RD)),
                 "copy counts");
   static_assert(CPIECES % 64 == 0, "code rows are whole copies");
@@ -473,7 +483,8 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
         const _Float16* src =
-            xb + (mt * 16 + col) * S::XSTR + kx + g * G + h * QPL + s * (KS / 4);
+            xb + (S::XR < 16 ? (col & (S::XR - 1)) : mt * 16 + col) * S::XSTR + kx + g * G +
+            h * QPL + s * (KS / 4);
         if constexpr (mm_byte(FMT)) {
           const u32x2 v = *reinterpret_cast<const u32x2*>(src);
           a[s][mt][0] = v.x; a[s][mt][1] = v.y;
@@ -882,38 +893,38 @@ hipError_t launch_s(const Problem* const* p, int count, const GemmCfg& c, float*
   }
 }
 
-// The instance of plan P (an index into kPlans).
-template <int FMT, int MT, int G, int P>
-using MmPlan =
-    Mm<FMT, MT, kPlans[P].nt, kPlans[P].wr, kPlans[P].wk, G, kPlans[P].rd, kPlans[P].occ>;
+// The instance of plan P (an index into kPlans); XR as in Mm.
+template <int FMT, int MT, int G, int P, int XR = 0>
+using MmPlan = Mm<FMT, MT, kPlans[P].nt, kPlans[P].wr, kPlans[P].wk, G, kPlans[P].rd,
+                  kPlans[P].occ, XR>;
 
-template <int FMT, int MT, int G, int P = 0>
+template <int FMT, int MT, int G, int XR, int P = 0>
 hipError_t launch_plan(const Problem* const* p, int n, const GemmCfg& c, float* ws,
                        hipStream_t s) {
   if constexpr (P >= kNumPlans) {
     return hipErrorInvalidValue;  // no such plan
   } else {
-    if (c.plan == P) return launch_s<MmPlan<FMT, MT, G, P>>(p, n, c, ws, s);
-    return launch_plan<FMT, MT, G, P + 1>(p, n, c, ws, s);
+    if (c.plan == P) return launch_s<MmPlan<FMT, MT, G, P, XR>>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, G, XR, P + 1>(p, n, c, ws, s);
   }
 }
 
-template <int FMT, int MT>
+template <int FMT, int MT, int XR = 0>
 hipError_t launch_group(const Problem* const* p, int n, const GemmCfg& c, float* ws,
                         hipStream_t s) {
   const int g = p[0]->group;
   if constexpr (FMT == FMT_F8) {
-    return launch_plan<FMT, MT, MM_F8_GROUP>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, MM_F8_GROUP, XR>(p, n, c, ws, s);
   } else if constexpr (FMT == FMT_S8) {
-    if (g == 16) return launch_plan<FMT, MT, 16>(p, n, c, ws, s);
-    if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
-    return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
+    if (g == 16) return launch_plan<FMT, MT, 16, XR>(p, n, c, ws, s);
+    if (g == 32) return launch_plan<FMT, MT, 32, XR>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 64, XR>(p, n, c, ws, s);
   } else if constexpr (is_asym(FMT)) {
-    return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 32, XR>(p, n, c, ws, s);
   } else {
-    if (g == 32) return launch_plan<FMT, MT, 32>(p, n, c, ws, s);
-    if (g == 64) return launch_plan<FMT, MT, 64>(p, n, c, ws, s);
-    return launch_plan<FMT, MT, 128>(p, n, c, ws, s);
+    if (g == 32) return launch_plan<FMT, MT, 32, XR>(p, n, c, ws, s);
+    if (g == 64) return launch_plan<FMT, MT, 64, XR>(p, n, c, ws, s);
+    return launch_plan<FMT, MT, 128, XR>(p, n, c, ws, s);
   }
 }
 
@@ -921,7 +932,10 @@ template <int FMT>
 hipError_t launch_fmt(const Problem* const* p, int n, const GemmCfg& c, float* ws,
                       hipStream_t s) {
   switch (c.mt) {
-    case 1: return launch_group<FMT, 1>(p, n, c, ws, s);
+    case 1:
+      if (c.xr == 4) return launch_group<FMT, 1, 4>(p, n, c, ws, s);
+      if (c.xr == 8) return launch_group<FMT, 1, 8>(p, n, c, ws, s);
+      return launch_group<FMT, 1>(p, n, c, ws, s);
     case 2: return launch_group<FMT, 2>(p, n, c, ws, s);
     case 3: return launch_group<FMT, 3>(p, n, c, ws, s);
     default: return launch_group<FMT, 4>(p, n, c, ws, s);

@@ -18,33 +18,37 @@ static int round_k(int fmt, int mt, int group, int plan) {
 // Whether plan `plan` fits (LDS, registers, copy layout) for the format, M-tile
 // count and group: read from the kernel instance's own FITS, so the host and
 // the device cannot disagree.
-template <int FMT, int MT, int G, size_t... P>
+template <int FMT, int MT, int G, int XR, size_t... P>
 static constexpr std::array<bool, kNumPlans> fits_row(std::index_sequence<P...>) {
-  return {{MmPlan<FMT, MT, G, (int)P>::FITS...}};
+  return {{MmPlan<FMT, MT, G, (int)P, XR>::FITS...}};
 }
-template <int FMT, int MT, int G>
+template <int FMT, int MT, int G, int XR>
 static constexpr std::array<bool, kNumPlans> kFits =
-    fits_row<FMT, MT, G>(std::make_index_sequence<kNumPlans>{});
+    fits_row<FMT, MT, G, XR>(std::make_index_sequence<kNumPlans>{});
 
-template <int FMT, int MT>
+template <int FMT, int MT, int XR = 0>
 static bool fits_mt(int g, int plan) {
   if constexpr (FMT == FMT_F8) {
-    return g == MM_F8_GROUP && kFits<FMT, MT, MM_F8_GROUP>[plan];
+    return g == MM_F8_GROUP && kFits<FMT, MT, MM_F8_GROUP, XR>[plan];
   } else if constexpr (is_asym(FMT)) {
-    return g == SB_GROUP && kFits<FMT, MT, SB_GROUP>[plan];
+    return g == SB_GROUP && kFits<FMT, MT, SB_GROUP, XR>[plan];
   } else if constexpr (FMT == FMT_S8) {
-    return g == 16 ? kFits<FMT, MT, 16>[plan]
-                   : (g == 32 ? kFits<FMT, MT, 32>[plan] : (g == 64 && kFits<FMT, MT, 64>[plan]));
+    return g == 16 ? kFits<FMT, MT, 16, XR>[plan]
+                   : (g == 32 ? kFits<FMT, MT, 32, XR>[plan]
+                              : (g == 64 && kFits<FMT, MT, 64, XR>[plan]));
   } else {
-    return g == 32 ? kFits<FMT, MT, 32>[plan]
-                   : (g == 64 ? kFits<FMT, MT, 64>[plan] : (g == 128 && kFits<FMT, MT, 128>[plan]));
+    return g == 32 ? kFits<FMT, MT, 32, XR>[plan]
+                   : (g == 64 ? kFits<FMT, MT, 64, XR>[plan]
+                              : (g == 128 && kFits<FMT, MT, 128, XR>[plan]));
   }
 }
 
 template <int FMT>
-static bool fits_fmt(int mt, int g, int plan) {
+static bool fits_fmt(int mt, int g, int plan, int xr) {
   switch (mt) {
-    case 1: return fits_mt<FMT, 1>(g, plan);
+    case 1:
+      return xr == 4 ? fits_mt<FMT, 1, 4>(g, plan)
+                     : (xr == 8 ? fits_mt<FMT, 1, 8>(g, plan) : fits_mt<FMT, 1>(g, plan));
     case 2: return fits_mt<FMT, 2>(g, plan);
     case 3: return fits_mt<FMT, 3>(g, plan);
     case 4: return fits_mt<FMT, 4>(g, plan);
@@ -52,24 +56,30 @@ static bool fits_fmt(int mt, int g, int plan) {
   }
 }
 
-static bool plan_fits(int fmt, int mt, int g, int plan) {
+// xr: x rows staged per round (4 or 8 for one M-tile, 0 for 16 * mt)
+static bool plan_fits(int fmt, int mt, int g, int plan, int xr = 0) {
   if (plan < 0 || plan >= kNumPlans) return false;
+  if (xr != 0 && (mt != 1 || (xr != 4 && xr != 8))) return false;
   switch (fmt) {
-    case FMT_S4: return fits_fmt<FMT_S4>(mt, g, plan);
-    case FMT_S8: return fits_fmt<FMT_S8>(mt, g, plan);
-    case FMT_A4: return fits_fmt<FMT_A4>(mt, g, plan);
-    case FMT_A5: return fits_fmt<FMT_A5>(mt, g, plan);
-    case FMT_A6: return fits_fmt<FMT_A6>(mt, g, plan);
-    case FMT_F8: return fits_fmt<FMT_F8>(mt, g, plan);
+    case FMT_S4: return fits_fmt<FMT_S4>(mt, g, plan, xr);
+    case FMT_S8: return fits_fmt<FMT_S8>(mt, g, plan, xr);
+    case FMT_A4: return fits_fmt<FMT_A4>(mt, g, plan, xr);
+    case FMT_A5: return fits_fmt<FMT_A5>(mt, g, plan, xr);
+    case FMT_A6: return fits_fmt<FMT_A6>(mt, g, plan, xr);
+    case FMT_F8: return fits_fmt<FMT_F8>(mt, g, plan, xr);
     default: return false;
   }
 }
 
+// x rows to stage for M activation rows: only as many as the rows present
+// when M <= 8 (fewer copies per round; the copies bound the 16-row plans).
+static int x_rows(int M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 0); }
+
 // The plan can run this problem: K is a whole number of rounds, a row's
 // scales are whole dwords, and the workgroup's layout fits the LDS.
-static bool plan_ok(int fmt, int mt, int group, int K, int plan) {
+static bool plan_ok(int fmt, int mt, int group, int K, int plan, int xr = 0) {
   const int rk = round_k(fmt, mt, group, plan);
-  return K % rk == 0 && (K / group) % 2 == 0 && plan_fits(fmt, mt, group, plan);
+  return K % rk == 0 && (K / group) % 2 == 0 && plan_fits(fmt, mt, group, plan, xr);
 }
 
 size_t gemm_workspace_floats(const GemmCfg& c, int M, int N) {
@@ -80,7 +90,7 @@ bool gemm_supports(int fmt, int M, int K, int group) {
   if (fmt == FMT_F8) group = MM_F8_GROUP;
   const int mt = (M + 15) / 16;
   for (int p = 0; p < kNumPlans; p++)
-    if (plan_ok(fmt, mt, group, K, p)) return true;
+    if (plan_ok(fmt, mt, group, K, p, x_rows(M))) return true;
   return false;
 }
 
@@ -88,6 +98,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   if (fmt == FMT_F8) group = MM_F8_GROUP;
   GemmCfg c{};
   c.mt = (M + 15) / 16;
+  c.xr = x_rows(M);
   c.splits = 1;
   const Tuning& tu = tuning();
   // Preference order by row count: with few rows, more K-slices per
@@ -130,7 +141,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
     order = small_n;
   c.plan = -1;
   if (tu.gemm_plan > 0 && tu.gemm_plan <= kNumPlans &&
-      plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1))
+      plan_ok(fmt, c.mt, group, K, tu.gemm_plan - 1, c.xr))
     c.plan = tu.gemm_plan - 1;
   // Measured best arrangements for the RWKV-7 matrices of the 1.5B- and
   // 2.9B-shaped workloads (one product, weights cold; sweeps of every plan x
@@ -156,7 +167,7 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   if (c.plan < 0 && blocks48 == 0) {
     for (const Tuned& t : tuned) {
       if (t.fmt == fmt && t.group == group && t.mt == c.mt && t.N == N && t.K == K &&
-          plan_ok(fmt, c.mt, group, K, t.plan)) {
+          plan_ok(fmt, c.mt, group, K, t.plan, c.xr)) {
         c.plan = t.plan;
         tuned_splits = t.splits;
         break;
@@ -171,10 +182,10 @@ GemmCfg choose_gemm(int fmt, int M, int N, int K, int group, int blocks48, bool 
   const int b48 = blocks48 > 0 ? blocks48 : (N + 47) / 48;
   if (c.plan < 0 && !split_k && b48 >= 224 && b48 <= 256) {
     const int p48 = c.mt <= 2 ? 17 : 15;
-    if (plan_ok(fmt, c.mt, group, K, p48)) c.plan = p48;
+    if (plan_ok(fmt, c.mt, group, K, p48, c.xr)) c.plan = p48;
   }
   for (int i = 0; i < kNumPlans && c.plan < 0; i++)
-    if (plan_ok(fmt, c.mt, group, K, order[i])) c.plan = order[i];
+    if (plan_ok(fmt, c.mt, group, K, order[i], c.xr)) c.plan = order[i];
   // Splits divide K into whole rounds and the partial sums stay under 64 MiB.
   // Automatic only in the case above, enough row blocks x K-ranges for 256
   // CUs (at most 4); RQ_GEMM_SPLITS overrides.

@@ -57,6 +57,7 @@ struct GemmCfg {
   int mt;      // 16-row M-tiles (1..4)
   int plan;    // workgroup arrangement (index into the kernel's plan table)
   int splits;  // K split across workgroups
+  int xr;      // x rows staged per round: 4 or 8 for M <= 4 or 8, else 0 (16 * mt)
 };
 
 // The matrix-core kernel needs K to be a whole number of its rounds.

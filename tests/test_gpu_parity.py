@@ -283,7 +283,7 @@ def test_gemm_split_and_plans(tune, splits, plan):
     ran = 0
     for f in (S.INT4_G64, S.INT8_G16, S.ASYM4_G32):
         p = small(f, 300, 4096, tag=6)
-        for M in (16, 33, 64):
+        for M in (5, 16, 33, 64):  # M = 5 stages 8 x rows per round
             if not forced_plan_taken(f, M, 300, 4096, plan):
                 T.say(f"gemm splits={splits} plan={plan} {f.tag} M={M}: plan cannot take it")
                 continue
@@ -304,7 +304,7 @@ def test_gemm_plans_all_formats(tune, plan, f):
     tune(RQ_GEMM_PLAN=plan)
     p = small(f, 130, 2048, tag=9)
     ran = 0
-    for M in (17, 48):
+    for M in (3, 7, 17, 48):  # 4 and 8 staged x rows, then 16 per M-tile
         if not forced_plan_taken(f, M, 130, 2048, plan):
             T.say(f"gemm plan={plan} {f.tag} M={M}: plan cannot take it")
             continue
@@ -315,7 +315,7 @@ def test_gemm_plans_all_formats(tune, plan, f):
         T.assert_close(y, yr, b, f"plan={plan} {f.tag} M={M}")
         ran += 1
     if not ran:
-        pytest.skip(f"plan {plan} cannot take {f.tag} at K=2048, M=17 or 48")
+        pytest.skip(f"plan {plan} cannot take {f.tag} at K=2048, M=3, 7, 17 or 48")
 
 
 # ------------------------------------------------------ exact cases ---

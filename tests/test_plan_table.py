@@ -44,6 +44,11 @@ def test_every_format_has_plans_at_every_m_tile(table):
     for name in ("int4", "int8", "asym4", "asym5", "asym6", "fp8"):
         for mt in (1, 2, 3, 4):
             assert (name, f"mt={mt}") in have, (name, mt)
+    # one M-tile with 4 or 8 staged x rows (M <= 4, M <= 8) as well
+    xr = {(l[1], l[3]) for l in lines if l[2] == "mt=1"}
+    for name in ("int4", "int8", "asym4", "asym5", "asym6", "fp8"):
+        for r in ("xr=4", "xr=8", "xr=0"):
+            assert (name, r) in xr, (name, r)
 
 
 def test_lds_within_the_cu(table):
@@ -57,7 +62,7 @@ def test_48_row_four_slice_plan_fits_past_48_rows(table):
     """The 48-row, four-K-slice arrangement (plan index 17) fits at four M-tiles
     for int4 group 64: its K-slice reduction takes 48 KiB, well inside the LDS
     (a byte count taken four times too large once excluded it)."""
-    assert "fits int4 mt=4 g=64 plan=17 " in table.stdout
+    assert "fits int4 mt=4 xr=0 g=64 plan=17 " in table.stdout
 
 
 def test_gpu_tests_cover_every_plan(table):
