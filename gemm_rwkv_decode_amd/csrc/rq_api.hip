@@ -226,13 +226,12 @@ enum Kernel { KERN_VECTOR, KERN_DECODE_MFMA, KERN_SMALLM_MFMA };
 // The kernel rq_gemv and rq_gemv_batched use for M activation rows (N: rows of
 // the launch).  Measured on MI355X, weights cold in HBM, int4 g64 / int8 g16 /
 // asym4 / FP8 / 5- and 6-bit codes at widths 2048..4096 and K up to 16384:
-//  * M >= 5: the small-batch matrix-core kernel (M padded to 16) beats the
-//    vector-unit passes of eight rows by 1.35x to 11x (int4 4096x4096 M = 8:
-//    11.5 -> 5.8 us; 2560x10240 asymmetric M = 8: 65.7 -> 13.1 us).
-//  * M = 3..4: the same kernel for int4, int8 and FP8 (int8 8192x2048 M = 4:
-//    8.6 us on the decode kernel -> 7.6 us); the decode kernel for asymmetric
-//    4-bit (2560x10240: 11.7 vs 12.8 us); the vector-unit kernel for 5- and
-//    6-bit codes (16384x4096: 20.8 vs 23.0 us).
+//  * M >= 3: the small-batch matrix-core kernel (4 or 8 x rows staged for
+//    M <= 4 or 8, else 16 per M-tile) beats the vector-unit passes of eight
+//    rows by up to 11x (int4 4096x4096 M = 8: 11.5 -> 5.3 us; 2560x10240
+//    asymmetric M = 8: 65.7 -> 11.0 us) and, at M = 3..4, the decode kernel
+//    (int8 8192x2048 M = 4: 7.5 -> 6.8 us; asymmetric 2560x2560 M = 4:
+//    6.1 -> 5.2 us; 5-bit 16384x4096 M = 4: 20.2 -> 19.5 us).
 //  * M <= 2: the vector-unit kernel, unless none of its tuned launch shapes
 //    splits the row (the generic kernel: FP8 4096x16384 at M = 2 takes
 //    52.1 us there, 18.0 us on the small-batch kernel).  Then the decode
@@ -257,18 +256,8 @@ Kernel pick_kernel(int fmt, int M, int N, int K, int group, rq::GemvCfg* gc) {
     k = mv ? KERN_DECODE_MFMA : KERN_VECTOR;
   } else if (t == 3) {
     k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
-  } else if (M >= 5) {
-    k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
   } else if (M >= 3) {
-    if (fmt == FMT_A4 && mv) {
-      k = KERN_DECODE_MFMA;
-    } else if (fmt == FMT_A5 || fmt == FMT_A6) {
-      *gc = rq::choose_gemv(fmt, M, N, K);
-      if (gc->lpr != 0) return KERN_VECTOR;
-      k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
-    } else {
-      k = mm ? KERN_SMALLM_MFMA : (mv ? KERN_DECODE_MFMA : KERN_VECTOR);
-    }
+    k = mm ? KERN_SMALLM_MFMA : (mv ? KERN_DECODE_MFMA : KERN_VECTOR);
   } else {  // M <= 2 on the generic vector-unit kernel
     if (mv && (fmt == FMT_S4 || fmt == FMT_A4 || !mm)) return KERN_DECODE_MFMA;
     k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;

@@ -1,7 +1,8 @@
 """A decode step captured as a HIP graph and replayed gives the same outputs
 as direct launches, bit for bit, on every replay (the kernels are
 deterministic), with other GPU work between replays.  Covers the grouped
-vector-unit launch (M = 1), the matrix-core decode kernel (M = 4), grouped
+vector-unit launch (M = 1), the small-batch matrix-core kernel with four
+staged activation rows (M = 4), grouped
 matrix-core launches (M = 16) and the split-K path with its in-launch
 reduction (M = 64, few long rows), rq_gemv on the matrix cores captured as
 the first call on a fresh stream, and rq_gemm_smallm captured after one eager

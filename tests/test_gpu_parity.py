@@ -230,8 +230,8 @@ def test_decode_kernels(tune, f, kern):
     (S.INT4_G64, 65536, 1),    # decode kernel
     (S.ASYM4_G32, 65536, 1),   # decode kernel
     (S.INT4_G64, 16384, 3),    # small-batch kernel at M = 3
-    (S.ASYM5_G32, 4096, 4),    # vector-unit kernel kept for 5-bit codes
-    (S.ASYM5_G32, 16384, 4),   # ... unless the row is too long for it
+    (S.ASYM5_G32, 4096, 4),    # small-batch kernel from M = 3 for every format
+    (S.ASYM5_G32, 16384, 4),   # the same with long rows
 ], ids=lambda v: getattr(v, "tag", str(v)))
 def test_kernel_choice_long_rows(f, K, M):
     """Rows too long for the vector-unit kernel's tuned launch shapes take a
@@ -418,7 +418,7 @@ def test_batched_matches_oracle(f, M):
     """Mixed N and K in one call (K groups share launches), more problems than
     one launch holds, and a K the tuned kernel cannot split."""
     shapes = [(256, 1024), (100, 1024), (300, 2048), (64, 1024)] * 5 + [(40, 768)]
-    shapes += [(130, 4096), (64, 4096), (17, 4096)] * 7  # matrix-core decode kernel at M <= 4
+    shapes += [(130, 4096), (64, 4096), (17, 4096)] * 7  # matrix-core kernels at M <= 4
     if f.layout == S.LAYOUT_SYM and f.bits == 4:
         shapes.append((33, 64 * 7))  # 14 chunks: generic kernel
     mats = [small(f, N, K, tag=20 + i) for i, (N, K) in enumerate(shapes)]
