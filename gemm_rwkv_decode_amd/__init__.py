@@ -142,7 +142,7 @@ def rq_dequant(qweight, scales, zeros, out, N, K, bits, group, layout,
 
 def rq_gemv(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, stream=None):
     """y[m][n] = sum_k x[m][k] w[n][k]; the kernel is chosen for M (vector units
-    at M <= 2, matrix cores from M = 5 on), K is never split, nothing is
+    at M <= 2, matrix cores from M = 3 on), K is never split, nothing is
     allocated."""
     st = lib().rq_gemv(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y), int(M),
                        int(N), int(K), int(bits), int(group), int(layout),

@@ -1,5 +1,5 @@
 // rq_gemm_impl.h -- the matrix-core kernel k_mm and its launch templates,
-// shared by rq_gemm.hip (plan choice, dispatch, split-K reduce) and the
+// shared by rq_gemm_plan.h (plan choice), rq_gemm.hip (dispatch) and the
 // per-format translation units rq_gemm_<format>.hip that instantiate it (so
 // the instances compile in parallel).
 //
@@ -23,19 +23,19 @@
 //
 // Work split (MI355X: 256 CUs, 64 B/clk per CU from L2, ~160 B/clk of LDS
 // reads).  A workgroup owns WR*NT*16 rows and the whole K range (or one
-// K-range when K is split across workgroups).  Its W = WR*WK waves form WR
-// row groups of NT 16-row tiles times WK K-slices.  K advances in rounds of
-// WK*KC k: in a round, K-slice w multiplies the w-th KC-wide chunk.  The
-// round's x tile [M][WK*KC] is staged once per workgroup into LDS (double
-// buffered, one barrier per round) with coalesced 16-byte loads; every wave
-// reads its MFMA fragments from there.  Codes and scales are prefetched D
-// rounds ahead into registers.  At the end the WK K-slices of a row group
-// are added in a fixed order through LDS, so no other workgroup and no
-// second kernel is involved.  Every workgroup of a launch on a small-N
-// matrix reads all of x, so staging x (M*K*2 bytes per workgroup at up to
-// 64 B/clk) bounds those launches; splitting K over workgroups shortens it at
-// the price of a partial-sum workspace and a reduce kernel, used only where
-// that wins.
+// K-range when K is split across workgroups).  Its W = WR*WK multiplying
+// waves form WR row groups of NT 16-row tiles times WK K-slices; MM_XP + MM_CP
+// more waves only copy.  K advances in rounds of WK*KC k: in a round, K-slice
+// w multiplies the w-th KC-wide chunk.  The copying waves stream the round's
+// x tile [MP][WK*KC] (from L2) and the rows' codes and scale material (from
+// HBM) into LDS rings of DX+1 and DC+1 round slots, DX and DC rounds ahead,
+// with global->LDS buffer loads; one barrier per round hands a slot over, and
+// every multiplying wave reads its MFMA fragments from there.  At the end
+// the WK K-slices of a row group are added in a fixed order through LDS.
+// Every workgroup stages all of x (MP*K*2 bytes), and a wave issues about one
+// 1 KB global->LDS copy per 50 cycles, so the copies bound the 16-row plans;
+// splitting K over workgroups shortens them at the price of a partial-sum
+// workspace and the in-launch reduction below, used only where that wins.
 //
 // Split-K reduction, in the same launch.  When the K dimension is split, each
 // multiplying wave that stores a 16-row tile writes its partial tile to the

@@ -21,10 +21,9 @@ import gemm_rwkv_decode_amd as rq
 RECEPTANCE, KEY, VALUE, OUTPUT, FFN_KEY, FFN_VALUE, HEAD = range(7)
 
 # Smallest M a step sends to rq_gemm_smallm, which may split K over
-# workgroups (through its workspace).  From M = 5 on rq_gemv and
-# rq_gemv_batched run the same matrix-core kernel but keep K whole; below it
-# rq_gemv picks the kernel for M (vector units or the decode matrix-core
-# kernel).
+# workgroups (through its workspace).  Below it the step calls rq_gemv and
+# rq_gemv_batched, which pick the kernel for M (vector units at M <= 2, the
+# same matrix-core kernel from M = 3 on, with K kept whole).
 MFMA_MIN_M = 5
 
 KINDS = ("layer", "matrix", "batched")

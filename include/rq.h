@@ -141,14 +141,13 @@ rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
  *   x: binary16 [M][K] row-major.  y: float [M][N] row-major, overwritten.
  * Each output is within 1e-3 * sum_k |x[m][k] * w[n][k]| of the exact value
  * (fp32 accumulation).  The kernel is chosen per M, format and shape:
- * vector units at M <= 2 (matrix cores where K is too long for their tuned
- * launch shapes); at M = 3..4 a matrix-core decode kernel (where K
- * holds at least eight of its chunks: 8 groups, or one 256-weight superblock,
- * each) or, for int4, int8 and FP8, the small-batch matrix-core kernel of
- * rq_gemm_smallm; from M = 5 on that small-batch kernel (M padded to a
- * multiple of 16); the vector units, in passes of up to 8 rows, wherever K
- * does not suit the matrix-core kernels.  The small-batch kernel runs here
- * with K whole: this entry point never allocates or synchronizes.
+ * vector units at M <= 2 (a matrix-core kernel where K is too long for their
+ * tuned launch shapes); from M = 3 on the small-batch matrix-core kernel of
+ * rq_gemm_smallm (4 or 8 activation rows staged for M <= 4 or 8, else M
+ * padded to a multiple of 16), or the matrix-core decode kernel where the
+ * former does not take K; the vector units, in passes of up to 8 rows,
+ * wherever K suits neither.  The small-batch kernel runs here with K whole:
+ * this entry point never allocates or synchronizes.
  * Shape rules as for rq_dequant, plus 1 <= M <= RQ_MAX_M.
  */
 rq_status rq_gemv(const void* qweight, const void* scales, const void* zeros,
@@ -181,8 +180,9 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
  * int4 GPTQ for rwkv-sglang" names in its "Speed" line (a small-M GEMM next
  * to the GEMV, credited with beating fp16 at every batch up to 32).  Every
  * layout and code width, 5- and 6-bit codes included.
- * Tuned for 16 <= M <= 64 (batched decode); smaller M is padded to 16, which
- * still beats the vector units from M = 5 on.
+ * Tuned for 16 <= M <= 64 (batched decode); for M <= 4 or 8 only 4 or 8
+ * activation rows are staged per round, otherwise M is padded to a multiple
+ * of 16; it beats the vector units from M = 3 on.
  * Workspace.  For some shapes the K dimension is split across workgroups and
  * the partial sums pass through a workspace of 64 MiB that the library
  * allocates (and zeroes its arrival counters) at the first such call on a
