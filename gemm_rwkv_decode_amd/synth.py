@@ -322,6 +322,11 @@ def massive_channels(cfg: Config, layer: int, mat: int, K: int) -> Tuple[List[in
     xs = cfg.x
     if xs.kind == "plain":
         return [], 1.0
+    # the recipe's fixed channels must exist in a K-channel input (checked on
+    # the host: an index past K would reach the device unchecked)
+    fixed = [xs.channel] if xs.kind == "fixed" else list(xs.forced)
+    if any(not 0 <= c < K for c in fixed):
+        raise ValueError(f"{cfg.key}: massive channel {fixed} outside a {K}-wide input")
     if xs.kind == "fixed":
         return [xs.channel], xs.factor
     g = generator(seed_for(cfg.key, layer, mat, "channels", "x", 0), "cpu")

@@ -79,6 +79,18 @@ def test_massive_channels_fixed():
     assert big > 10 * rest
 
 
+def test_massive_channel_outside_the_input_is_refused():
+    """A recipe's fixed channel past K raises on the host, before any tensor
+    is indexed (on the GPU an index past the end would not be checked)."""
+    with pytest.raises(ValueError):
+        S.massive_channels(S.CONFIGS["rwkv7-1.5b"], 0, 0, 768)   # channel 1202
+    with pytest.raises(ValueError):
+        S.gen_x(S.CONFIGS["rwkv7-1.5b"], 0, 0, 1, 768)
+    with pytest.raises(ValueError):
+        S.massive_channels(S.CONFIGS["rwkv7-2.9b"], 0, 0, 512)   # forced channel 517
+    assert S.massive_channels(S.CONFIGS["rwkv7-2.9b"], 0, 0, 2560)[0][0] == 517
+
+
 @pytest.mark.parametrize("wkey,K,share", [("rwkv7-2.9b", 2560, 0.98),
                                           ("rwkv7-2.9b", 10240, 0.98),
                                           ("rwkv7-13.3b", 4096, 0.99),
