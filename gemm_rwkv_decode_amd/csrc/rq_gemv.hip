@@ -476,7 +476,8 @@ GemvCfg choose_gemv(int fmt, int M, int N, int K) {
     if ((N + 15) / 16 >= 512) best = 0;        // {16, 1, 4}
     else if ((N + 7) / 8 >= 512) best = 9;     // {16, 1, 2}
   }
-  for (int i = 0; i < ncand && best < 0; i++) {
+  const bool picked = best >= 0;
+  for (int i = 0; i < ncand && !picked; i++) {
     const int lpr = cand[i][0], cpl = cand[i][1], np = cand[i][2];
     if (chunks % (lpr * cpl)) continue;
     const int sk = chunks / (lpr * cpl);
@@ -496,6 +497,14 @@ GemvCfg choose_gemv(int fmt, int M, int N, int K) {
   c.lpr = cand[best][0];
   c.cpl = cand[best][1];
   c.npass = cand[best][2];
+  // few, long rows at M = 1 (the FFN value of widths 2048..2560): four rows
+  // per lane leave 256..320 workgroups; two rows per lane, where that stays
+  // at most 640 workgroups, measured faster (weights cold: int4 2048x8192
+  // 4.99 -> 4.07 us, int8 2048x8192 5.56 -> 5.08 us, asymmetric 2560x10240
+  // 7.37 -> 6.39 us; 4096x16384 keeps four: 512 workgroups, 8.45 against
+  // 9.8 us)
+  if (c.mt == 1 && c.npass == 4 && (N + (64 / c.lpr) * 2 - 1) / ((64 / c.lpr) * 2) <= 640)
+    c.npass = 2;
   if (forced > 0) {  // tuning: RQ_GEMV_LPR / RQ_GEMV_CPL / RQ_GEMV_NPASS
     const int cpl = tu.gemv_cpl ? tu.gemv_cpl : c.cpl;
     if (chunks % (forced * cpl) == 0 &&
