@@ -443,10 +443,15 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
       zfield[nt] = ((((uint64_t)zr[1] << 32) | zr[0]) >> 16) >> (6 * jb);
     }
   }
-#pragma unroll
-  for (int g = 0; g < S::GPC; g++) {
-    // this lane's codes: row n, bytes [cb0 + g*GB + h*BPL, +BPL) of the row
-    u32 code[NT][DPG];
+  // one group's LDS fragments: the lane's codes (row n, bytes [cb0 + g*GB +
+  // h*BPL, +BPL) of the row), for 5-/6-bit codes the high-bit dwords of the
+  // row's 32-code chunk, and the A fragments of every K-step and M-tile
+  struct Frag {
+    u32 code[S::NT][S::DPG];
+    u32 hw[S::NT][2];
+    u32 a[S::DPG][S::MT][4];
+  };
+  auto fetch = [&](int g, Frag& f) {
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
       const int n = wr * S::TR + nt * 16 + col;
@@ -455,29 +460,24 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
           sl + S::C_OFF + (n * S::PR + ((byte / 16) ^ (n & S::SWZ))) * 16 + byte % 16;
       if constexpr (S::BPL == 16) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        code[nt][0] = v.x; code[nt][1] = v.y; code[nt][2] = v.z; code[nt][3] = v.w;
+        f.code[nt][0] = v.x; f.code[nt][1] = v.y; f.code[nt][2] = v.z; f.code[nt][3] = v.w;
       } else if constexpr (S::BPL == 8) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-        code[nt][0] = v.x; code[nt][1] = v.y;
+        f.code[nt][0] = v.x; f.code[nt][1] = v.y;
       } else {
-        code[nt][0] = *reinterpret_cast<const u32*>(src);
+        f.code[nt][0] = *reinterpret_cast<const u32*>(src);
       }
     }
-    // 5-/6-bit codes: the high-bit dwords of the row's 32-code chunk
-    u32 hw[NT][2];
     if constexpr (S::HB > 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         const int n = wr * S::TR + nt * 16 + col;
         const u32* hp = reinterpret_cast<const u32*>(sl + S::H_OFF + n * S::HRS +
                                                      (cb0 / 16 + g) * 4 * S::HB);
-        hw[nt][0] = hp[0];
-        hw[nt][1] = S::HB == 2 ? hp[1] : 0u;
+        f.hw[nt][0] = hp[0];
+        f.hw[nt][1] = S::HB == 2 ? hp[1] : 0u;
       }
     }
-    f4 P[NT][MT];
-    // A fragments of every K-step of the group and every M-tile
-    u32 a[DPG][MT][4];
 #pragma unroll
     for (int s = 0; s < DPG; s++)
 #pragma unroll
@@ -487,18 +487,22 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
             h * QPL + s * (KS / 4);
         if constexpr (mm_byte(FMT)) {
           const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-          a[s][mt][0] = v.x; a[s][mt][1] = v.y;
+          f.a[s][mt][0] = v.x; f.a[s][mt][1] = v.y;
         } else {
           const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-          a[s][mt][0] = v.x; a[s][mt][1] = v.y; a[s][mt][2] = v.z; a[s][mt][3] = v.w;
+          f.a[s][mt][0] = v.x; f.a[s][mt][1] = v.y; f.a[s][mt][2] = v.z; f.a[s][mt][3] = v.w;
         }
       }
+  };
+  // group g's MFMAs and binary32 epilogue
+  auto compute = [&](int g, const Frag& f) {
+    f4 P[NT][MT];
 #pragma unroll
     for (int s = 0; s < DPG; s++) {
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         u32 b[4];
-        const u32 d = code[nt][s];
+        const u32 d = f.code[nt][s];
         if constexpr (mm_byte(FMT)) {
           h2 q[2];
           if constexpr (FMT == FMT_F8) unpack_fp8(d, q);
@@ -507,7 +511,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
         } else if constexpr (S::HB > 0) {
           // this lane's nibble dword is dword h of the group's 32-code chunk
           u32 hlo, hhi;
-          hi_words<S::HB>(hw[nt], h, &hlo, &hhi);
+          hi_words<S::HB>(f.hw[nt], h, &hlo, &hhi);
           h2 q[4];
           unpack4h<S::HB>(d, hlo, hhi, q);
           // pairs (q0,q4) (q1,q5) (q2,q6) (q3,q7) -> k order (q0,q1) .. (q6,q7)
@@ -526,7 +530,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
         for (int mt = 0; mt < MT; mt++) {
           // FP8: no group scale, so the products accumulate straight into acc
           const f4 c0 = (FMT == FMT_F8) ? acc[nt][mt] : f4{0, 0, 0, 0};
-          P[nt][mt] = mfma_step<FMT>(a[s][mt], b, s == 0 ? c0 : P[nt][mt]);
+          P[nt][mt] = mfma_step<FMT>(f.a[s][mt], b, s == 0 ? c0 : P[nt][mt]);
         }
       }
     }
@@ -537,7 +541,7 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
       const u32 one2 = 0x3C003C00u;  // binary16 (1, 1)
       const u32 ones[4] = {one2, one2, one2, one2};
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) xg[mt] = mfma_step<FMT>(a[0][mt], ones, f4{0, 0, 0, 0});
+      for (int mt = 0; mt < MT; mt++) xg[mt] = mfma_step<FMT>(f.a[0][mt], ones, f4{0, 0, 0, 0});
     }
     // group epilogue in binary32
 #pragma unroll
@@ -569,9 +573,34 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
         }
       }
     }
-    // keep the scheduler from hoisting later groups' LDS reads into this one
-    // (it would hold every group's fragments in registers at once)
-    if constexpr (MT * NT >= 4) __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (NT == 1 && MT <= 2 && S::OCC == 1 && S::XR == 16 * MT) {
+    // one 16-row tile per wave, one workgroup per CU, M <= 32: group g+1's
+    // fragments are read from LDS while group g is multiplied (two register
+    // sets; the scheduling barriers keep that order), which hides the LDS
+    // latency (int4, M = 32: 2-7% faster for these plans).  Plans with two
+    // tiles per wave hold twice the fragments and were 1-5% slower this way,
+    // and so were the M <= 8 steps, whose plans share a CU between two
+    // workgroups (half the registers each): 5-11%.
+    Frag f[2];
+    fetch(0, f[0]);
+#pragma unroll
+    for (int g = 0; g < S::GPC; g++) {
+      if (g + 1 < S::GPC) fetch(g + 1, f[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(g, f[g & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < S::GPC; g++) {
+      Frag f;
+      fetch(g, f);
+      compute(g, f);
+      // keep the scheduler from hoisting later groups' LDS reads into this one
+      // (it would hold every group's fragments in registers at once)
+      if constexpr (MT * NT >= 4) __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
