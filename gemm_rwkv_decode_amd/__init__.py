@@ -99,6 +99,8 @@ def lib():
             ip = ctypes.POINTER(ctypes.c_int)
             L.rq_gemm_config.argtypes = [i, i, i, i, i, i, i, ip, ip]
             L.rq_gemm_config.restype = i
+            L.rq_gemv_config.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
+            L.rq_gemv_config.restype = i
             _lib = L
     return _lib
 
@@ -236,6 +238,22 @@ def gemm_config(M, N, K, bits, group, layout, allow_split=True):
     if st != RQ_OK:
         raise RqError("rq_gemm_config", st)
     return plan.value, splits.value
+
+
+GEMV_KERNELS = ("vector", "decode_mfma", "smallm_mfma")
+
+
+def gemv_config(M, N, K, bits, group, layout):
+    """The kernel rq_gemv runs for one product, as (name, lpr, cpl, npass):
+    name one of GEMV_KERNELS; lpr, cpl, npass the vector-unit launch shape
+    (lanes per row, 0 for the generic kernel; 16-byte chunks per lane; rows
+    per lane), zeros for the matrix-core kernels.  Host-only."""
+    v = [ctypes.c_int(0) for _ in range(4)]
+    st = lib().rq_gemv_config(int(M), int(N), int(K), int(bits), int(group), int(layout),
+                              *[ctypes.byref(t) for t in v])
+    if st != RQ_OK:
+        raise RqError("rq_gemv_config", st)
+    return (GEMV_KERNELS[v[0].value],) + tuple(t.value for t in v[1:])
 
 
 def tuning_reload():

@@ -80,6 +80,17 @@ size_t scale_bytes(int N, int K, int group, int layout) {
                                      : (size_t)N * (K / group) * 2;
 }
 
+// Sizes every kernel takes: whole groups, rows of whole 16-byte chunks,
+// operands addressed with 32-bit offsets, whole superblocks.
+rq_status check_shape(int N, int K, int bits, int group, int layout) {
+  if (N < 1 || K < 1) return RQ_ERR_SHAPE;
+  if (group > 0 && (K < group || K % group != 0)) return RQ_ERR_SHAPE;
+  if (((size_t)K * bits / 8) % 16 != 0) return RQ_ERR_SHAPE;
+  if (code_bytes(N, K, bits) >= ((size_t)1 << 31)) return RQ_ERR_SHAPE;
+  if (layout == RQ_LAYOUT_ASYM_SB && K % 256 != 0) return RQ_ERR_SHAPE;
+  return RQ_OK;
+}
+
 // Shared checks of the weight description.  Returns RQ_OK and the format id.
 rq_status check_weights(const void* qweight, const void* scales, const void* zeros, int N,
                         int K, int bits, int group, int layout, int* fmt) {
@@ -90,12 +101,7 @@ rq_status check_weights(const void* qweight, const void* scales, const void* zer
   if (f < 0) return RQ_ERR_UNSUPPORTED;
   if (layout == RQ_LAYOUT_ASYM_SB && !zeros) return RQ_ERR_NULL;
   if (layout != RQ_LAYOUT_ASYM_SB && zeros) return RQ_ERR_UNSUPPORTED;
-  if (N < 1 || K < 1) return RQ_ERR_SHAPE;
-  if (group > 0 && (K < group || K % group != 0)) return RQ_ERR_SHAPE;
-  if (((size_t)K * bits / 8) % 16 != 0) return RQ_ERR_SHAPE;
-  // kernels index within an operand with 32-bit offsets
-  if (code_bytes(N, K, bits) >= ((size_t)1 << 31)) return RQ_ERR_SHAPE;
-  if (layout == RQ_LAYOUT_ASYM_SB && K % 256 != 0) return RQ_ERR_SHAPE;
+  if (check_shape(N, K, bits, group, layout) != RQ_OK) return RQ_ERR_SHAPE;
   if (!aligned16(qweight) || !aligned16(scales) || (zeros && !aligned16(zeros)))
     return RQ_ERR_ALIGN;
   *fmt = f;
@@ -466,6 +472,22 @@ int rq_gemm_config(int M, int N, int K, int bits, int group, int layout, int all
   const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group, 0, allow_split != 0);
   *plan = c.plan + 1;
   *splits = c.splits;
+  return RQ_OK;
+}
+
+int rq_gemv_config(int M, int N, int K, int bits, int group, int layout, int* kernel,
+                   int* lpr, int* cpl, int* npass) {
+  if (!kernel || !lpr || !cpl || !npass) return RQ_ERR_NULL;
+  const int fmt = format_of(layout, bits, group);
+  if (fmt < 0) return RQ_ERR_UNSUPPORTED;
+  if (M < 1 || M > RQ_MAX_M || check_shape(N, K, bits, group, layout) != RQ_OK)
+    return RQ_ERR_SHAPE;
+  rq::GemvCfg gc{};
+  const Kernel k = pick_kernel(fmt, M, N, K, group, &gc);
+  *kernel = (int)k;
+  *lpr = k == KERN_VECTOR ? gc.lpr : 0;
+  *cpl = k == KERN_VECTOR ? gc.cpl : 0;
+  *npass = k == KERN_VECTOR ? gc.npass : 0;
   return RQ_OK;
 }
 

@@ -86,6 +86,18 @@ int rq_tuning_reload(void);
 int rq_gemm_config(int M, int N, int K, int bits, int group, int layout, int allow_split,
                    int* plan, int* splits);
 
+/* The kernel rq_gemv runs for one product of M activation rows: *kernel
+ * receives 0 for the vector-unit kernel, 1 for the matrix-core decode kernel,
+ * 2 for the small-batch matrix-core kernel.  For the vector-unit kernel,
+ * *lpr receives the lanes per weight row (0 = the generic kernel, which
+ * splits no row), *cpl the 16-byte chunks per lane per row and *npass the
+ * rows each lane streams; all three are 0 for the other kernels.  Overrides
+ * in effect are applied.  Host-only; no GPU needed.  Returns
+ * RQ_ERR_UNSUPPORTED for an unknown format, RQ_ERR_SHAPE for sizes rq_gemv
+ * rejects. */
+int rq_gemv_config(int M, int N, int K, int bits, int group, int layout, int* kernel,
+                   int* lpr, int* cpl, int* npass);
+
 #ifdef __cplusplus
 }
 #endif

@@ -244,3 +244,88 @@ def test_gemm_config_on_the_host(L):
             assert 1 <= p <= 18 and s >= 1 and s * M * N * 4 <= 64 << 20
     with pytest.raises(rq.RqError):
         rq.gemm_config(0, 64, 256, 4, 64, 0)
+
+
+# vector-unit launch shapes the chooser takes for the RWKV-7 widths at M = 1
+# (lanes per row, 16-byte chunks per lane, rows per lane), as measured on MI355X
+GEMV_SHAPES_M1 = [
+    # (N, K, bits, group, layout) -> (lpr, cpl, npass)
+    ((4096, 4096, 4, 64, 0), (16, 1, 2)),    # 512 workgroups of two rows per lane
+    ((16384, 4096, 4, 64, 0), (16, 1, 4)),   # 1024 workgroups of four
+    ((4096, 16384, 4, 64, 0), (32, 1, 4)),   # 512 workgroups keep four
+    ((2048, 8192, 4, 64, 0), (32, 1, 2)),    # 256 -> 512 workgroups: two rows per lane
+    ((2048, 8192, 8, 16, 0), (32, 1, 2)),
+    ((2560, 10240, 4, 32, 1), (32, 1, 2)),
+    ((768, 768, 4, 64, 0), (8, 1, 1)),
+    ((3072, 768, 4, 64, 0), (8, 1, 1)),
+]
+
+
+def test_gemv_config_on_the_host(L):
+    """The kernel query of rq_probe.h: rq_gemv's choice of kernel and of the
+    vector-unit launch shape, on the host."""
+    for (N, K, bits, group, layout), shape in GEMV_SHAPES_M1:
+        assert rq.gemv_config(1, N, K, bits, group, layout) == ("vector",) + shape, (N, K, bits)
+    # matrix cores from M = 3 where the small-batch kernel takes K; the decode
+    # kernel for int4 rows too long for the vector kernel's shapes at M = 1
+    for M in (3, 4, 8, 16, 32, 64):
+        assert rq.gemv_config(M, 4096, 4096, 4, 64, 0)[0] == "smallm_mfma"
+        assert rq.gemv_config(M, 2560, 10240, 4, 32, 1)[0] == "smallm_mfma"
+    assert rq.gemv_config(1, 4096, 65536, 4, 64, 0)[0] == "decode_mfma"
+    assert rq.gemv_config(1, 4096, 65536, 8, 16, 0)[0] == "smallm_mfma"
+    # FP8 at M = 2 with a row the vector kernel cannot split
+    assert rq.gemv_config(2, 4096, 16384, 8, 0, 2)[0] != "vector"
+    with pytest.raises(rq.RqError):
+        rq.gemv_config(0, 4096, 4096, 4, 64, 0)
+    with pytest.raises(rq.RqError):
+        rq.gemv_config(1, 4096, 4096 + 16, 4, 64, 0)  # not a whole number of groups
+    with pytest.raises(rq.RqError):
+        rq.gemv_config(1, 4096, 4096, 3, 64, 0)
+
+
+def test_gemv_config_shapes_are_valid(L):
+    """Every vector-unit shape the chooser returns splits the row into whole
+    slices of at most the workgroup's waves, and at M = 1 a row of 16-chunk
+    multiples with at least 512 row pairs takes 16 lanes per row."""
+    widths = [(768, 768), (3072, 768), (768, 3072), (2048, 2048), (8192, 2048), (2048, 8192),
+              (2560, 2560), (10240, 2560), (2560, 10240), (4096, 4096), (16384, 4096),
+              (4096, 16384), (65536, 4096), (1000, 4096), (4096, 1024), (17, 256)]
+    fmts = [(4, 64, 0, 32), (8, 16, 0, 16), (4, 32, 1, 32), (8, 0, 2, 16), (4, 128, 0, 32)]
+    for M in (1, 2, 4, 8):
+        for bits, group, layout, kpc in fmts:
+            for N, K in widths:
+                if layout == 1 and K % 256:
+                    continue
+                kern, lpr, cpl, npass = rq.gemv_config(M, N, K, bits, group, layout)
+                if kern != "vector" or lpr == 0:
+                    continue
+                chunks = K // kpc
+                mt = 1 if M == 1 else (2 if M == 2 else (4 if M <= 4 else 8))
+                max_threads = 256 if mt * cpl >= 4 else (512 if mt * cpl >= 2 else 1024)
+                assert lpr in (8, 16, 32, 64) and cpl in (1, 2, 4) and npass in (1, 2, 4, 8)
+                assert chunks % (lpr * cpl) == 0, (M, N, K, bits, lpr, cpl)
+                assert chunks // (lpr * cpl) <= max_threads // 64, (M, N, K, bits, lpr, cpl)
+                if mt >= 4:
+                    assert npass <= 4
+                if M == 1 and chunks % 16 == 0 and chunks // 16 <= 16 and (N + 15) // 16 >= 512:
+                    assert (lpr, cpl) == (16, 1), (N, K, bits)
+
+
+def test_gemv_config_follows_overrides(L, monkeypatch):
+    """RQ_GEMV_KERNEL and RQ_GEMV_NPASS are applied by the query as by rq_gemv."""
+    try:
+        monkeypatch.setenv("RQ_GEMV_KERNEL", "1")
+        rq.tuning_reload()
+        assert rq.gemv_config(32, 4096, 4096, 4, 64, 0)[0] == "vector"
+        monkeypatch.setenv("RQ_GEMV_KERNEL", "3")
+        rq.tuning_reload()
+        assert rq.gemv_config(1, 4096, 4096, 4, 64, 0)[0] == "smallm_mfma"
+        monkeypatch.delenv("RQ_GEMV_KERNEL")
+        monkeypatch.setenv("RQ_GEMV_NPASS", "8")
+        rq.tuning_reload()
+        assert rq.gemv_config(1, 4096, 4096, 4, 64, 0) == ("vector", 16, 1, 8)
+    finally:
+        monkeypatch.delenv("RQ_GEMV_KERNEL", raising=False)
+        monkeypatch.delenv("RQ_GEMV_NPASS", raising=False)
+        rq.tuning_reload()
+    assert rq.gemv_config(1, 4096, 4096, 4, 64, 0) == ("vector", 16, 1, 2)
