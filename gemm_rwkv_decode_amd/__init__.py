@@ -94,6 +94,10 @@ def lib():
             L.rq_probe_barrier.restype = i
             L.rq_probe_mfma.argtypes = [i, i, i, vp, vp]
             L.rq_probe_mfma.restype = i
+            L.rq_probe_valu.argtypes = [i, i, i, vp, vp]
+            L.rq_probe_valu.restype = i
+            L.rq_probe_overlap.argtypes = [i, i, i, i, i, vp, vp]
+            L.rq_probe_overlap.restype = i
             L.rq_tuning_reload.argtypes = []
             L.rq_tuning_reload.restype = i
             ip = ctypes.POINTER(ctypes.c_int)

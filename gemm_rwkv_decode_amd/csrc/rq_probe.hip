@@ -248,6 +248,149 @@ __global__ void __launch_bounds__(256) k_probe_mfma(int iters, int shape, float*
   if (s == 1234.5f) sink[blockIdx.x] = s;  // practically never true; keeps the work live
 }
 
+// Vector-unit issue cost of one instruction kind: every lane runs `iters` x 64
+// instructions of kind OP over eight independent registers.  Inline assembly,
+// so that exactly the named instruction is timed; the values are never used
+// beyond the final fold.
+constexpr int VALU_KINDS = 17;
+template <int OP>
+__global__ void __launch_bounds__(512) k_probe_valu(int iters, unsigned* sink) {
+  const u32 lane = threadIdx.x;
+  u32 a[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) a[i] = lane * 2654435761u + (u32)i * 0x3C003C00u;
+  const u32 b = 0x3BFF3BFFu ^ lane, c = 0x00010001u + lane;
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        if constexpr (OP == 0) asm volatile("v_and_b32 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        if constexpr (OP == 1) asm volatile("v_lshrrev_b32 %0, 3, %0" : "+v"(a[i]));
+        if constexpr (OP == 2) asm volatile("v_perm_b32 %0, %0, %1, %2" : "+v"(a[i]) : "v"(b), "v"(c));
+        if constexpr (OP == 3)
+          asm volatile("v_bitop3_b32 %0, %0, %1, %2 bitop3:0x6c" : "+v"(a[i]) : "v"(b), "v"(c));
+        if constexpr (OP == 4) asm volatile("v_pk_fma_f16 %0, %0, %1, %2" : "+v"(a[i]) : "v"(b), "v"(c));
+        if constexpr (OP == 5) asm volatile("v_pk_add_f16 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        if constexpr (OP == 6) asm volatile("v_dot2c_f32_f16 %0, %1, %2" : "+v"(a[i]) : "v"(b), "v"(c));
+        if constexpr (OP == 7)
+          asm volatile("v_fma_mix_f32 %0, %1, %0, %2 op_sel_hi:[1,0,0]" : "+v"(a[i]) : "v"(b), "v"(c));
+        if constexpr (OP == 8) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(a[i]) : "v"(b), "v"(c));
+        if constexpr (OP == 9) asm volatile("v_cvt_f32_f16 %0, %0" : "+v"(a[i]));
+        if constexpr (OP == 10) asm volatile("v_add_u32 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        if constexpr (OP == 11) asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        if constexpr (OP == 12) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        if constexpr (OP == 13)
+          asm volatile("v_mov_b32_dpp %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(a[i]));
+        if constexpr (OP == 14)
+          asm volatile("v_add_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf"
+                       : "+v"(a[i]));
+        if constexpr (OP == 15) asm volatile("v_lshl_or_b32 %0, %0, 4, %1" : "+v"(a[i]) : "v"(b));
+        if constexpr (OP == 16)
+          asm volatile("v_and_or_b32 %0, %0, %1, %2" : "+v"(a[i]) : "v"(b), "v"(c));
+      }
+  }
+  u32 f = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) f ^= a[i];
+  if (f == 0x12345679u) sink[blockIdx.x] = f;  // practically never true
+}
+
+template <int OP>
+hipError_t launch_valu(int op, int blocks, int iters, unsigned* sink, hipStream_t s) {
+  if constexpr (OP >= VALU_KINDS) {
+    return hipErrorInvalidValue;
+  } else {
+    if (op != OP) return launch_valu<OP + 1>(op, blocks, iters, sink, s);
+    hipLaunchKernelGGL(k_probe_valu<OP>, dim3(blocks), dim3(512), 0, s, iters, sink);
+    return hipGetLastError();
+  }
+}
+
+// Vector work beside the matrix pipe.  Each wave runs `iters` rounds; a round
+// is eight independent v_mfma_f32_16x16x32_f16 and/or PER vector operations
+// per MFMA (KIND 0: binary16 pair FMAs, 1: integer bit operations, 2: binary32
+// FMAs, on eight independent registers).  MODE 0: MFMAs only; 1: vector work
+// only; 2: both in every wave, each MFMA followed by its share of the vector
+// work; 3: the MFMAs in waves 0-3 and the vector work in waves 4-7 of the
+// 512-thread workgroup (which share the four SIMDs when waves are spread over
+// them in turn).
+template <int MODE, int KIND, int PER>
+__global__ void __launch_bounds__(512) k_probe_overlap(int iters, float* sink) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const h8 a = (h8)(_Float16)(0.001f * lane), b = (h8)(_Float16)(0.002f * lane);
+  f4 c[8];
+  h2v v[8];
+  u32 u[8];
+  float w[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    c[i] = f4{0, 0, 0, 0};
+    v[i] = h2v{(_Float16)(0.5f + lane * 1e-3f * i), (_Float16)0.25f};
+    u[i] = (u32)lane * 2654435761u + (u32)i;
+    w[i] = 0.5f + lane * 1e-3f * i;
+  }
+  const h2v m = {(_Float16)0.999f, (_Float16)0.999f}, ad = {(_Float16)0.001f, (_Float16)0.001f};
+  const bool do_m = MODE == 0 || MODE == 2 || (MODE == 3 && wave < 4);
+  const bool do_v = MODE == 1 || MODE == 2 || (MODE == 3 && wave >= 4);
+  auto vop = [&](int j) {
+    if constexpr (KIND == 0) v[j & 7] = __builtin_elementwise_fma(v[j & 7], m, ad);
+    else if constexpr (KIND == 1) u[j & 7] = ((u[j & 7] & 0x0F0F0F0Fu) ^ 0x64646464u) | (u[j & 7] >> 3);
+    else w[j & 7] = __builtin_fmaf(w[j & 7], 0.999f, 0.001f);
+  };
+  for (int it = 0; it < iters; it++) {
+    if (do_m && do_v) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        c[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[i], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < PER; j++) vop(j);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);  // then vector work
+      }
+    } else if (do_m) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) c[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[i], 0, 0, 0);
+    } else if (do_v) {
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j = 0; j < PER; j++) vop(j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) s += c[i][0] + c[i][3] + (float)v[i][0] + (float)(u[i] & 7u) + w[i];
+  if (s == 1234.5f) sink[blockIdx.x] = s;  // practically never true
+}
+
+template <int MODE, int KIND>
+hipError_t launch_overlap_k(int per, int blocks, int iters, float* sink, hipStream_t s) {
+  switch (per) {
+    case 4: hipLaunchKernelGGL((k_probe_overlap<MODE, KIND, 4>), dim3(blocks), dim3(512), 0, s, iters, sink); break;
+    case 8: hipLaunchKernelGGL((k_probe_overlap<MODE, KIND, 8>), dim3(blocks), dim3(512), 0, s, iters, sink); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+template <int MODE>
+hipError_t launch_overlap_m(int kind, int per, int blocks, int iters, float* sink, hipStream_t s) {
+  switch (kind) {
+    case 0: return launch_overlap_k<MODE, 0>(per, blocks, iters, sink, s);
+    case 1: return launch_overlap_k<MODE, 1>(per, blocks, iters, sink, s);
+    case 2: return launch_overlap_k<MODE, 2>(per, blocks, iters, sink, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 bool ok16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -315,6 +458,31 @@ int rq_probe_mfma(int blocks, int iters, int shape, float* sink, void* stream) {
   hipLaunchKernelGGL(k_probe_mfma, dim3(blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), iters, shape, sink);
   return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
+}
+
+int rq_probe_valu(int op, int blocks, int iters, unsigned* sink, void* stream) {
+  if (!sink) return RQ_ERR_NULL;
+  if (op < 0 || op >= VALU_KINDS || blocks < 1 || iters < 1) return RQ_ERR_SHAPE;
+  return launch_valu<0>(op, blocks, iters, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? RQ_OK
+             : RQ_ERR_LAUNCH;
+}
+
+int rq_probe_overlap(int mode, int kind, int per, int blocks, int iters, float* sink,
+                     void* stream) {
+  if (!sink) return RQ_ERR_NULL;
+  if (mode < 0 || mode > 3 || kind < 0 || kind > 2 || (per != 4 && per != 8) || blocks < 1 ||
+      iters < 1)
+    return RQ_ERR_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (mode) {
+    case 0: e = launch_overlap_m<0>(kind, per, blocks, iters, sink, s); break;
+    case 1: e = launch_overlap_m<1>(kind, per, blocks, iters, sink, s); break;
+    case 2: e = launch_overlap_m<2>(kind, per, blocks, iters, sink, s); break;
+    default: e = launch_overlap_m<3>(kind, per, blocks, iters, sink, s); break;
+  }
+  return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 
 int rq_probe_empty(void* stream) {

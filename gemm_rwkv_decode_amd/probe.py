@@ -13,6 +13,11 @@ workgroup after a __threadfence() against after device-scope coherent writes,
 per launch of 256..2048 workgroups) and the latency of one grid-wide barrier
 among co-resident workgroups, both ways, with the exchanged data checked.
 --mfma adds "mfma": the dense fp16 matrix-core rate (v_mfma_f32_16x16x32_f16).
+--valu adds "valu": the issue cost, in cycles at 2.4 GHz per wave instruction,
+of each vector instruction kind the product kernels use.
+--overlap adds "overlap": the duration of matrix-core work alone, vector work
+alone, both interleaved in every wave, and both in separate waves of a
+workgroup, per SIMD and MFMA slot.
 """
 import argparse
 import json
@@ -185,6 +190,57 @@ def mfma_probe(blocks=2048, iters=2000):
     return out
 
 
+VALU_KINDS = ("v_and_b32", "v_lshrrev_b32", "v_perm_b32", "v_bitop3_b32", "v_pk_fma_f16",
+              "v_pk_add_f16", "v_dot2c_f32_f16", "v_fma_mix_f32", "v_fma_f32", "v_cvt_f32_f16",
+              "v_add_u32", "v_add_f32", "v_mul_f32", "v_mov_b32_dpp", "v_add_f32_dpp",
+              "v_lshl_or_b32", "v_and_or_b32")
+CLOCK_HZ = 2.4e9
+
+
+def valu_probe(blocks=512, iters=1000):
+    """Cycles (at 2.4 GHz) per wave instruction of each kind, 512-thread
+    workgroups, two per CU (four waves per SIMD)."""
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    waves_per_simd = blocks // 256 * 2
+    out = {"blocks": blocks, "threads": 512, "waves_per_simd": waves_per_simd,
+           "clock_hz": CLOCK_HZ, "cycles": {}}
+    for op, name in enumerate(VALU_KINDS):
+        fn = lambda i, op=op: L.rq_probe_valu(op, blocks, iters, sink.data_ptr(), stream)  # noqa: E731
+        if fn(0) != 0:
+            raise RuntimeError(f"rq_probe_valu({op}) failed")
+        t = min(_time_launches(fn, 3) for _ in range(3))
+        out["cycles"][name] = round(t * CLOCK_HZ / (iters * 64 * waves_per_simd), 2)
+    return out
+
+
+def overlap_probe(iters=2000):
+    """Cycles (at 2.4 GHz) per SIMD and MFMA slot for matrix-core work alone
+    (mode 0), vector work alone (1), both in every wave (2) and both in
+    separate waves (3), for three kinds of vector work and 4 or 8 vector
+    operations per MFMA, at two and four waves per SIMD."""
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for blocks in (256, 512):
+        sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+        wps = blocks // 256 * 2
+        for kind, kname in enumerate(("pk_fma_f16", "bit_ops", "fma_f32")):
+            for per in (4, 8):
+                row = {"waves_per_simd": wps, "vector_kind": kname, "vector_per_mfma": per}
+                for mode, mname in enumerate(("mfma_only", "vector_only", "same_wave",
+                                              "separate_waves")):
+                    fn = lambda i, mode=mode: L.rq_probe_overlap(  # noqa: E731
+                        mode, kind, per, blocks, iters, sink.data_ptr(), stream)
+                    if fn(0) != 0:
+                        raise RuntimeError("rq_probe_overlap failed")
+                    t = min(_time_launches(fn, 2) for _ in range(3))
+                    row[mname] = round(t * CLOCK_HZ / (iters * 8 * wps), 1)
+                rows.append(row)
+    return {"threads": 512, "clock_hz": CLOCK_HZ, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--sizes", type=str, default=None,
@@ -192,6 +248,8 @@ def main():
     ap.add_argument("--sync", action="store_true")
     ap.add_argument("--mfma", action="store_true")
     ap.add_argument("--no-read", action="store_true")
+    ap.add_argument("--valu", action="store_true")
+    ap.add_argument("--overlap", action="store_true")
     a = ap.parse_args()
     kw = {}
     if a.sizes:
@@ -202,6 +260,10 @@ def main():
         r["mfma"] = mfma_probe()
     if a.sync:
         r["sync"] = sync_probe()
+    if a.valu:
+        r["valu"] = valu_probe()
+    if a.overlap:
+        r["overlap"] = overlap_probe()
     r["seconds"] = time.time() - t
     print(json.dumps(r), flush=True)
 

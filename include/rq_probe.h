@@ -63,6 +63,27 @@ int rq_probe_barrier(unsigned* flags, int mode, int blocks, int rounds, int spin
  * written). */
 int rq_probe_mfma(int blocks, int iters, int shape, float* sink, void* stream);
 
+/* Vector-unit issue cost of one instruction kind: `blocks` workgroups of 512
+ * threads, every lane running `iters` x 64 instructions of kind `op` over
+ * eight independent registers.  Kinds: 0 v_and_b32, 1 v_lshrrev_b32,
+ * 2 v_perm_b32, 3 v_bitop3_b32, 4 v_pk_fma_f16, 5 v_pk_add_f16,
+ * 6 v_dot2c_f32_f16, 7 v_fma_mix_f32, 8 v_fma_f32, 9 v_cvt_f32_f16,
+ * 10 v_add_u32, 11 v_add_f32, 12 v_mul_f32, 13 v_mov_b32 with a DPP row
+ * shift, 14 v_add_f32 with a DPP row shift, 15 v_lshl_or_b32,
+ * 16 v_and_or_b32.  sink: `blocks` entries (practically never written). */
+int rq_probe_valu(int op, int blocks, int iters, unsigned* sink, void* stream);
+
+/* Vector work beside the matrix pipe: every wave of `blocks` 512-thread
+ * workgroups runs `iters` rounds of eight independent
+ * v_mfma_f32_16x16x32_f16 and/or `per` (4 or 8) vector operations per MFMA
+ * of kind `kind` (0 binary16 pair FMAs, 1 integer bit operations, 2 binary32
+ * FMAs).  mode 0: MFMAs only; 1: vector work only; 2: both in every wave,
+ * each MFMA followed by its share; 3: MFMAs in waves 0-3, vector work in
+ * waves 4-7 of each workgroup.  Comparing the four durations shows whether
+ * the two kinds of work overlap in time.  sink: `blocks` floats. */
+int rq_probe_overlap(int mode, int kind, int per, int blocks, int iters, float* sink,
+                     void* stream);
+
 /* Re-read the launch-shape override variables (RQ_GEMV_LPR, RQ_GEMV_CPL,
  * RQ_GEMV_NPASS, RQ_GEMM_PLAN (1-based index of a workgroup arrangement of
  * the matrix-core kernel), RQ_GEMM_SPLITS, RQ_GEMV_KERNEL (the kernel of

@@ -329,3 +329,21 @@ def test_gemv_config_follows_overrides(L, monkeypatch):
         monkeypatch.delenv("RQ_GEMV_NPASS", raising=False)
         rq.tuning_reload()
     assert rq.gemv_config(1, 4096, 4096, 4, 64, 0) == ("vector", 16, 1, 2)
+
+
+def test_probe_arguments_checked_on_the_host(L):
+    """The measurement kernels of rq_probe.h reject bad arguments before any
+    HIP call."""
+    sink = ctypes.c_void_p(A)
+    assert L.rq_probe_valu(17, 1, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_valu(-1, 1, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_valu(0, 0, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_valu(0, 1, 1, None, None) == header_enum("RQ_ERR_NULL")
+    assert L.rq_probe_overlap(4, 0, 4, 1, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_overlap(0, 3, 4, 1, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_overlap(0, 0, 5, 1, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_overlap(0, 0, 4, 1, 0, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_overlap(0, 0, 4, 1, 1, None, None) == header_enum("RQ_ERR_NULL")
+    assert L.rq_probe_mfma(1, 1, 2, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_barrier(sink, 1, 1, 1, 1, sink, None) == header_enum("RQ_ERR_SHAPE")
+    assert L.rq_probe_copy(sink, ctypes.c_void_p(A + 16), 32, None) == header_enum("RQ_ERR_ALIAS")
