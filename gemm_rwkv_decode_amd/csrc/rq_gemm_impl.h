@@ -562,6 +562,10 @@ __device__ __forceinline__ void mm_chunk(const char* __restrict__ xsl,
         const int j = j0 + g;  // group within the round
         const u32 pair = reinterpret_cast<const u32*>(sl + S::S_OFF)[n * S::SRD + j / 2];
         sc = (j & 1) ? half_hi(pair) : half_lo(pair);
+        // converted once here: the compiler would otherwise fold the conversion
+        // into each of the MT*4 FMAs below as v_fma_mix_f32, which issues at half
+        // the rate of v_fma_f32 (same result: the conversion is exact)
+        asm volatile("" : "+v"(sc));
       }
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
