@@ -93,3 +93,52 @@ def test_random_shape(seed):
     T.assert_close(y1, yr, b, f"batched {f.tag} M={M} {N}x{K}")
     yr2, b2 = T.oracle_y(p2, x2)
     T.assert_close(y2, yr2, b2, f"batched {f.tag} M={M} {N2}x{K2}")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_dequant(seed):
+    """rq_dequant at random shapes: binary32 values and int8 codes bit-exact."""
+    rng = np.random.default_rng(3000 + seed)
+    f, _, N, K = draw(rng, 1)
+    T.say(f"random dequant {seed}: {f.tag} N={N} K={K}")
+    p = T.to_dev(S.gen_matrix(f"rdq{seed}", 0, 0, N, K, f))
+    w = T.dequant(p).cpu().numpy()
+    ref = T.oracle_dequant(p)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32)), (f.tag, N, K)
+    if f.layout != S.LAYOUT_FP8_TENSOR:
+        c = T.dequant(p, rq.RQ_OUT_CODES_I8).cpu().numpy()
+        assert np.array_equal(c, T.oracle_codes(p)), (f.tag, N, K)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_forced_kernel_and_plan(seed, monkeypatch):
+    """rq_gemv with its kernel forced (vector units, matrix-core decode,
+    small-batch matrix cores; each falls back where it cannot take the shape),
+    and rq_gemm_smallm with a random plan and split count (ignored where they
+    do not fit), at random shapes."""
+    rng = np.random.default_rng(4000 + seed)
+    f, M, N, K = draw(rng)
+    p = T.to_dev(S.gen_matrix(f"rfk{seed}", 0, 0, N, K, f))
+    x = x_of(M, K, 9000 + seed)
+    yr, b = T.oracle_y(p, x)
+    try:
+        for kern in (1, 2, 3):
+            monkeypatch.setenv("RQ_GEMV_KERNEL", str(kern))
+            rq.tuning_reload()
+            T.say(f"random forced {seed}: {f.tag} M={M} N={N} K={K} kernel {kern} "
+                  f"-> {rq.gemv_config(M, N, K, f.bits, f.group, f.layout)}")
+            y = T.run("gemv", p, x)
+            T.assert_close(y, yr, b, f"forced kernel {kern} {f.tag} M={M} {N}x{K}")
+        monkeypatch.delenv("RQ_GEMV_KERNEL")
+        plan, splits = int(rng.integers(1, 28)), int(rng.choice([1, 2, 3, 4, 8]))
+        monkeypatch.setenv("RQ_GEMM_PLAN", str(plan))
+        monkeypatch.setenv("RQ_GEMM_SPLITS", str(splits))
+        rq.tuning_reload()
+        T.say(f"random plan {seed}: {f.tag} M={M} N={N} K={K} asked p{plan}s{splits} -> "
+              f"{rq.gemm_config(M, N, K, f.bits, f.group, f.layout)}")
+        y = T.run("gemm", p, x)
+        T.assert_close(y, yr, b, f"plan {plan} splits {splits} {f.tag} M={M} {N}x{K}")
+    finally:
+        for v in ("RQ_GEMV_KERNEL", "RQ_GEMM_PLAN", "RQ_GEMM_SPLITS"):
+            monkeypatch.delenv(v, raising=False)
+        rq.tuning_reload()
