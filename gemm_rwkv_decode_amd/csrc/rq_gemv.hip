@@ -505,6 +505,31 @@ GemvCfg choose_gemv(int fmt, int M, int N, int K) {
   // 9.8 us)
   if (c.mt == 1 && c.npass == 4 && (N + (64 / c.lpr) * 2 - 1) / ((64 / c.lpr) * 2) <= 640)
     c.npass = 2;
+  // Measured at M = 1 (weights cold, interleaved repeats): the heavier codes
+  // of these RWKV-7 shapes run faster in workgroups of at most 8 waves than
+  // in the 16-wave ones the rules above give -- 5-bit 4096x16384 13.65 ->
+  // 11.70 us, 6-bit 14.57 -> 12.42, 5-bit 2560x10240 7.15 -> 6.78 (64 lanes
+  // per row), FP8 16384x4096 14.12 -> 11.48 us, FP8 4096x4096 4.66 -> 4.56
+  // (two 16-code chunks per lane, the codes per lane of one 4-bit chunk).
+  struct Tuned {
+    int fmt, N, K, lpr, cpl, npass;
+  };
+  static const Tuned tuned[] = {
+      {FMT_A5, 4096, 16384, 64, 1, 4}, {FMT_A6, 4096, 16384, 64, 1, 4},
+      {FMT_A5, 2560, 10240, 64, 1, 4}, {FMT_F8, 16384, 4096, 16, 2, 2},
+      {FMT_F8, 4096, 4096, 16, 2, 2},
+  };
+  if (c.mt == 1) {
+    for (const Tuned& t : tuned) {
+      if (t.fmt == fmt && t.N == N && t.K == K && chunks % (t.lpr * t.cpl) == 0 &&
+          chunks / (t.lpr * t.cpl) <= gemv_max_threads(1, t.cpl) / 64) {
+        c.lpr = t.lpr;
+        c.cpl = t.cpl;
+        c.npass = t.npass;
+        break;
+      }
+    }
+  }
   if (forced > 0) {  // tuning: RQ_GEMV_LPR / RQ_GEMV_CPL / RQ_GEMV_NPASS
     const int cpl = tu.gemv_cpl ? tu.gemv_cpl : c.cpl;
     if (chunks % (forced * cpl) == 0 &&

@@ -258,6 +258,13 @@ GEMV_SHAPES_M1 = [
     ((2560, 10240, 4, 32, 1), (32, 1, 2)),
     ((768, 768, 4, 64, 0), (8, 1, 1)),
     ((3072, 768, 4, 64, 0), (8, 1, 1)),
+    # heavier codes: at most 8 waves per workgroup
+    ((4096, 16384, 5, 32, 1), (64, 1, 4)),
+    ((4096, 16384, 6, 32, 1), (64, 1, 4)),
+    ((2560, 10240, 5, 32, 1), (64, 1, 4)),
+    ((16384, 4096, 8, 0, 2), (16, 2, 2)),
+    ((4096, 4096, 8, 0, 2), (16, 2, 2)),
+    ((4096, 16384, 8, 0, 2), (64, 1, 4)),
 ]
 
 
@@ -315,7 +322,9 @@ def test_gemv_config_shapes_are_valid(L):
                 assert chunks // (lpr * cpl) <= max_threads // 64, (M, N, K, bits, lpr, cpl)
                 if mt >= 4:
                     assert npass <= 4
-                if M == 1 and chunks % 16 == 0 and chunks // 16 <= 16 and (N + 15) // 16 >= 512:
+                tuned = [sh for sh, _ in GEMV_SHAPES_M1 if sh[2] in (5, 6) or sh[4] == 2]
+                if (M == 1 and chunks % 16 == 0 and chunks // 16 <= 16 and
+                        (N + 15) // 16 >= 512 and (N, K, bits, group, layout) not in tuned):
                     assert (lpr, cpl) == (16, 1), (N, K, bits)
 
 

@@ -249,6 +249,29 @@ def test_kernel_choice_long_rows(f, K, M):
     T.assert_close(yb, yr, b, f"rq_gemv_batched {f.tag} K={K} M={M}")
 
 
+@pytest.mark.parametrize("f,N,K,M,kernel", [
+    # measured vector-unit launch shapes of heavier codes at M = 1
+    (S.ASYM5_G32, 4096, 16384, 1, ("vector", 64, 1, 4)),
+    (S.ASYM6_G32, 4096, 16384, 1, ("vector", 64, 1, 4)),
+    (S.ASYM5_G32, 2560, 10240, 1, ("vector", 64, 1, 4)),
+    (S.FP8_E4M3, 16384, 4096, 1, ("vector", 16, 2, 2)),
+    (S.FP8_E4M3, 4096, 4096, 1, ("vector", 16, 2, 2)),
+    # measured decode-kernel shapes at M = 3..4
+    (S.INT4_G64, 2048, 8192, 4, ("decode_mfma", 0, 0, 0)),
+    (S.ASYM4_G32, 10240, 2560, 3, ("decode_mfma", 0, 0, 0)),
+], ids=lambda v: getattr(v, "tag", str(v)))
+def test_tuned_shapes(f, N, K, M, kernel):
+    """The RWKV-7 shapes with a measured kernel or launch shape of their own
+    take it, and match the oracle at full size."""
+    assert rq.gemv_config(M, N, K, f.bits, f.group, f.layout) == kernel
+    p = small(f, N, K, tag=11)
+    x = x_for(M, K, seed=N + K + M)
+    yr, b = T.oracle_y(p, x)
+    T.say(f"tuned shape {f.tag} {N}x{K} M={M} {kernel}")
+    y = T.run("gemv", p, x)
+    T.assert_close(y, yr, b, f"rq_gemv {f.tag} {N}x{K} M={M}")
+
+
 def test_matrix_decode_kernel_falls_back(tune):
     """Forcing the matrix-core decode kernel where K holds fewer than eight
     chunks leaves the vector-unit kernel in charge (still correct)."""
