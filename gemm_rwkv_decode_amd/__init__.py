@@ -24,14 +24,16 @@ __all__ = [
     "RQ_OK", "RQ_LAYOUT_SYM", "RQ_LAYOUT_ASYM_SB", "RQ_LAYOUT_FP8_TENSOR", "RQ_OUT_F32",
     "RQ_OUT_CODES_I8",
     "RQ_MAX_M", "RQ_MAX_BATCH", "RqError", "RqLibraryMissing", "rq_dequant", "rq_gemv",
-    "rq_gemv_batched", "rq_gemm_smallm", "rq_gemm_smallm_noalloc", "rq_status_string",
-    "rq_version", "prepare", "lib", "LIB_PATH",
+    "rq_gemv_batched", "rq_gemm_smallm", "rq_gemm_smallm_ws", "rq_gemm_smallm_workspace_size",
+    "rq_gemm_smallm_noalloc", "rq_status_string", "rq_version", "prepare", "gemm_workspace",
+    "lib", "LIB_PATH",
 ]
 
 RQ_OK = 0
 RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED, RQ_ERR_ALIGN = 1, 2, 3, 4
 RQ_ERR_LAUNCH, RQ_ERR_ALIAS, RQ_ERR_DEVICE, RQ_ERR_SCRATCH = 5, 6, 7, 8
 RQ_NOALLOC_SCRATCH_BYTES = (8 << 20) + (64 << 10)
+RQ_GEMM_WORKSPACE_MAX_BYTES = 64 << 20
 RQ_LAYOUT_SYM, RQ_LAYOUT_ASYM_SB, RQ_LAYOUT_FP8_TENSOR = 0, 1, 2
 RQ_OUT_F32, RQ_OUT_CODES_I8 = 0, 1
 RQ_MAX_M = 64
@@ -75,6 +77,12 @@ def lib():
                 f = getattr(L, name)
                 f.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
                 f.restype = i
+            L.rq_gemm_smallm_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp,
+                                            ctypes.c_size_t, vp]
+            L.rq_gemm_smallm_ws.restype = i
+            L.rq_gemm_smallm_workspace_size.argtypes = [i, i, i, i, i, i,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+            L.rq_gemm_smallm_workspace_size.restype = i
             L.rq_gemv_batched.argtypes = [ctypes.POINTER(RqProblem), i, i, i, i, i, vp]
             L.rq_gemv_batched.restype = i
             L.rq_status_string.argtypes = [i]
@@ -158,15 +166,92 @@ def rq_gemv(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, stream=N
     return y
 
 
+# Sentinel: the binding's own split-K workspace for the call's stream.
+AUTO = "auto"
+_workspaces = {}  # (device index, stream handle) -> int32 tensor
+
+
+def gemm_workspace(stream=None, device=None):
+    """The binding's split-K workspace for one stream: a torch tensor of
+    RQ_GEMM_WORKSPACE_MAX_BYTES whose arrival counters are zeroed on that
+    stream, made by the first call on the stream and kept for the process (the
+    library never allocates; PyTorch owns this memory).  None while that
+    stream is being captured into a graph and has no workspace yet: the call
+    then keeps K whole."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    dev = torch.device(dev)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    if stream is None:
+        h = int(torch.cuda.current_stream(dev).cuda_stream)
+    else:
+        h = int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    key = (dev.index, h)
+    with _lock:
+        ws = _workspaces.get(key)
+        if ws is not None:
+            return ws
+        if torch.cuda.is_current_stream_capturing():
+            return None
+        cur = torch.cuda.current_stream(dev)
+        st = cur if int(cur.cuda_stream) == h else torch.cuda.ExternalStream(h, device=dev)
+        with torch.cuda.device(dev), torch.cuda.stream(st):
+            ws = torch.zeros(RQ_GEMM_WORKSPACE_MAX_BYTES // 4, dtype=torch.int32, device=dev)
+        _workspaces[key] = ws
+        return ws
+
+
+def _ws_args(workspace, stream, like):
+    """(pointer, bytes) of a workspace argument: AUTO, None or a tensor."""
+    if isinstance(workspace, str) and workspace == AUTO:
+        workspace = gemm_workspace(stream, like.device)
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def rq_gemm_smallm(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
-                   stream=None):
-    """Same product on the matrix cores (tuned for 16 <= M <= 64)."""
-    st = lib().rq_gemm_smallm(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
-                              int(M), int(N), int(K), int(bits), int(group), int(layout),
-                              _stream(stream, qweight))
+                   stream=None, workspace=AUTO):
+    """Same product on the matrix cores (tuned for 16 <= M <= 64).
+
+    ``workspace``: AUTO (default) passes the binding's workspace for the
+    stream to rq_gemm_smallm_ws, so K may be split; a tensor passes that one;
+    None calls rq_gemm_smallm, which keeps K whole."""
+    if workspace is None:
+        st = lib().rq_gemm_smallm(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                                  int(M), int(N), int(K), int(bits), int(group), int(layout),
+                                  _stream(stream, qweight))
+        if st != RQ_OK:
+            raise RqError("rq_gemm_smallm", st)
+        return y
+    return rq_gemm_smallm_ws(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
+                             workspace, stream=stream)
+
+
+def rq_gemm_smallm_ws(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, workspace,
+                      stream=None):
+    """rq_gemm_smallm with a caller-owned workspace (a tensor whose first 64 KiB
+    are zero before first use, or AUTO, or None to keep K whole)."""
+    L = lib()
+    ptrs = (_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y))
+    wp, wb = _ws_args(workspace, stream, qweight)
+    st = L.rq_gemm_smallm_ws(*ptrs, int(M), int(N), int(K), int(bits), int(group), int(layout),
+                             wp, wb, _stream(stream, qweight))
     if st != RQ_OK:
-        raise RqError("rq_gemm_smallm", st)
+        raise RqError("rq_gemm_smallm_ws", st)
     return y
+
+
+def rq_gemm_smallm_workspace_size(M, N, K, bits, group, layout):
+    """Bytes of workspace rq_gemm_smallm_ws uses for one product (0: K kept
+    whole).  Host-only."""
+    b = ctypes.c_size_t(0)
+    st = lib().rq_gemm_smallm_workspace_size(int(M), int(N), int(K), int(bits), int(group),
+                                             int(layout), ctypes.byref(b))
+    if st != RQ_OK:
+        raise RqError("rq_gemm_smallm_workspace_size", st)
+    return b.value
 
 
 def rq_gemm_smallm_noalloc(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
@@ -200,13 +285,17 @@ def rq_gemv_batched(problems, M, bits, group, layout, stream=None):
         raise RqError("rq_gemv_batched", st)
 
 
-def prepare(name, *args, stream=None):
+def prepare(name, *args, stream=None, workspace=AUTO):
     """Resolve the tensor arguments of one call now and return a callable that
     repeats it with no per-call argument conversion in Python (for step loops
     and graph capture).  ``name`` is "rq_gemv", "rq_gemm_smallm",
-    "rq_gemv_batched" or "rq_dequant"; ``args`` are those of the Python
-    function of that name, without ``stream``.  The tensors must stay alive."""
+    "rq_gemm_smallm_noalloc", "rq_gemv_batched" or "rq_dequant"; ``args`` are
+    those of the Python function of that name, without ``stream`` (and
+    ``workspace``, which rq_gemm_smallm takes as a keyword, resolved now).
+    The tensors must stay alive."""
     L = lib()
+    if name == "rq_gemm_smallm" and workspace is not None:
+        name = "rq_gemm_smallm_ws"
     f = getattr(L, name)
     if name == "rq_gemv_batched":
         problems, M, bits, group, layout = args
@@ -218,9 +307,13 @@ def prepare(name, *args, stream=None):
         cargs = (_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out), int(N), int(K),
                  int(bits), int(group), int(layout), int(out_kind), _stream(stream, qweight))
     else:
-        qweight, scales, zeros, x, y, M, N, K, bits, group, layout = args
+        qweight, scales, zeros, x, y, M, N, K, bits, group, layout = args[:11]
         cargs = (_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y), int(M), int(N),
-                 int(K), int(bits), int(group), int(layout), _stream(stream, qweight))
+                 int(K), int(bits), int(group), int(layout))
+        if name == "rq_gemm_smallm_ws":
+            ws = args[11] if len(args) > 11 else workspace
+            cargs += _ws_args(ws, stream, qweight)
+        cargs += (_stream(stream, qweight),)
 
     def call():
         st = f(*cargs)

@@ -150,40 +150,6 @@ rq_status check_device(int* dev_out) {
   return RQ_OK;
 }
 
-// Split-K workspace: one per (device, stream), allocated by the first call on
-// that stream that splits K, at the largest size the chooser ever asks for
-// (rq::GEMM_WS_MAX_BYTES), and kept until the process ends: never regrown,
-// freed or reused for another stream, so no later call allocates or waits.
-// Calls on one stream are ordered, so they may share it.
-float* stream_workspace(int dev, hipStream_t stream) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, float*> cache;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(std::make_pair(dev, stream));
-  if (it != cache.end()) return it->second;
-  // hipMalloc is not a stream operation, but a stream under capture is left
-  // alone all the same: the caller then gets K kept whole
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (stream && hipStreamIsCapturing(stream, &cs) == hipSuccess &&
-      cs != hipStreamCaptureStatusNone)
-    return nullptr;
-  float* p = nullptr;
-  if (hipMalloc(&p, rq::GEMM_WS_MAX_BYTES) != hipSuccess) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  // the split-K arrival counters start at zero (each launch leaves them so);
-  // cleared on the caller's stream, ahead of the launch that will use them
-  // (the stream is not capturing here, so no graph records this memset)
-  if (hipMemsetAsync(p, 0, rq::SPLIT_COUNTERS * sizeof(unsigned), stream) != hipSuccess) {
-    (void)hipGetLastError();
-    (void)hipFree(p);
-    return nullptr;
-  }
-  cache[std::make_pair(dev, stream)] = p;
-  return p;
-}
-
 // Split-K scratch of rq_gemm_smallm_noalloc: a fixed device array (each GPU
 // the library runs on holds its own copy until the process ends), so that
 // entry point never allocates.  It holds the split-K arrival counters (zero
@@ -408,30 +374,75 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
   return RQ_OK;
 }
 
+// The arrangement rq_gemm_smallm_ws would launch and the workspace bytes it
+// needs (0 when K is kept whole).
+rq::GemmCfg smallm_cfg(int fmt, int M, int N, int K, int group, size_t* need) {
+  const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
+  *need = rq::gemm_workspace_floats(c, M, N) * sizeof(float);
+  return c;
+}
+
 rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* zeros,
                          const void* x, float* y, int M, int N, int K, int bits,
                          int group, int layout, void* stream) {
+  // no workspace: K kept whole
+  return rq_gemm_smallm_ws(qweight, scales, zeros, x, y, M, N, K, bits, group, layout,
+                           nullptr, 0, stream);
+}
+
+rq_status rq_gemm_smallm_workspace_size(int M, int N, int K, int bits, int group, int layout,
+                                        size_t* bytes) {
+  if (!bytes) return RQ_ERR_NULL;
+  *bytes = 0;
+  const int fmt = format_of(layout, bits, group);
+  if (fmt < 0) return RQ_ERR_UNSUPPORTED;
+  if (M < 1 || M > RQ_MAX_M || check_shape(N, K, bits, group, layout) != RQ_OK)
+    return RQ_ERR_SHAPE;
+  if (rq::gemm_supports(fmt, M, K, group)) smallm_cfg(fmt, M, N, K, group, bytes);
+  return RQ_OK;
+}
+
+rq_status rq_gemm_smallm_ws(const void* qweight, const void* scales, const void* zeros,
+                            const void* x, float* y, int M, int N, int K, int bits,
+                            int group, int layout, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   int fmt = -1;
   rq_status st =
       check_product(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, &fmt);
   if (st != RQ_OK) return st;
+  const bool has_ws = workspace != nullptr;
+  if (has_ws) {
+    if (!aligned16(workspace)) return RQ_ERR_ALIGN;
+    // the workspace against every input and the output
+    st = check_output(static_cast<const float*>(workspace), workspace_bytes, qweight, scales,
+                      zeros, x, N, K, bits, group, layout, M);
+    if (st != RQ_OK) return st;
+    if (overlaps(range_of(workspace, workspace_bytes), range_of(y, (size_t)M * N * 4)))
+      return RQ_ERR_ALIAS;
+  }
+  // host-only choice first, so a too-small workspace enqueues nothing
+  const bool mfma = rq::gemm_supports(fmt, M, K, group);
+  size_t need = 0;
+  rq::GemmCfg c{};
+  if (mfma) c = smallm_cfg(fmt, M, N, K, group, &need);
+  float* ws = nullptr;
+  if (need > 0) {
+    if (!has_ws) {
+      c = rq::choose_gemm(fmt, M, N, K, group, 0, false);  // K kept whole
+    } else {
+      if (workspace_bytes < need) return RQ_ERR_SCRATCH;
+      ws = static_cast<float*>(workspace);
+    }
+  }
   int dev;
   st = check_device(&dev);
   if (st != RQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   rq::Problem p{qweight, scales, zeros, x, y, M, N, K, group, fmt};
-  if (!rq::gemm_supports(fmt, M, K, group)) {
+  if (!mfma) {
     // K is not a whole number of the matrix-core kernel's chunks
-    const rq::GemvCfg c = rq::choose_gemv(fmt, M, N, K);
-    return rq::launch_gemv(p, c, s) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
-  }
-  rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
-  float* ws = nullptr;
-  if (c.splits > 1) {
-    ws = stream_workspace(dev, s);
-    // no workspace (first split call made under graph capture, or out of
-    // memory): keep K whole
-    if (!ws) c = rq::choose_gemm(fmt, M, N, K, group, 0, false);
+    const rq::GemvCfg gc = rq::choose_gemv(fmt, M, N, K);
+    return rq::launch_gemv(p, gc, s) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
   }
   const hipError_t e = rq::launch_gemm(p, c, ws, s);
   return e == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
@@ -453,7 +464,7 @@ rq_status rq_gemm_smallm_noalloc(const void* qweight, const void* scales, const 
     const rq::GemvCfg c = rq::choose_gemv(fmt, M, N, K);
     return rq::launch_gemv(p, c, s) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
   }
-  // the same arrangement rq_gemm_smallm chooses, partial sums in `scratch`
+  // the arrangement rq_gemm_smallm_ws chooses, partial sums in `scratch`
   const rq::GemmCfg c = rq::choose_gemm(fmt, M, N, K, group);
   float* ws = nullptr;
   if (c.splits > 1) {
@@ -476,12 +487,12 @@ const char* rq_status_string(int status) {
     case RQ_ERR_LAUNCH: return "the kernel launch failed";
     case RQ_ERR_ALIAS: return "an output overlaps an input";
     case RQ_ERR_DEVICE: return "no usable gfx950 device";
-    case RQ_ERR_SCRATCH: return "the call needs more scratch than the fixed device array holds";
+    case RQ_ERR_SCRATCH: return "the call needs more scratch or workspace than it was given";
     default: return "unknown status";
   }
 }
 
-int rq_version(void) { return (1 << 16) | 0; }
+int rq_version(void) { return (1 << 16) | 1; }
 
 int rq_gemm_config(int M, int N, int K, int bits, int group, int layout, int allow_split,
                    int* plan, int* splits) {

@@ -61,8 +61,10 @@
  *
  * Pointers.  Every pointer is device memory owned by the caller and must be
  * 16-byte aligned.  Each operand (packed codes, scales, x, y) must be smaller
- * than 2 GiB (RQ_ERR_SHAPE otherwise).  The library does not free or retain
- * caller memory, never copies to the host and never synchronizes: work is
+ * than 2 GiB (RQ_ERR_SHAPE otherwise).  The library never allocates or frees
+ * device memory, does not retain caller memory between calls (a workspace
+ * is passed in: rq_gemm_smallm_ws), never copies to the host and never
+ * synchronizes: work is
  * enqueued on `stream`
  * (a hipStream_t; NULL means the null stream) and the call returns after the
  * enqueue.  Outputs must not overlap any input.
@@ -75,6 +77,8 @@
  */
 #ifndef RQ_H
 #define RQ_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -89,8 +93,9 @@ typedef enum {
     RQ_ERR_LAUNCH = 5,      /* the kernel launch was rejected by the runtime    */
     RQ_ERR_ALIAS = 6,       /* an output range overlaps an input range          */
     RQ_ERR_DEVICE = 7,      /* no usable gfx950 device                           */
-    RQ_ERR_SCRATCH = 8      /* rq_gemm_smallm_noalloc: the partial sums would not
-                               fit its fixed scratch array                       */
+    RQ_ERR_SCRATCH = 8      /* the split-K partial sums would not fit the
+                               caller's workspace (rq_gemm_smallm_ws) or the
+                               fixed array (rq_gemm_smallm_noalloc)              */
 } rq_status;
 
 typedef enum { RQ_LAYOUT_SYM = 0, RQ_LAYOUT_ASYM_SB = 1, RQ_LAYOUT_FP8_TENSOR = 2 } rq_layout;
@@ -185,21 +190,48 @@ rq_status rq_gemv_batched(const rq_problem* problems, int count, int M, int bits
  * Tuned for 16 <= M <= 64 (batched decode); for M <= 4 or 8 only 4 or 8
  * activation rows are staged per round, otherwise M is padded to a multiple
  * of 16; it beats the vector units from M = 3 on.
- * Workspace.  For some shapes the K dimension is split across workgroups and
- * the partial sums pass through a workspace of 64 MiB that the library
- * allocates (and zeroes its arrival counters) at the first such call on a
- * (device, stream) pair and keeps until the process ends; it is never
- * regrown, freed or shared with another stream, so no later call allocates,
- * frees or synchronizes.  If that first call is
- * made while the stream is being captured into a graph (or the allocation
- * fails), the call keeps K whole instead.  Work that uses one stream's
- * workspace must not run concurrently with other work that uses it (graphs
- * captured on one stream and replayed on several at once race on it).
- * Partial sums are added in a fixed order, so results are deterministic.
+ * This entry point keeps K whole: it has no workspace, and the library never
+ * allocates, frees or synchronizes.  rq_gemm_smallm_ws below is the same call
+ * with a caller-owned workspace, through which K may be split.
  */
 rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* zeros,
                          const void* x, float* y, int M, int N, int K, int bits,
                          int group, int layout, void* stream);
+
+/* The most workspace rq_gemm_smallm_ws ever uses (split-K arrival counters
+ * and partial sums); a workspace of this size suits every call. */
+#define RQ_GEMM_WORKSPACE_MAX_BYTES (64 << 20)
+
+/*
+ * rq_gemm_smallm_workspace_size -- *bytes = the workspace rq_gemm_smallm_ws
+ * uses at these arguments: 0 where K is kept whole, at most
+ * RQ_GEMM_WORKSPACE_MAX_BYTES.  Host-only (no device call); shape rules and
+ * errors as for rq_gemm_smallm.
+ */
+rq_status rq_gemm_smallm_workspace_size(int M, int N, int K, int bits, int group,
+                                        int layout, size_t* bytes);
+
+/*
+ * rq_gemm_smallm_ws -- rq_gemm_smallm with a workspace owned by the caller.
+ * For long rows at small row counts the kernel splits K across workgroups
+ * (more rows share each staged copy of x); the partial sums then go through
+ * `workspace`, and the last workgroup to finish a 16-row tile adds them in a
+ * fixed order, so results are deterministic.
+ *   workspace: device memory, 16-byte aligned, of workspace_bytes bytes,
+ *   overlapping no input and not y.  Its first 64 KiB (the arrival counters)
+ *   must be zero before its first use; every call leaves them zero again, and
+ *   the rest needs no clearing.  NULL keeps K whole (then workspace_bytes is
+ *   ignored).
+ * Errors as for rq_gemm_smallm, plus RQ_ERR_SCRATCH when a non-NULL workspace
+ * is smaller than rq_gemm_smallm_workspace_size reports (nothing enqueued).
+ * Calls that share one workspace must not overlap in time (calls on one
+ * stream are ordered; graphs holding the same workspace must not be replayed
+ * concurrently).  The library never allocates, frees or synchronizes.
+ */
+rq_status rq_gemm_smallm_ws(const void* qweight, const void* scales, const void* zeros,
+                            const void* x, float* y, int M, int N, int K, int bits,
+                            int group, int layout, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Bytes of the fixed device array behind rq_gemm_smallm_noalloc. */
 #define RQ_NOALLOC_SCRATCH_BYTES ((8 << 20) + (64 << 10))
@@ -207,8 +239,9 @@ rq_status rq_gemm_smallm(const void* qweight, const void* scales, const void* ze
 /*
  * rq_gemm_smallm_noalloc -- rq_gemm_smallm for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses
- * that forbid allocation): same arguments, same kernels, same arrangement and
- * K split, same results bit for bit, but the split-K arrival counters and
+ * that forbid allocation): the arguments of rq_gemm_smallm and the kernels,
+ * arrangement, K split and results (bit for bit) of rq_gemm_smallm_ws with an
+ * ample workspace, but the split-K arrival counters and
  * partial sums go to a fixed device array of RQ_NOALLOC_SCRATCH_BYTES that
  * the library holds on each GPU it runs on until the process ends.  The call
  * never allocates, frees or synchronizes.  The array covers every split the

@@ -54,7 +54,7 @@ def test_status_values_match_header():
 
 
 def test_version_and_strings(L):
-    assert rq.rq_version() == (1 << 16)
+    assert rq.rq_version() == (1 << 16) | 1
     seen = set()
     for s in range(9):
         t = rq.rq_status_string(s)
@@ -125,10 +125,63 @@ GEMV_ONLY = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["rq_gemv", "rq_gemm_smallm", "rq_gemm_smallm_noalloc"])
+def ws_args(ws=None, ws_bytes=0, **kw):
+    """rq_gemm_smallm_ws arguments: those of gemv_args plus the workspace."""
+    a = gemv_args(**kw)
+    return a[:-1] + [ws, ws_bytes, None]
+
+
+@pytest.mark.parametrize("fn", ["rq_gemv", "rq_gemm_smallm", "rq_gemm_smallm_noalloc",
+                                "rq_gemm_smallm_ws"])
 @pytest.mark.parametrize("what,kw,status", CASES + GEMV_ONLY, ids=[c[0] for c in CASES + GEMV_ONLY])
 def test_product_rejects(L, fn, what, kw, status):
-    assert getattr(L, fn)(*gemv_args(**kw)) == status, what
+    args = ws_args(**kw) if fn == "rq_gemm_smallm_ws" else gemv_args(**kw)
+    assert getattr(L, fn)(*args) == status, what
+
+
+# rq_gemm_smallm_ws at a shape whose automatic choice splits K (int4 g64,
+# 4096 x 16384, M = 32), with fake, disjoint addresses
+SPLIT = dict(M=32, N=4096, K=16384)
+WS = A + (5 << 30)
+
+WS_CASES = [
+    ("misaligned workspace", dict(ws=WS + 4, ws_bytes=1 << 26), rq.RQ_ERR_ALIGN),
+    ("workspace overlaps y", dict(ws=A + (3 << 30) + 256, ws_bytes=1 << 26), rq.RQ_ERR_ALIAS),
+    ("workspace overlaps x", dict(ws=A + (2 << 30), ws_bytes=1 << 20), rq.RQ_ERR_ALIAS),
+    ("workspace overlaps codes", dict(ws=A, ws_bytes=64), rq.RQ_ERR_ALIAS),
+    ("workspace one byte short", dict(ws=WS, ws_bytes=None), rq.RQ_ERR_SCRATCH),
+    ("workspace of zero bytes", dict(ws=WS, ws_bytes=0), rq.RQ_ERR_SCRATCH),
+]
+
+
+@pytest.mark.parametrize("what,kw,status", WS_CASES, ids=[c[0] for c in WS_CASES])
+def test_workspace_rejects(L, what, kw, status):
+    """Workspace checks run on the host before any HIP call (a too-small
+    workspace enqueues nothing)."""
+    need = rq.rq_gemm_smallm_workspace_size(SPLIT["M"], SPLIT["N"], SPLIT["K"], 4, 64, 0)
+    assert need > 0
+    if kw.get("ws_bytes", 0) is None:
+        kw = dict(kw, ws_bytes=need - 1)
+    assert L.rq_gemm_smallm_ws(*ws_args(**kw, **SPLIT)) == status, what
+
+
+def test_workspace_size_on_the_host(L):
+    """The size query matches the split the plan query reports: splits * M * N
+    partial sums plus 64 KiB of arrival counters, 0 where K is kept whole, and
+    never above RQ_GEMM_WORKSPACE_MAX_BYTES."""
+    for (M, N, K) in ((32, 4096, 16384), (64, 4096, 16384), (32, 4096, 4096),
+                      (16, 16384, 4096), (64, 1000, 4096), (3, 2048, 8192)):
+        plan, splits = rq.gemm_config(M, N, K, 4, 64, 0)
+        b = rq.rq_gemm_smallm_workspace_size(M, N, K, 4, 64, 0)
+        assert b == (0 if splits == 1 else 65536 + 4 * splits * M * N), (M, N, K)
+        assert b <= rq.RQ_GEMM_WORKSPACE_MAX_BYTES
+    assert rq.rq_gemm_smallm_workspace_size(32, 4096, 16384, 4, 64, 0) > 0
+    sz = ctypes.c_size_t(7)
+    assert L.rq_gemm_smallm_workspace_size(0, 64, 256, 4, 64, 0, ctypes.byref(sz)) == \
+        rq.RQ_ERR_SHAPE
+    assert L.rq_gemm_smallm_workspace_size(1, 64, 256, 3, 64, 0, ctypes.byref(sz)) == \
+        rq.RQ_ERR_UNSUPPORTED
+    assert L.rq_gemm_smallm_workspace_size(1, 64, 256, 4, 64, 0, None) == rq.RQ_ERR_NULL
 
 
 DQ_ONLY = [
@@ -154,6 +207,8 @@ def test_valid_call_without_gpu_reports_device(L):
     assert L.rq_gemv(*gemv_args()) == rq.RQ_ERR_DEVICE
     assert L.rq_gemm_smallm(*gemv_args(M=32)) == rq.RQ_ERR_DEVICE
     assert L.rq_gemm_smallm_noalloc(*gemv_args(M=32)) == rq.RQ_ERR_DEVICE
+    assert L.rq_gemm_smallm_ws(*ws_args(M=32)) == rq.RQ_ERR_DEVICE
+    assert L.rq_gemm_smallm_ws(*ws_args(ws=WS, ws_bytes=1 << 26, **SPLIT)) == rq.RQ_ERR_DEVICE
     assert L.rq_dequant(*dq_args()) == rq.RQ_ERR_DEVICE
 
 

@@ -101,8 +101,9 @@ def test_rq_gemv_captures_as_first_call(M):
 
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 16384), (32, 4096, 16384), (64, 1000, 4096)])
 def test_rq_gemm_smallm_captured_after_one_eager_call(M, N, K):
-    """The first split call on a stream allocates the workspace; a capture of
-    the same call afterwards holds no allocation, free or wait, and every
+    """The binding makes its workspace for a stream at the first call there
+    (a torch tensor; the library never allocates); a capture of the same call
+    afterwards holds no allocation, free or wait, and every
     replay matches the eager call bit for bit (counters reset each time)."""
     import gemm_rwkv_decode_amd as rq
     from tests import rqtest as T
@@ -138,8 +139,8 @@ def test_rq_gemm_smallm_captured_after_one_eager_call(M, N, K):
 
 
 def test_rq_gemm_smallm_captured_as_first_call_keeps_k_whole():
-    """As the first call on a fresh stream under capture there is no workspace
-    yet: the call keeps K whole (no allocation under capture) and is still at
+    """As the first call on a fresh stream under capture the binding has no
+    workspace yet: the call keeps K whole (no allocation under capture) and is still at
     parity on every replay."""
     import gemm_rwkv_decode_amd as rq
     from tests import rqtest as T

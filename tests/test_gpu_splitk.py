@@ -1,5 +1,6 @@
 """K split over workgroups on the matrix-core kernel: partial tiles in the
-per-stream workspace, added in K-range order by the wave that finishes each
+caller's workspace (the binding's per-stream one unless a test passes its
+own), added in K-range order by the wave that finishes each
 16-row tile last (same launch; arrival counters reset by that wave).  Against the oracle: forced and automatic splits, calls back to back
 that reuse the workspace (with changing splits, M and shapes, and a grouped
 launch in between), bit-identical repeats, and the width-4096 FFN-value
@@ -106,3 +107,91 @@ def test_split_then_batched_then_split(tune):
         yq, bq = T.oracle_y(q, x)
         T.assert_close(yb, yq, bq, f"batched {i}")
     T.assert_close(gemm_nan(p, x), yr, b, "split after")
+
+
+def c_smallm(p, x, y, ws=None, ws_bytes=0, plain=False):
+    """rq_gemm_smallm (plain) or rq_gemm_smallm_ws through the C interface."""
+    import ctypes
+    f = p.fmt
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = [p.qweight.data_ptr(), p.scales.data_ptr(),
+            None if p.zeros is None else p.zeros.data_ptr(), x.data_ptr(), y.data_ptr(),
+            x.shape[0], p.N, p.K, f.bits, f.group, f.layout]
+    if plain:
+        return rq.lib().rq_gemm_smallm(*args, s)
+    return rq.lib().rq_gemm_smallm_ws(*args, None if ws is None else ws.data_ptr(), ws_bytes, s)
+
+
+@pytest.mark.parametrize("f,N,K,M", [(S.INT4_G64, 4096, 16384, 32),
+                                     (S.ASYM4_G32, 2560, 10240, 64),
+                                     (S.INT8_G16, 1000, 4096, 64)],
+                         ids=["int4g64", "asym4g32", "int8g16"])
+def test_caller_workspace_and_k_kept_whole(f, N, K, M):
+    """At shapes the chooser splits: a workspace of exactly the queried size
+    (counters zeroed by the caller) gives the binding's result bit for bit,
+    twice in a row; rq_gemm_smallm (no workspace) and rq_gemm_smallm_ws with
+    NULL keep K whole and agree bit for bit; all within the oracle's bound;
+    a workspace one byte short is refused with y untouched."""
+    need = rq.rq_gemm_smallm_workspace_size(M, N, K, f.bits, f.group, f.layout)
+    assert need > 0, "shape does not split K"
+    p = mat(f, N, K, f"ws{f.tag}")
+    x = x_for(M, K, 11)
+    yr, b = T.oracle_y(p, x)
+    T.say(f"caller workspace {f.tag} {N}x{K} M={M} need={need}")
+    ya = gemm_nan(p, x)  # binding's workspace
+    torch.cuda.synchronize()
+    T.assert_close(ya, yr, b, "auto workspace")
+    ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda")
+    for r in range(2):
+        y = torch.full((M, N), float("nan"), device="cuda")
+        assert c_smallm(p, x, y, ws, need) == rq.RQ_OK
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ya.view(torch.int32)), f"call {r}"
+    assert torch.count_nonzero(ws[:16384]).item() == 0, "counters not left at zero"
+    y1 = torch.full((M, N), float("nan"), device="cuda")
+    y2 = torch.full((M, N), float("nan"), device="cuda")
+    assert c_smallm(p, x, y1, plain=True) == rq.RQ_OK
+    assert c_smallm(p, x, y2) == rq.RQ_OK
+    torch.cuda.synchronize()
+    T.assert_close(y1, yr, b, "K kept whole")
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    y3 = torch.full((M, N), float("nan"), device="cuda")
+    assert c_smallm(p, x, y3, ws, need - 1) == rq.RQ_ERR_SCRATCH
+    torch.cuda.synchronize()
+    assert torch.isnan(y3).all()
+
+
+def test_graph_with_caller_workspace_forced_split(tune):
+    """A graph captured with the caller's workspace and a forced 8-way split
+    (more than the automatic choice) replays at parity into NaN-filled
+    outputs, bit-identical on every replay, with other GPU work between."""
+    f, M, N, K = S.INT4_G64, 32, 2048, 16384
+    tune(RQ_GEMM_SPLITS=8)
+    assert rq.gemm_config(M, N, K, f.bits, f.group, f.layout)[1] == 8
+    need = rq.rq_gemm_smallm_workspace_size(M, N, K, f.bits, f.group, f.layout)
+    p = mat(f, N, K, "graphws")
+    x = x_for(M, K, 5)
+    yr, b = T.oracle_y(p, x)
+    ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda")
+    y = torch.full((M, N), float("nan"), device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    call = rq.prepare("rq_gemm_smallm_ws", p.qweight, p.scales, None, x, y, M, N, K, f.bits,
+                      f.group, f.layout, ws, stream=s)
+    T.say(f"graph with caller workspace {N}x{K} M={M} splits=8 need={need}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device="cuda")
+    first = None
+    for r in range(4):
+        y.fill_(float("nan"))
+        junk.mul_(1.0001)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        T.assert_close(y, yr, b, f"replay {r}")
+        if first is None:
+            first = y.clone()
+        assert torch.equal(y.view(torch.int32), first.view(torch.int32)), f"replay {r}"

@@ -1,16 +1,17 @@
 """rq_gemm_smallm_noalloc: the allocation-free form of rq_gemm_smallm.
 
-It runs the same kernels, arrangement and K split as rq_gemm_smallm, with the
+It runs the same kernels, arrangement and K split as rq_gemm_smallm_ws (which
+the binding's rq_gemm_smallm calls with its per-stream workspace), with the
 split-K partial sums in the library's fixed device array instead of a
-workspace it allocates.  Checked through the C interface:
+caller's workspace.  Checked through the C interface:
 
 * two calls in a row, each splitting K (the second smaller), bit-identical to
-  rq_gemm_smallm on the same inputs and within 1e-3 * sum|w x| of the oracle;
+  rq_gemm_smallm_ws on the same inputs and within 1e-3 * sum|w x| of the oracle;
 * a shape that keeps K whole;
 * a call whose partial sums would exceed the array (a forced split count)
   returns RQ_ERR_SCRATCH and leaves y untouched;
 * captured into a graph as the first call on a fresh stream (where
-  rq_gemm_smallm would have no workspace yet), every replay matches the eager
+  the binding has no workspace yet), every replay matches the eager
   call, with other work on the GPU between replays.
 """
 import ctypes
@@ -77,7 +78,7 @@ CASES = [  # (format, N, K, M): the first two of each pair split K
 
 
 @pytest.mark.parametrize("i", [0, 2, 4], ids=["int4g64", "int8g16", "asym4g32"])
-def test_two_calls_in_a_row_match_the_allocating_entry(i):
+def test_two_calls_in_a_row_match_the_workspace_entry(i):
     for (f, N, K, M) in CASES[i:i + 2]:
         cfg = rq.gemm_config(M, N, K, f.bits, f.group, f.layout)
         assert cfg is not None and cfg[1] > 1, f"{f.tag} {N}x{K} M={M} does not split K"
