@@ -235,11 +235,15 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 #pragma unroll
   for (int c = 0; c < CPL; c++) kc[c] = w * (LPR * CPL) + c * LPR + li;
 
-  u32 rowi[NP], roff[NP];  // each visited row and its code offset
+  // each visited row (rows past the end re-read the last row) and its code
+  // offset: one multiply, then adds (the clamp commutes with the scaling)
+  u32 rowi[NP], roff[NP];
+  const u32 r0 = (u32)(row0 + rs), rlast = (u32)(N - 1);
+  const u32 off0 = r0 * row_bytes, ostep = (u32)RPW * row_bytes, olast = rlast * row_bytes;
 #pragma unroll
   for (int p = 0; p < NP; p++) {
-    rowi[p] = (u32)min(row0 + p * RPW + rs, N - 1);
-    roff[p] = rowi[p] * row_bytes;
+    rowi[p] = min(r0 + (u32)(p * RPW), rlast);
+    roff[p] = min(off0 + (u32)p * ostep, olast);
   }
 
   // 1. the activations of this lane's chunks (from L2), issued first: loads of
@@ -335,11 +339,11 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
     }
   }
   // 4. multiply, row by row
+  float acc[NP][MT];
 #pragma unroll
   for (int p = 0; p < NP; p++) {
-    float acc[MT];
 #pragma unroll
-    for (int m = 0; m < MT; m++) acc[m] = 0.0f;
+    for (int m = 0; m < MT; m++) acc[p][m] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
       float sc, t = 0.0f;
@@ -355,19 +359,47 @@ k_gemv(const GemvBatch<B> bt, int Mrows, int K, int gsh, int ssh) {
 #pragma unroll
       for (int m = 0; m < MT; m++) {
         const float d = chunk_dot<FMT>(code[p][c], xr[m][c], hw[p][c]);
-        acc[m] = __builtin_fmaf(d, sc, acc[m]);
-        if (is_asym(FMT)) acc[m] = __builtin_fmaf(-t, xs[m][c], acc[m]);
+        acc[p][m] = __builtin_fmaf(d, sc, acc[p][m]);
+        if (is_asym(FMT)) acc[p][m] = __builtin_fmaf(-t, xs[m][c], acc[p][m]);
       }
     }
-    const int n = row0 + p * RPW + rs;
+  }
+  // 5. each (row, activation row) summed over the row's LPR lanes
+  constexpr int V = NP * MT;
+  if constexpr (V <= LPR) {
+    // all sums at once, halving the values per exchange level; the SUB
+    // lanes li = idx*SUB .. idx*SUB+SUB-1 end with the total of value idx
+    float v[V];
 #pragma unroll
-    for (int m = 0; m < MT; m++) {
-      const float v = group_sum<LPR>(acc[m]);
-      if (li == 0) {
-        if (SK == 1) {
-          if (m < Mrows && n < N) y[(u32)m * (u32)N + (u32)n] = v * mscale;
-        } else {
-          part[(w * RB + p * RPW + rs) * MT + m] = v;
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int m = 0; m < MT; m++) v[p * MT + m] = acc[p][m];
+    group_sum_multi<LPR, V>(v, li);
+    constexpr int SUB = LPR / V;
+    if (li % SUB == 0) {
+      const int idx = li / SUB;
+      const int p = idx / MT, m = idx % MT;
+      const int r = p * RPW + rs;
+      const int n = row0 + r;
+      if (SK == 1) {
+        if (m < Mrows && n < N) y[(u32)m * (u32)N + (u32)n] = v[0] * mscale;
+      } else {
+        part[(w * RB + r) * MT + m] = v[0];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      const int n = row0 + p * RPW + rs;
+#pragma unroll
+      for (int m = 0; m < MT; m++) {
+        const float v = group_sum<LPR>(acc[p][m]);
+        if (li == 0) {
+          if (SK == 1) {
+            if (m < Mrows && n < N) y[(u32)m * (u32)N + (u32)n] = v * mscale;
+          } else {
+            part[(w * RB + p * RPW + rs) * MT + m] = v;
+          }
         }
       }
     }
