@@ -261,73 +261,4 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Sums of V values per lane (V a power of two, V <= LPR) over the LPR
-// consecutive lanes of a row group, the values halved at the first levels:
-// each level pairs a lane with one whose level bit differs, the lane keeps
-// one half of its values (the upper half where its bit is set) and adds the
-// partner's copy of that half, so a level costs one exchange per kept value
-// instead of one per value.  Levels run from the widest distance down:
-// 32 and 16 by v_permlane32/16_swap (which also select the half, no
-// per-lane choice), 8 by row_mirror (lane ^ 15), 4 by row_half_mirror
-// (lane ^ 7), 2 and 1 by quad permutes; each pairs lanes that agree on the
-// bits already decided, and together they cover the whole group.  On return
-// v[0] holds the group total of value li >> (log2 LPR - log2 V) (li: lane
-// index in the group); the other entries are spent.
-template <int D>
-__device__ __forceinline__ float level_partner(float v) {
-  if constexpr (D == 8) return dpp_mov<0x140>(v);       // row_mirror
-  else if constexpr (D == 4) return dpp_mov<0x141>(v);  // row_half_mirror
-  else if constexpr (D == 2) return dpp_mov<0x4E>(v);   // quad_perm(2,3,0,1)
-  else return dpp_mov<0xB1>(v);                         // quad_perm(1,0,3,2)
-}
-
-template <int LPR, int V>
-__device__ __forceinline__ void group_sum_multi(float* v, int li) {
-  static_assert(V >= 1 && V <= LPR && (V & (V - 1)) == 0 && (LPR & (LPR - 1)) == 0, "V, LPR");
-  constexpr int LEVELS = __builtin_ctz(LPR);
-  int w = V;  // live values
-#pragma unroll
-  for (int lv = 0; lv < LEVELS; lv++) {
-    const int d = LPR >> (lv + 1);
-    if (w > 1) {
-      const int half = w / 2;
-#pragma unroll
-      for (int j = 0; j < half; j++) {
-        if (d >= 16) {
-          // rows (16 lanes) pair up at distance d; the swap leaves the kept
-          // half in one register and the partner's copy in the other
-          u32 a = __builtin_bit_cast(u32, v[j]), b = __builtin_bit_cast(u32, v[j + half]);
-          if (d == 32) lane_swap32(a, b);
-          else lane_swap16(a, b);
-          v[j] = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-        } else {
-          const bool hi = (li & d) != 0;
-          const float keep = hi ? v[j + half] : v[j];
-          const float send = hi ? v[j] : v[j + half];
-          if (d == 8) v[j] = keep + level_partner<8>(send);
-          else if (d == 4) v[j] = keep + level_partner<4>(send);
-          else if (d == 2) v[j] = keep + level_partner<2>(send);
-          else v[j] = keep + level_partner<1>(send);
-        }
-      }
-      w = half;
-    } else {
-      if (d >= 16) {
-        u32 a = __builtin_bit_cast(u32, v[0]), b = a;
-        if (d == 32) lane_swap32(a, b);
-        else lane_swap16(a, b);
-        v[0] = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-      } else if (d == 8) {
-        v[0] += level_partner<8>(v[0]);
-      } else if (d == 4) {
-        v[0] += level_partner<4>(v[0]);
-      } else if (d == 2) {
-        v[0] += level_partner<2>(v[0]);
-      } else {
-        v[0] += level_partner<1>(v[0]);
-      }
-    }
-  }
-}
-
 }  // namespace rq
