@@ -411,16 +411,9 @@ rq_status rq_gemm_smallm_ws(const void* qweight, const void* scales, const void*
       check_product(qweight, scales, zeros, x, y, M, N, K, bits, group, layout, &fmt);
   if (st != RQ_OK) return st;
   const bool has_ws = workspace != nullptr;
-  if (has_ws) {
-    if (!aligned16(workspace)) return RQ_ERR_ALIGN;
-    // the workspace against every input and the output
-    st = check_output(static_cast<const float*>(workspace), workspace_bytes, qweight, scales,
-                      zeros, x, N, K, bits, group, layout, M);
-    if (st != RQ_OK) return st;
-    if (overlaps(range_of(workspace, workspace_bytes), range_of(y, (size_t)M * N * 4)))
-      return RQ_ERR_ALIAS;
-  }
-  // host-only choice first, so a too-small workspace enqueues nothing
+  if (has_ws && !aligned16(workspace)) return RQ_ERR_ALIGN;
+  // host-only choice first, so a workspace that is too small or overlaps an
+  // operand enqueues nothing
   const bool mfma = rq::gemm_supports(fmt, M, K, group);
   size_t need = 0;
   rq::GemmCfg c{};
@@ -431,6 +424,12 @@ rq_status rq_gemm_smallm_ws(const void* qweight, const void* scales, const void*
       c = rq::choose_gemm(fmt, M, N, K, group, 0, false);  // K kept whole
     } else {
       if (workspace_bytes < need) return RQ_ERR_SCRATCH;
+      // the bytes this call uses against every input and the output
+      st = check_output(workspace, need, qweight, scales, zeros, x, N, K, bits, group, layout,
+                        M);
+      if (st != RQ_OK) return st;
+      if (overlaps(range_of(workspace, need), range_of(y, (size_t)M * N * 4)))
+        return RQ_ERR_ALIAS;
       ws = static_cast<float*>(workspace);
     }
   }

@@ -217,8 +217,9 @@ rq_status rq_gemm_smallm_workspace_size(int M, int N, int K, int bits, int group
  * (more rows share each staged copy of x); the partial sums then go through
  * `workspace`, and the last workgroup to finish a 16-row tile adds them in a
  * fixed order, so results are deterministic.
- *   workspace: device memory, 16-byte aligned, of workspace_bytes bytes,
- *   overlapping no input and not y.  Its first 64 KiB (the arrival counters)
+ *   workspace: device memory, 16-byte aligned, of workspace_bytes bytes; the
+ *   bytes the call uses (the size rq_gemm_smallm_workspace_size reports) must
+ *   overlap no input and not y (RQ_ERR_ALIAS).  Its first 64 KiB (the arrival counters)
  *   must be zero before its first use; every call leaves them zero again, and
  *   the rest needs no clearing.  NULL keeps K whole (then workspace_bytes is
  *   ignored).

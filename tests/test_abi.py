@@ -147,8 +147,8 @@ WS = A + (5 << 30)
 WS_CASES = [
     ("misaligned workspace", dict(ws=WS + 4, ws_bytes=1 << 26), rq.RQ_ERR_ALIGN),
     ("workspace overlaps y", dict(ws=A + (3 << 30) + 256, ws_bytes=1 << 26), rq.RQ_ERR_ALIAS),
-    ("workspace overlaps x", dict(ws=A + (2 << 30), ws_bytes=1 << 20), rq.RQ_ERR_ALIAS),
-    ("workspace overlaps codes", dict(ws=A, ws_bytes=64), rq.RQ_ERR_ALIAS),
+    ("workspace overlaps x", dict(ws=A + (2 << 30), ws_bytes=1 << 26), rq.RQ_ERR_ALIAS),
+    ("workspace overlaps codes", dict(ws=A, ws_bytes=1 << 26), rq.RQ_ERR_ALIAS),
     ("workspace one byte short", dict(ws=WS, ws_bytes=None), rq.RQ_ERR_SCRATCH),
     ("workspace of zero bytes", dict(ws=WS, ws_bytes=0), rq.RQ_ERR_SCRATCH),
 ]
@@ -163,6 +163,22 @@ def test_workspace_rejects(L, what, kw, status):
     if kw.get("ws_bytes", 0) is None:
         kw = dict(kw, ws_bytes=need - 1)
     assert L.rq_gemm_smallm_ws(*ws_args(**kw, **SPLIT)) == status, what
+
+
+def test_workspace_checked_only_where_used(L):
+    """Only the bytes the call uses are checked against the operands: a
+    workspace whose unused tail runs into y passes the host checks (and then
+    reports the missing device here)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    need = rq.rq_gemm_smallm_workspace_size(SPLIT["M"], SPLIT["N"], SPLIT["K"], 4, 64, 0)
+    y = A + (3 << 30)
+    ws = y - need
+    assert L.rq_gemm_smallm_ws(*ws_args(ws=ws, ws_bytes=need + 4096, **SPLIT)) == \
+        rq.RQ_ERR_DEVICE
+    assert L.rq_gemm_smallm_ws(*ws_args(ws=ws + 16, ws_bytes=need, **SPLIT)) == \
+        rq.RQ_ERR_ALIAS
 
 
 def test_workspace_size_on_the_host(L):
