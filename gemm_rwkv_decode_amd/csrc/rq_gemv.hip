@@ -633,7 +633,11 @@ GemvCfg choose_gemv(int fmt, int M, int N, int K) {
   }
   if (forced > 0) {  // tuning: RQ_GEMV_LPR / RQ_GEMV_CPL / RQ_GEMV_NPASS
     const int cpl = tu.gemv_cpl ? tu.gemv_cpl : c.cpl;
-    if (chunks % (forced * cpl) == 0 &&
+    // only the pairs launch_mt instantiates for this pass size
+    const bool inst = (forced == 8 || forced == 16 || forced == 32 || forced == 64) &&
+                      (cpl == 1 || (c.mt == 1 && ((forced == 8 && (cpl == 2 || cpl == 4)) ||
+                                                  (forced == 16 && cpl == 2))));
+    if (inst && chunks % (forced * cpl) == 0 &&
         chunks / (forced * cpl) <= gemv_max_threads(c.mt, cpl) / 64) {
       c.lpr = forced;
       c.cpl = cpl;
