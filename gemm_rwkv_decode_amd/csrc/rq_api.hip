@@ -204,9 +204,10 @@ enum Kernel { KERN_VECTOR, KERN_DECODE_MFMA, KERN_SMALLM_MFMA };
 //    asymmetric M = 8: 65.7 -> 11.0 us) and, at M = 3..4, the decode kernel
 //    (int8 8192x2048 M = 4: 7.5 -> 6.8 us; asymmetric 2560x2560 M = 4:
 //    6.1 -> 5.2 us; 5-bit 16384x4096 M = 4: 20.2 -> 19.5 us), except for
-//    the measured shapes below, where the decode kernel wins at M = 3..4
-//    (these calls keep K whole, so few, long rows or many short ones leave
-//    the small-batch kernel with too little work per workgroup).
+//    the measured shapes below, where the decode kernel or the vector units
+//    win at M = 3..4 (these calls keep K whole, so few, long rows or many
+//    short ones leave the small-batch kernel with too little work per
+//    workgroup).
 //  * M <= 2: the vector-unit kernel, unless none of its tuned launch shapes
 //    splits the row (the generic kernel: FP8 4096x16384 at M = 2 takes
 //    52.1 us there, 18.0 us on the small-batch kernel).  Then the decode
@@ -217,20 +218,27 @@ enum Kernel { KERN_VECTOR, KERN_DECODE_MFMA, KERN_SMALLM_MFMA };
 // *gc receives the vector-unit launch shape when that kernel is chosen.  The
 // common decode case (M <= 2, a tuned vector-unit shape) returns after one
 // launch-shape search, so stream-mode callers pay little host time per call.
-// RWKV-7 matrices where, at M = 3..4, the matrix-core decode kernel beats
-// the small-batch kernel with K kept whole (one product, weights cold):
-// int4 g64 2048x8192, the 1.5B-shaped FFN value (8.75-9.03 -> 7.09-7.32 us),
-// and 4-bit asymmetric 10240x2560, the 2.9B-shaped FFN key (10.16-10.57 ->
-// 8.65-8.81 us).  N is the launch's row count, so a grouped launch of several
+// RWKV-7 matrices where, at M = 3..4, another kernel beats the small-batch
+// kernel with K kept whole (one product, weights cold, launches replayed from
+// a graph).  N is the launch's row count, so a grouped launch of several
 // problems does not match.
+//  * the matrix-core decode kernel: 4-bit asymmetric 10240x2560, the
+//    2.9B-shaped FFN key (10.36-10.39 -> 8.74-8.97 us);
+//  * the vector units in one pass of 4 rows: int4 g64 2048x8192, the
+//    1.5B-shaped FFN value (decode kernel 7.19-7.39, small-batch 9.34-9.43,
+//    vector units 6.36-6.76 us; the 24-layer step at M = 4 0.581-0.584 ->
+//    0.563 ms).  (int8 g16 2048x2048, 5.1 -> 4.7 us alone, left the int8
+//    step no faster: 0.755-0.759 -> 0.763 ms.)
 struct MvShape {
   int fmt, group, N, K;
 };
-constexpr MvShape kDecodeWins[] = {{FMT_S4, 64, 2048, 8192}, {FMT_A4, 32, 10240, 2560}};
+constexpr MvShape kDecodeWins[] = {{FMT_A4, 32, 10240, 2560}};
+constexpr MvShape kVectorWins[] = {{FMT_S4, 64, 2048, 8192}};
 
-bool decode_wins(int fmt, int M, int N, int K, int group) {
+template <size_t n>
+bool listed(const MvShape (&tab)[n], int fmt, int M, int N, int K, int group) {
   if (M < 3 || M > 4) return false;
-  for (const MvShape& s : kDecodeWins)
+  for (const MvShape& s : tab)
     if (s.fmt == fmt && s.group == group && s.N == N && s.K == K) return true;
   return false;
 }
@@ -250,7 +258,11 @@ Kernel pick_kernel(int fmt, int M, int N, int K, int group, rq::GemvCfg* gc) {
   } else if (t == 3) {
     k = mm ? KERN_SMALLM_MFMA : KERN_VECTOR;
   } else if (M >= 3) {
-    if (mv && decode_wins(fmt, M, N, K, group)) return KERN_DECODE_MFMA;
+    if (listed(kVectorWins, fmt, M, N, K, group)) {
+      *gc = rq::choose_gemv(fmt, M, N, K);
+      if (gc->lpr != 0) return KERN_VECTOR;
+    }
+    if (mv && listed(kDecodeWins, fmt, M, N, K, group)) return KERN_DECODE_MFMA;
     k = mm ? KERN_SMALLM_MFMA : (mv ? KERN_DECODE_MFMA : KERN_VECTOR);
   } else {  // M <= 2 on the generic vector-unit kernel
     if (mv && (fmt == FMT_S4 || fmt == FMT_A4 || !mm)) return KERN_DECODE_MFMA;

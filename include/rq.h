@@ -150,10 +150,10 @@ rq_status rq_dequant(const void* qweight, const void* scales, const void* zeros,
  * tuned launch shapes); from M = 3 on the small-batch matrix-core kernel of
  * rq_gemm_smallm (4 or 8 activation rows staged for M <= 4 or 8, else M
  * padded to a multiple of 16), or the matrix-core decode kernel where the
- * former does not take K and for two measured RWKV-7 shapes at M = 3..4
- * (int4 g64 2048x8192, 4-bit asymmetric 10240x2560); the vector units, in
- * passes of up to 8 rows,
- * wherever K suits neither.  The small-batch kernel runs here with K whole:
+ * former does not take K and for one measured RWKV-7 shape at M = 3..4
+ * (4-bit asymmetric 10240x2560); the vector units, in passes of up to 8
+ * rows, wherever K suits neither and for one measured shape at M = 3..4
+ * (int4 g64 2048x8192).  The small-batch kernel runs here with K whole:
  * this entry point never allocates or synchronizes.
  * Shape rules as for rq_dequant, plus 1 <= M <= RQ_MAX_M.
  */

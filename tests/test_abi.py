@@ -350,14 +350,18 @@ def test_gemv_config_on_the_host(L):
         assert rq.gemv_config(M, 4096, 4096, 4, 64, 0)[0] == "smallm_mfma"
         assert rq.gemv_config(M, 2560, 10240, 4, 32, 1)[0] == "smallm_mfma"
     assert rq.gemv_config(1, 4096, 65536, 4, 64, 0)[0] == "decode_mfma"
-    # measured exceptions at M = 3..4: the 1.5B-shaped FFN value (int4) and the
-    # 2.9B-shaped FFN key (asymmetric) run on the decode kernel
+    # measured exceptions at M = 3..4: the 2.9B-shaped FFN key (asymmetric)
+    # runs on the decode kernel, the 1.5B-shaped FFN value (int4) on the
+    # vector units
     for M in (3, 4):
-        assert rq.gemv_config(M, 2048, 8192, 4, 64, 0)[0] == "decode_mfma"
         assert rq.gemv_config(M, 10240, 2560, 4, 32, 1)[0] == "decode_mfma"
+        assert rq.gemv_config(M, 2048, 8192, 4, 64, 0)[0] == "vector"
+        assert rq.gemv_config(M, 2048, 2048, 8, 16, 0)[0] == "smallm_mfma"
         assert rq.gemv_config(M, 2048, 8192, 8, 16, 0)[0] == "smallm_mfma"
+        assert rq.gemv_config(M, 2048, 2048, 4, 64, 0)[0] == "smallm_mfma"
     for M in (2, 5):
         assert rq.gemv_config(M, 2048, 8192, 4, 64, 0)[0] != "decode_mfma"
+    assert rq.gemv_config(5, 2048, 8192, 4, 64, 0)[0] == "smallm_mfma"
     assert rq.gemv_config(1, 4096, 65536, 8, 16, 0)[0] == "smallm_mfma"
     # FP8 at M = 2 with a row the vector kernel cannot split
     assert rq.gemv_config(2, 4096, 16384, 8, 0, 2)[0] != "vector"

@@ -256,9 +256,10 @@ def test_kernel_choice_long_rows(f, K, M):
     (S.ASYM5_G32, 2560, 10240, 1, ("vector", 64, 1, 4)),
     (S.FP8_E4M3, 16384, 4096, 1, ("vector", 16, 2, 2)),
     (S.FP8_E4M3, 4096, 4096, 1, ("vector", 16, 2, 2)),
-    # measured decode-kernel shapes at M = 3..4
-    (S.INT4_G64, 2048, 8192, 4, ("decode_mfma", 0, 0, 0)),
+    # measured decode-kernel and vector-unit shapes at M = 3..4
     (S.ASYM4_G32, 10240, 2560, 3, ("decode_mfma", 0, 0, 0)),
+    (S.INT4_G64, 2048, 8192, 4, ("vector", 64, 1, 4)),
+    (S.INT4_G64, 2048, 8192, 3, ("vector", 64, 1, 4)),
 ], ids=lambda v: getattr(v, "tag", str(v)))
 def test_tuned_shapes(f, N, K, M, kernel):
     """The RWKV-7 shapes with a measured kernel or launch shape of their own
